@@ -1,0 +1,141 @@
+"""Pins for the reference planner: a hand-worked example, brute-force masks
+from ancestor sets built by closure, and the layout invariants."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle.plan import PlanError, ref_plan
+from tree_structured_decode_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_hand_worked_tiny_binary_tree():
+    with open(os.path.join(GOLDEN, "plan_tiny_binary_tree_c64.json")) as f:
+        g = json.load(f)
+    t, e = g["tree"], g["expect"]
+    pl = ref_plan(t["parents"], t["seg_lens"], t["query_nodes"], t["chunk_tokens"])
+    for key in ("total_tokens", "num_chunks", "num_slots", "mask_words"):
+        assert pl[key] == e[key], key
+    for key in ("node_start", "flat_node_order", "node_flat_start", "chunk_start", "group_offsets",
+                "slot_query", "chunk_full", "query_slot_offsets", "query_slots"):
+        assert pl[key].tolist() == e[key], key
+    assert pl["slot_mask"].tolist() == e["slot_mask"]
+    f2l = np.empty(e["total_tokens"], dtype=np.int64)
+    for fs, ls, n in e["flat_to_logical_runs"]:
+        f2l[fs:fs + n] = np.arange(ls, ls + n)
+    assert pl["flat_to_logical"].tolist() == f2l.tolist()
+    lens = np.diff(pl["chunk_start"])
+    go = pl["group_offsets"]
+    assert int(sum(lens[c] * (go[c + 1] - go[c]) for c in range(pl["num_chunks"]))) == e["computed_token_query_pairs"]
+    assert int(sum(bin(int(w)).count("1") for w in pl["slot_mask"].ravel())) == e["useful_token_query_pairs"]
+
+
+def _ancestor_sets(parents):
+    anc = []
+    for i, p in enumerate(parents):
+        a = {i}
+        if p >= 0:
+            a |= anc[p]
+        anc.append(a)
+    return anc
+
+
+def check_plan_invariants(pl, parents, seg, queries, c):
+    n, nq = len(parents), len(queries)
+    total = int(np.sum(seg))
+    assert pl["total_tokens"] == total
+    # flattening is a permutation and each node's segment stays contiguous and in order
+    f2l = pl["flat_to_logical"].astype(np.int64)
+    assert sorted(f2l.tolist()) == list(range(total))
+    ns, nfs = pl["node_start"], pl["node_flat_start"]
+    for x in range(n):
+        assert (f2l[nfs[x]:nfs[x] + seg[x]] == np.arange(ns[x], ns[x] + seg[x])).all()
+    # pre-order: a subtree occupies one flat interval starting at its root
+    sub = np.array(seg, dtype=np.int64)
+    for x in range(n - 1, -1, -1):
+        if parents[x] >= 0:
+            sub[parents[x]] += sub[x]
+    for x in range(n):
+        if parents[x] >= 0:
+            p = parents[x]
+            assert nfs[p] + seg[p] <= nfs[x] and nfs[x] + sub[x] <= nfs[p] + sub[p]
+    # chunks: equal C except the last, covering [0, T)
+    cs = pl["chunk_start"]
+    assert cs[0] == 0 and cs[-1] == total
+    lens = np.diff(cs)
+    assert (lens[:-1] == c).all() and 1 <= lens[-1] <= c
+    # masks against ancestor sets built by closure
+    anc = _ancestor_sets(parents)
+    flat_node = np.empty(total, dtype=np.int64)
+    for x in range(n):
+        flat_node[nfs[x]:nfs[x] + seg[x]] = x
+    go, sq, sm = pl["group_offsets"], pl["slot_query"], pl["slot_mask"]
+    words = -(-c // 32)
+    assert sm.shape == (pl["num_slots"], words)
+    for k in range(len(cs) - 1):
+        members = []
+        for qi in range(nq):
+            vis = [flat_node[f] in anc[queries[qi]] for f in range(cs[k], cs[k + 1])]
+            if any(vis):
+                members.append((qi, vis))
+        assert go[k + 1] - go[k] == len(members)
+        full = bool(members) and all(all(v) for _, v in members)
+        assert pl["chunk_full"][k] == int(full)
+        for j, (qi, vis) in enumerate(members):
+            s = go[k] + j
+            assert sq[s] == qi
+            bits = [(int(sm[s, t >> 5]) >> (t & 31)) & 1 for t in range(words * 32)]
+            assert bits[:len(vis)] == [int(v) for v in vis]
+            assert not any(bits[len(vis):])
+    # merge lists: each query's slots in ascending chunk order; popcounts give path lengths
+    qso, qs = pl["query_slot_offsets"], pl["query_slots"]
+    for qi in range(nq):
+        mine = qs[qso[qi]:qso[qi + 1]].tolist()
+        assert mine == sorted(mine) and all(sq[s] == qi for s in mine)
+        pop = sum(bin(int(w)).count("1") for s in mine for w in sm[s])
+        assert pop == sum(seg[x] for x in anc[queries[qi]])
+    assert qso[-1] == pl["num_slots"]
+
+
+@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("c", [1, 7, 16, 64, 100, 128])
+def test_random_trees_against_closure(seed, c):
+    rng = np.random.default_rng(seed * 31 + c)
+    n = int(rng.integers(1, 40))
+    p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([1, 3, 60])), int(rng.integers(1, 12)),
+                             forest_prob=0.15)
+    check_plan_invariants(ref_plan(p, s, qn, c), p, s, qn, c)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_standard_workload_plans(cfg):
+    wl = W.standard_workload(cfg)
+    pl = ref_plan(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens)
+    if cfg in (1, 2, 3):
+        check_plan_invariants(pl, wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens)
+    assert pl["num_slots"] == pl["query_slot_offsets"][-1]
+
+
+def test_rejects_bad_input():
+    ok = ([-1, 0], [3, 4], [1])
+    with pytest.raises(PlanError) as e:
+        ref_plan([-1, 1], [3, 4], [1], 4)
+    assert e.value.kind == "invalid_tree"
+    with pytest.raises(PlanError) as e:
+        ref_plan([-1, -2], [3, 4], [1], 4)
+    assert e.value.kind == "invalid_tree"
+    with pytest.raises(PlanError) as e:
+        ref_plan(ok[0], [3, 0], ok[2], 4)
+    assert e.value.kind == "invalid_tree"
+    with pytest.raises(PlanError) as e:
+        ref_plan(ok[0], ok[1], [2], 4)
+    assert e.value.kind == "invalid_tree"
+    with pytest.raises(PlanError) as e:
+        ref_plan(*ok, 0)
+    assert e.value.kind == "invalid_argument"
+    with pytest.raises(PlanError) as e:
+        ref_plan(ok[0], ok[1], [], 4)
+    assert e.value.kind == "invalid_argument"
