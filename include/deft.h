@@ -1,0 +1,221 @@
+/*
+ * deft.h - C ABI of libdeft: DeFT-style tree attention for one decode step on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * A decode step's queries each sit on a node of a prefix tree whose nodes own
+ * KV segments; a query attends to the KV of its node and of all the node's
+ * ancestors.  Sources (the DeFT pages: arXiv 2404.00242, abstract, and "DeFT
+ * Guide: Flash Tree-Attention for LLM Serving"):
+ *   - the result: "Tree-Constrained Attention Formulation" (masked softmax
+ *     over prefix and ancestor tokens, scale 1/sqrt(d));
+ *   - KV-Guided Grouping: each KV chunk is read once for every query that
+ *     needs it ("1. KV-Guided Grouping");
+ *   - Flattened Tree KV Splitting: the tree's KV is laid out as one linear
+ *     index space cut into equal token chunks ("2. Flattened Tree KV
+ *     Splitting");
+ *   - per-chunk partials with a running max m and sum l, combined by the
+ *     online-softmax rule ("The Online Softmax Tile Accumulation");
+ *   - paged KV: flattened indices map onto non-contiguous pages through a
+ *     block table ("Integration with Paged KV Caches", "2. Paged KV-Cache
+ *     Compatibility").
+ *
+ * Conventions for every call:
+ *   - integers are int32 unless stated; arrays are contiguous and row-major;
+ *   - "host" pointers are ordinary CPU memory, "device" pointers are HIP
+ *     device memory of the current device;
+ *   - streams are hipStream_t passed as void* (NULL = the null stream);
+ *   - every device-side call is asynchronous on its stream and never
+ *     synchronises the host;
+ *   - the library never allocates device memory: plan images, workspaces,
+ *     KV pools and outputs all belong to the caller;
+ *   - a call returns DEFT_OK or a negative code; deft_last_error() then
+ *     describes the failure (per thread).  Nothing aborts or throws across
+ *     this boundary.
+ *
+ * Tree encoding (borrowed, read during the call only):
+ *   parents[i]     parent of node i, or -1 for a root; must lie in [-1, i)
+ *                  (a forest is allowed)
+ *   seg_lens[i]    KV tokens owned by node i, >= 1
+ *   query_nodes[q] node that query q sits on (several queries may share a
+ *                  node; internal nodes are allowed)
+ * Logical KV order: node segments concatenated in node-id order, so node i
+ * owns logical tokens [node_start[i], node_start[i] + seg_lens[i]) with
+ * node_start the exclusive prefix sum of seg_lens.
+ *
+ * Tensor layouts:
+ *   q, out        [num_queries][num_q_heads][head_dim], dtype of desc
+ *   k_cache,      [num_pages][page_size][num_kv_heads][head_dim], dtype of desc;
+ *   v_cache       logical token t is at page block_table[t / page_size],
+ *                 row t % page_size
+ *   block_table   [ceil(total_tokens / page_size)] int32 physical page ids
+ *   query head h reads KV head h / (num_q_heads / num_kv_heads)
+ *   scale 1/sqrt(head_dim); output is the exact softmax-weighted mean of V,
+ *   rounded to the output dtype (round to nearest even for bf16).
+ */
+#ifndef DEFT_H
+#define DEFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define DEFT_OK                     0
+#define DEFT_ERR_INVALID_ARGUMENT  -1  /* null pointer, bad count, buffer too small, plan/desc mismatch */
+#define DEFT_ERR_INVALID_TREE      -2  /* parents/seg_lens/query_nodes break the encoding above */
+#define DEFT_ERR_UNSUPPORTED       -3  /* valid request outside what this build implements */
+#define DEFT_ERR_HIP               -4  /* a HIP call or kernel launch failed */
+#define DEFT_ERR_NO_MEMORY         -5  /* host allocation failed */
+
+/* Element types of q, k_cache, v_cache and out. */
+#define DEFT_DTYPE_F32   0
+#define DEFT_DTYPE_BF16  1
+
+typedef struct deft_plan deft_plan;   /* opaque, host-owned */
+
+/*
+ * Read-only view of a plan's arrays (host memory owned by the plan, valid
+ * until deft_plan_destroy).  Definitions, with T = total_tokens, C =
+ * chunk_tokens, W = mask_words = ceil(C / 32), S = num_slots:
+ *   node_start[N]          logical start of each node's segment
+ *   flat_node_order[N]     depth-first pre-order of the nodes: roots in
+ *                          ascending id, then each node's children in
+ *                          ascending id (the flattened index space of
+ *                          "2. Flattened Tree KV Splitting")
+ *   node_flat_start[N]     flat index of each node's first token
+ *   flat_to_logical[T]     logical token stored at each flat index
+ *   chunk_start[nc+1]      chunk c covers flat [c*C, min((c+1)*C, T))
+ *   group_offsets[nc+1]    CSR over chunks into slot_query
+ *   slot_query[S]          the query of each (chunk, query) slot: per chunk,
+ *                          the queries that see >= 1 of its tokens, in
+ *                          ascending query index ("1. KV-Guided Grouping")
+ *   slot_mask[S*W]         bit (t & 31) of word (t >> 5) of a slot's row is set
+ *                          iff the chunk's t-th token lies on the query's
+ *                          root-to-node path; bits at t >= chunk length are 0
+ *   chunk_full[nc]         1 iff the chunk has slots and all their bits are set
+ *   query_slot_offsets[Nq+1], query_slots[S]
+ *                          each query's slots in ascending chunk order (the
+ *                          operands of its log-sum-exp merge)
+ */
+typedef struct {
+  int32_t num_nodes;
+  int32_t num_queries;
+  int32_t chunk_tokens;
+  int32_t total_tokens;
+  int32_t num_chunks;
+  int32_t num_slots;
+  int32_t mask_words;
+  const int32_t*  node_start;
+  const int32_t*  flat_node_order;
+  const int32_t*  node_flat_start;
+  const int32_t*  flat_to_logical;
+  const int32_t*  chunk_start;
+  const int32_t*  group_offsets;
+  const int32_t*  slot_query;
+  const uint32_t* slot_mask;
+  const uint8_t*  chunk_full;
+  const int32_t*  query_slot_offsets;
+  const int32_t*  query_slots;
+} deft_plan_view;
+
+/* Shapes of one attention call. */
+typedef struct {
+  int32_t dtype;         /* DEFT_DTYPE_F32 or DEFT_DTYPE_BF16 */
+  int32_t num_q_heads;   /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* Hkv */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t page_size;     /* tokens per KV page: 16 */
+  int32_t num_pages;     /* pages in k_cache and v_cache (each) */
+} deft_attn_desc;
+
+/*
+ * Build a plan on the host (flattening, chunking, grouping, bitmasks, merge
+ * lists).  The tree arrays are host pointers read during the call only.
+ * chunk_tokens >= 1 (the attention calls support chunk_tokens <= 4096).
+ * Errors: INVALID_ARGUMENT for null pointers, num_nodes < 1,
+ * num_queries < 1 or chunk_tokens < 1; INVALID_TREE for parents[i] outside
+ * [-1, i), seg_lens[i] < 1, query_nodes[q] outside [0, num_nodes), or more
+ * than 2^31 - 1 tokens in total; NO_MEMORY.  *out_plan is set on success.
+ */
+int deft_plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                     const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
+                     deft_plan** out_plan);
+
+/* Free a plan (NULL is ignored).  The caller must first let every stream that
+ * consumes its device image get past that work. */
+void deft_plan_destroy(deft_plan* plan);
+
+/* Fill *out_view with the plan's arrays (see deft_plan_view). */
+int deft_plan_export(const deft_plan* plan, deft_plan_view* out_view);
+
+/*
+ * Sizes the caller must allocate for a given attention shape:
+ *   *plan_bytes       device image of the plan (deft_plan_upload)
+ *   *workspace_bytes  per-slot partial results (deft_tree_attention)
+ * Either output pointer may be NULL.  UNSUPPORTED if desc is outside this
+ * build (head_dim not 64/128, page_size != 16, Hq % Hkv != 0, chunk_tokens
+ * > 4096); INVALID_ARGUMENT for non-positive shapes.
+ */
+int deft_plan_device_bytes(deft_plan* plan, const deft_attn_desc* desc,
+                           size_t* plan_bytes, size_t* workspace_bytes);
+
+/*
+ * Build the plan's device image for desc (chunk metadata, masks, the
+ * flattened-to-logical map, merge lists and the kernels' work lists) and copy
+ * it into dev_plan (device memory of at least plan_bytes, 256-byte aligned)
+ * on `stream`.  The plan remembers dev_plan and desc; later attention calls
+ * read the image from there.  The plan's host staging buffer must stay alive
+ * until the copy has run (keep the plan alive until the stream passes it).
+ */
+int deft_plan_upload(deft_plan* plan, const deft_attn_desc* desc, void* dev_plan,
+                     size_t dev_plan_bytes, void* stream);
+
+/*
+ * Tree attention for one decode step: the partial-attention kernel (every
+ * chunk's KV streamed once per KV head for all its grouped queries and their
+ * query heads, bitmask applied, unnormalised per-slot partials written to
+ * the workspace) followed by the log-sum-exp merge kernel.
+ * q, k_cache, v_cache, block_table, out, workspace: device pointers.
+ * desc must equal the desc of the last deft_plan_upload.  workspace_bytes
+ * must be at least the size from deft_plan_device_bytes.  block_table
+ * entries are not range-checked on the device; an entry outside
+ * [0, num_pages) is undefined behaviour.
+ */
+int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_table, const deft_plan* plan, void* out,
+                        const deft_attn_desc* desc, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * The partial-attention kernel on its own ("The Online Softmax Tile
+ * Accumulation" applied per chunk).  For every slot s (chunk c, query q) and
+ * query head h, over the chunk's tokens visible to q:
+ *   part_m[s*Hq + h]          max of the scaled scores (natural-log domain)
+ *   part_l[s*Hq + h]          sum of exp(score - m)
+ *   part_o[(s*Hq + h)*d + e]  sum of exp(score - m) * v[e]  (unnormalised)
+ * all fp32, device pointers of S*Hq*d, S*Hq, S*Hq floats.
+ */
+int deft_partial_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const deft_plan* plan,
+                           const deft_attn_desc* desc, float* part_o, float* part_m,
+                           float* part_l, void* stream);
+
+/*
+ * The merge kernel on its own: for every query q and head h, over q's slots
+ * M = max m_s, L = sum l_s exp(m_s - M), out = sum o_s exp(m_s - M) / L,
+ * rounded to desc->dtype.  Partials in the layout of deft_partial_attention.
+ */
+int deft_lse_merge(const deft_plan* plan, const deft_attn_desc* desc, const float* part_o,
+                   const float* part_m, const float* part_l, void* out, void* stream);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* deft_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DEFT_H */

@@ -1,0 +1,183 @@
+"""HIP path against the fp64 oracle, through the C ABI, on an MI355X.
+
+Tolerance (per element, like allclose with atol = rtol = tol): 1e-5 for fp32
+inputs, 2e-2 for bf16 inputs (fp32 accumulation).  Because 2e-2 is loose
+next to the output magnitudes of some workloads, bf16 cases also check the
+error against the output's own scale (_rms_check), and closed-form cases
+(zero keys, constant values) check the mask and the gather where a stray
+token would show.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as OA
+from oracle.plan import ref_plan
+from tree_structured_decode_amd import workloads as W
+from tree_structured_decode_amd import deft as D
+
+from gpu_helpers import DEV, TOL, check_close, gpu_inputs, oracle_out, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _rms_check(got, want, what):
+    """Scale-aware check for bf16 outputs whose magnitude is far below 2e-2.
+
+    Rounding the output to bf16 costs up to 2^-9 of each value and rounding the
+    probabilities to bf16 before PV adds a little more, so the largest error
+    stays below 2^-7 of the largest output and the mean error below 2^-8 of the
+    mean output.  An all-zero or badly mixed output fails this at any scale.
+    """
+    err = np.abs(got - want)
+    top, mean = float(np.abs(want).max()), float(np.abs(want).mean())
+    assert err.max() <= 2 ** -7 * top, f"{what}: max err {err.max():.3e} above 2^-7 * {top:.3e}"
+    assert err.mean() <= 2 ** -8 * mean, f"{what}: mean err {err.mean():.3e} above 2^-8 * {mean:.3e}"
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_standard_workload_matches_oracle(cfg):
+    wl = W.standard_workload(cfg)
+    say("standard", cfg, "C", wl.chunk_tokens)
+    got, _ = run_gpu(wl)
+    want = oracle_out(wl)
+    check_close(got, want, TOL[wl.dtype], f"workload {cfg}")
+    if wl.dtype == torch.bfloat16:
+        _rms_check(got, want, f"workload {cfg}")
+
+
+@pytest.mark.parametrize("c", [16, 64, 128, 256, 1024, 4096])
+def test_spec_tree_chunk_sizes(c):
+    wl = W.standard_workload(2, unscaled=True)
+    say("spec tree unscaled C", c)
+    got, _ = run_gpu(wl, chunk_tokens=c)
+    want = oracle_out(wl)
+    check_close(got, want, 2e-2, f"C={c}")
+    _rms_check(got, want, f"C={c}")
+
+
+def test_tiny_tree_shuffled_pages_and_chunk_sizes():
+    for c in (1, 7, 16, 64, 100, 448, 4096):
+        wl = W.standard_workload(1, placement="permuted")
+        say("tiny permuted C", c)
+        got, _ = run_gpu(wl, chunk_tokens=c)
+        check_close(got, oracle_out(wl), 1e-5, f"C={c}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("seed", range(6))
+def test_random_trees(seed, dtype):
+    rng = np.random.default_rng(5000 + seed)
+    n = int(rng.integers(1, 50))
+    p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([1, 9, 80, 300])), int(rng.integers(1, 40)),
+                             forest_prob=float(rng.choice([0.0, 0.2])))
+    hkv = int(rng.choice([1, 2, 8]))
+    hq = hkv * int(rng.choice([1, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    c = int(rng.choice([16, 32, 100, 128, 512]))
+    wl = W.make_workload("rand", p, s, qn, chunk_tokens=c, hq=hq, hkv=hkv, d=d, dtype=dtype,
+                         seed=seed, placement="scattered",
+                         pool_pages=2 * (-(-int(s.sum()) // 16)) + 3)
+    say("random", seed, str(dtype), f"N={n} Nq={len(qn)} Hq={hq} Hkv={hkv} d={d} C={c}")
+    got, _ = run_gpu(wl)
+    want = oracle_out(wl)
+    check_close(got, want, TOL[dtype], f"seed {seed}")
+    if dtype == torch.bfloat16:
+        _rms_check(got, want, f"seed {seed}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_zero_keys_give_segment_weighted_mean(dtype):
+    rng = np.random.default_rng(77)
+    p, s, qn = W.random_tree(rng, 40, 1, 60, 30, forest_prob=0.05)
+    d = 128
+    wl = W.make_workload("zk", p, s, qn, chunk_tokens=64, hq=8, hkv=2, d=d, dtype=dtype, seed=3,
+                         placement="scattered", pool_pages=3 * (-(-int(s.sum()) // 16)))
+    wl.k_tokens.zero_()
+    st = OA.node_starts(s)
+    pattern = np.zeros((len(p), d))
+    for node in range(len(p)):
+        pattern[node, node % d] = node + 1.0
+        wl.v_tokens[st[node]:st[node] + s[node]] = torch.from_numpy(pattern[node]).to(dtype)
+    say("zero keys", str(dtype))
+    got, _ = run_gpu(wl)
+    for i, node in enumerate(qn):
+        path = OA.path_nodes(p, node)
+        want = sum(s[x] * pattern[x] for x in path) / sum(s[x] for x in path)
+        rel = 1e-5 if dtype == torch.float32 else 2 ** -8
+        np.testing.assert_allclose(got[i], np.broadcast_to(want, got[i].shape), rtol=rel, atol=1e-6)
+
+
+def test_constant_values_bf16():
+    wl = W.standard_workload(4)
+    wl.v_tokens[:] = torch.linspace(-2, 2, 128).to(torch.bfloat16)
+    say("constant values")
+    got, _ = run_gpu(wl)
+    want = wl.v_tokens[0, 0].double().numpy()
+    np.testing.assert_allclose(got, np.broadcast_to(want, got.shape), rtol=2 ** -8, atol=0)
+
+
+@pytest.mark.parametrize("cfg,c", [(1, 64), (3, 512), (2, 256)])
+def test_partials_match_oracle(cfg, c):
+    wl = W.standard_workload(cfg, unscaled=True) if cfg == 2 else W.standard_workload(cfg)
+    if cfg == 2:
+        wl.q = wl.q[:, :8].contiguous()     # keep the oracle quick: 2 KV heads
+        wl.k_tokens = wl.k_tokens[:, :2].contiguous()
+        wl.v_tokens = wl.v_tokens[:, :2].contiguous()
+        wl.num_q_heads, wl.num_kv_heads = 8, 2
+    say("partials", cfg, c)
+    q, kc, vc, bt = gpu_inputs(wl)
+    desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    from tree_structured_decode_amd.runner import TreeAttention
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, c, desc, device=DEV)
+    po, pm, pl = ta.partials(q, kc, vc, bt)
+    torch.cuda.synchronize()
+    plan = ref_plan(wl.parents, wl.seg_lens, wl.query_nodes, c)
+    ids, kp, vp = W.compact_pool(wl)
+    o, m, l = OA.chunk_partials(wl.q, kp, vp, wl.block_table, wl.parents, wl.seg_lens,
+                                wl.query_nodes, plan, page_ids=ids)
+    tol = TOL[wl.dtype]
+    check_close(pm.double().cpu().numpy(), m, tol, "m")
+    check_close(pl.double().cpu().numpy(), l, tol, "l")
+    po = po.double().cpu().numpy()
+    scale = np.maximum(l[:, :, None], 1.0)     # O is a sum of up to l-weighted values
+    check_close(po / scale, o / scale, tol, "O / l")
+
+
+def test_deterministic_and_writes_every_slot():
+    wl = W.standard_workload(4)
+    say("determinism")
+    inputs = gpu_inputs(wl)
+    a, _ = run_gpu(wl, inputs=inputs, poison_workspace=True)
+    b, _ = run_gpu(wl, inputs=inputs, poison_workspace=False)
+    assert np.isfinite(a).all()
+    assert np.array_equal(a, b)
+
+
+def test_single_node_single_query_and_duplicates():
+    for parents, seg, qn in [([-1], [1], [0]), ([-1], [17], [0, 0, 0]), ([-1, 0, 0], [5, 1, 1], [0, 1, 2, 1])]:
+        for dtype in (torch.float32, torch.bfloat16):
+            wl = W.make_workload("edge", parents, seg, qn, chunk_tokens=16, hq=8, hkv=2, d=128,
+                                 dtype=dtype, seed=1, placement="identity")
+            say("edge", parents, seg, qn, str(dtype))
+            got, _ = run_gpu(wl)
+            check_close(got, oracle_out(wl), TOL[dtype], "edge")
+
+
+def test_long_context_spec_tree_sampled():
+    """The 32K-prefix / 256-node tree in a pool filling ~60% of HBM, pages at
+    random positions; a sample of queries checked against the oracle."""
+    total = torch.cuda.get_device_properties(0).total_memory
+    pages = W.hbm_pool_pages(total)
+    wl = W.standard_workload(5, pool_pages=pages)
+    say("long context", "pool pages", pages)
+    q, kc, vc, bt = gpu_inputs(wl)
+    got, _ = run_gpu(wl, inputs=(q, kc, vc, bt))
+    del kc, vc
+    torch.cuda.empty_cache()
+    depth = wl.meta["depths"]
+    pick = sorted({0, 1, len(wl.query_nodes) - 1, int(np.argmax(depth)), 100, 200})
+    want = oracle_out(wl, queries=pick)
+    check_close(got[pick], want, 2e-2, "long context")
+    _rms_check(got[pick], want, "long context")
+    assert np.isfinite(got).all()

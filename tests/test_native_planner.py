@@ -1,0 +1,152 @@
+"""The native planner against the reference planner (every array bit-exact),
+its error paths, and the library's exported symbols.  Host-only: no GPU."""
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle.plan import PlanError, ref_plan
+from tree_structured_decode_amd import deft as D
+from tree_structured_decode_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KEYS = ("node_start", "flat_node_order", "node_flat_start", "flat_to_logical", "chunk_start",
+        "group_offsets", "slot_query", "slot_mask", "chunk_full", "query_slot_offsets", "query_slots")
+COUNTS = ("num_nodes", "num_queries", "chunk_tokens", "total_tokens", "num_chunks", "num_slots",
+          "mask_words")
+
+
+def assert_same_plan(native, ref):
+    for k in COUNTS:
+        assert native[k] == ref[k], k
+    for k in KEYS:
+        a, b = native[k], ref[k]
+        assert a.dtype == b.dtype, k
+        assert a.shape == b.shape, k
+        assert np.array_equal(a, b), k
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "deft.h")).read()
+    declared = set(re.findall(r"^\S.*?\b(deft_\w+)\(", header, flags=re.M))
+    assert declared == set(D.EXPORTED_SYMBOLS)
+    L = D.lib()
+    for name in declared:
+        assert getattr(L, name) is not None
+
+
+def test_single_hip_runtime_in_process():
+    D.lib()
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_standard_workloads_bit_exact(cfg):
+    wl = W.standard_workload(cfg)
+    for c in sorted({wl.chunk_tokens, 64, 128, 256}):
+        native = D.deft_plan_export(D.deft_plan_create(wl.parents, wl.seg_lens, wl.query_nodes, c))
+        assert_same_plan(native, ref_plan(wl.parents, wl.seg_lens, wl.query_nodes, c))
+
+
+@pytest.mark.parametrize("c", [1, 7, 16, 64, 100, 128, 256, 512])
+@pytest.mark.parametrize("seed", range(25))
+def test_random_trees_bit_exact(seed, c):
+    rng = np.random.default_rng(1000 + seed * 17 + c)
+    n = int(rng.integers(1, 60))
+    p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([1, 2, 5, 70, 300])), int(rng.integers(1, 20)),
+                             forest_prob=float(rng.choice([0.0, 0.1, 0.5])))
+    native = D.deft_plan_export(D.deft_plan_create(p, s, qn, c))
+    assert_same_plan(native, ref_plan(p, s, qn, c))
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.data())
+def test_fuzzed_trees_bit_exact(data):
+    n = data.draw(st.integers(1, 25))
+    parents = [-1] + [data.draw(st.integers(-1, i - 1)) for i in range(1, n)]
+    seg = [data.draw(st.integers(1, 40)) for _ in range(n)]
+    nq = data.draw(st.integers(1, 10))
+    queries = [data.draw(st.integers(0, n - 1)) for _ in range(nq)]
+    c = data.draw(st.sampled_from([1, 2, 3, 16, 31, 32, 33, 64, 128]))
+    native = D.deft_plan_export(D.deft_plan_create(parents, seg, queries, c))
+    assert_same_plan(native, ref_plan(parents, seg, queries, c))
+
+
+@pytest.mark.parametrize("args,kind", [
+    (([-1, 1], [3, 4], [1], 4), D.DEFT_ERR_INVALID_TREE),
+    (([-1, -2], [3, 4], [1], 4), D.DEFT_ERR_INVALID_TREE),
+    (([0], [3], [0], 4), D.DEFT_ERR_INVALID_TREE),
+    (([-1, 0], [3, 0], [1], 4), D.DEFT_ERR_INVALID_TREE),
+    (([-1, 0], [3, -5], [1], 4), D.DEFT_ERR_INVALID_TREE),
+    (([-1, 0], [3, 4], [2], 4), D.DEFT_ERR_INVALID_TREE),
+    (([-1, 0], [3, 4], [-1], 4), D.DEFT_ERR_INVALID_TREE),
+    (([-1, 0], [2**30, 2**30], [1], 4), D.DEFT_ERR_INVALID_TREE),
+    (([-1, 0], [3, 4], [1], 0), D.DEFT_ERR_INVALID_ARGUMENT),
+    (([-1, 0], [3, 4], [1], -3), D.DEFT_ERR_INVALID_ARGUMENT),
+    (([-1, 0], [3, 4], [], 4), D.DEFT_ERR_INVALID_ARGUMENT),
+    (([], [], [0], 4), D.DEFT_ERR_INVALID_ARGUMENT),
+])
+def test_plan_errors_match_reference(args, kind):
+    with pytest.raises(D.DeftError) as e:
+        D.deft_plan_create(*args)
+    assert e.value.code == kind
+    assert D.deft_last_error()
+    if kind == D.DEFT_ERR_INVALID_TREE and args[1] != [2**30, 2**30]:
+        with pytest.raises(PlanError) as r:
+            ref_plan(*args)
+        assert r.value.kind == "invalid_tree"
+
+
+def test_null_pointer_arguments():
+    L = D.lib()
+    import ctypes
+    h = ctypes.c_void_p()
+    assert L.deft_plan_create(None, None, 3, None, 1, 4, ctypes.byref(h)) == D.DEFT_ERR_INVALID_ARGUMENT
+    p = np.array([-1], np.int32)
+    assert L.deft_plan_create(D._ptr_i32(p), D._ptr_i32(np.array([3], np.int32)), 1,
+                              D._ptr_i32(np.array([0], np.int32)), 1, 4, None) == D.DEFT_ERR_INVALID_ARGUMENT
+    assert L.deft_plan_export(None, None) == D.DEFT_ERR_INVALID_ARGUMENT
+
+
+def test_device_bytes_and_unsupported_shapes():
+    plan = D.deft_plan_create([-1, 0], [100, 20], [1, 1, 0], 64)
+    ok = D.make_desc(torch.bfloat16, 8, 2, 128, 100)
+    pb, wb = D.deft_plan_device_bytes(plan, ok)
+    slots = D.deft_plan_export(plan)["num_slots"]
+    assert pb > 0 and wb >= slots * 8 * (128 + 2) * 4
+    for desc, code in [
+        (D.make_desc(torch.bfloat16, 8, 2, 96, 100), D.DEFT_ERR_UNSUPPORTED),
+        (D.make_desc(torch.bfloat16, 8, 3, 128, 100), D.DEFT_ERR_UNSUPPORTED),
+        (D.make_desc(torch.float16, 8, 2, 128, 100), D.DEFT_ERR_UNSUPPORTED),
+        (D.make_desc(torch.bfloat16, 8, 2, 128, 100, page_size=32), D.DEFT_ERR_UNSUPPORTED),
+        (D.make_desc(torch.bfloat16, 0, 2, 128, 100), D.DEFT_ERR_INVALID_ARGUMENT),
+        (D.make_desc(torch.bfloat16, 8, 2, 128, 0), D.DEFT_ERR_INVALID_ARGUMENT),
+    ]:
+        with pytest.raises(D.DeftError) as e:
+            D.deft_plan_device_bytes(plan, desc)
+        assert e.value.code == code
+    big = D.deft_plan_create([-1], [10000], [0], 8192)
+    with pytest.raises(D.DeftError) as e:
+        D.deft_plan_device_bytes(big, ok)
+    assert e.value.code == D.DEFT_ERR_UNSUPPORTED
+
+
+def test_attention_rejects_plan_without_upload():
+    import ctypes
+    plan = D.deft_plan_create([-1, 0], [100, 20], [1], 64)
+    desc = D.make_desc(torch.bfloat16, 8, 2, 128, 100)
+    L = D.lib()
+    fake = ctypes.c_void_p(256)
+    rc = L.deft_tree_attention(fake, fake, fake, fake, plan.handle, fake, ctypes.byref(desc), fake,
+                               1 << 20, None)
+    assert rc == D.DEFT_ERR_INVALID_ARGUMENT
+    assert "upload" in D.deft_last_error()
+    rc = L.deft_plan_upload(plan.handle, ctypes.byref(desc), ctypes.c_void_p(100), 1 << 20, None)
+    assert rc == D.DEFT_ERR_INVALID_ARGUMENT and "aligned" in D.deft_last_error()
+    rc = L.deft_plan_upload(plan.handle, ctypes.byref(desc), None, 1 << 20, None)
+    assert rc == D.DEFT_ERR_INVALID_ARGUMENT

@@ -1,0 +1,822 @@
+// DeFT tree attention on gfx950: partial-attention kernels and the
+// log-sum-exp merge kernel, plus the C-ABI entry points that launch them.
+//
+// Sources (the DeFT pages: arXiv 2404.00242, abstract; "DeFT Guide: Flash
+// Tree-Attention for LLM Serving"):
+//   - "Tree-Constrained Attention Formulation": a query attends, with scale
+//     1/sqrt(d), to the tokens of its node and of every ancestor;
+//   - "1. KV-Guided Grouping": a chunk of KV is read from HBM once for all
+//     queries that need it; here one work-group streams one chunk for one KV
+//     head and scores every grouped query and every query head sharing that
+//     KV head (grouped-query attention), the tree bitmask selecting the
+//     visible tokens;
+//   - "2. Flattened Tree KV Splitting": the work unit is an equal-sized chunk
+//     of the flattened tree KV;
+//   - "The Online Softmax Tile Accumulation": running max, running sum and a
+//     rescaled output accumulator per row; per-chunk results (O, m, l) are
+//     merged by the same rule in a second kernel;
+//   - "Integration with Paged KV Caches" / "2. Paged KV-Cache Compatibility":
+//     a chunk's flat tokens are mapped to pool rows through the block table
+//     once per work-group, outside the inner loops.
+//
+// Row convention: for KV head g and chunk c with group slots j = 0..n-1, row
+// r = j * G + hh is slot j's query on query head g * G + hh (G = Hq / Hkv).
+//
+// Two partial kernels share the work description:
+//   mfma_partial  bf16 groups with >= 16 rows: 16x16x32 bf16 MFMA for S = K Q^T
+//                 and O^T = V^T P^T, 64 rows per work-group, the chunk's
+//                 tokens split across 4 waves and the waves merged in LDS;
+//   valu_partial  fp32 inputs and bf16 groups below one MFMA tile: per-token
+//                 dot products with wavefront reductions.
+// Scores are kept in log2 units (scale * log2(e) folded in) so exp2 is used;
+// the stored m is converted back to natural-log units.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "deft_internal.h"
+
+namespace deft {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kNegInf = -INFINITY;
+// A running max is only raised once a row's max exceeds it by this many
+// log2 units; the probabilities then stay below 2^8 and the accumulators
+// are rescaled rarely.  The stored partial is renormalised to the true max.
+constexpr float kRescaleSlack = 8.0f;
+
+struct DevPlan {
+  const int32_t* chunk_start;
+  const int32_t* group_offsets;
+  const int32_t* chunk_full;
+  const int32_t* slot_query;
+  const uint32_t* slot_mask;
+  const int32_t* flat_to_logical;
+  const int32_t* query_slot_offsets;
+  const int32_t* query_slots;
+  const int4* mfma_items;
+  const int4* valu_items;
+  int32_t n_mfma, n_valu, mask_words, num_queries;
+};
+
+struct PartialArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  float* po;
+  float* pm;
+  float* pl;
+  DevPlan plan;
+  int32_t hq, hkv, grp;
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+
+__device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+
+__device__ inline uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                      // round to nearest even
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kPerLoad = 4;
+  __device__ static void unpack(const u32x4& r, float* out) {
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(r[i]);
+  }
+  __device__ static void store(void* base, size_t idx, float x) { static_cast<float*>(base)[idx] = x; }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kPerLoad = 8;
+  __device__ static void unpack(const u32x4& r, float* out) {
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(r[i] << 16);
+      out[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(void* base, size_t idx, float x) {
+    static_cast<uint16_t*>(base)[idx] = f32_to_bf16(x);
+  }
+};
+
+__device__ inline u32x4 load16(const void* base, int64_t elem_off, int elem_bytes) {
+  return *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + elem_off * elem_bytes);
+}
+
+// Pool row (page * 16 + slot) of every flat token of the chunk, into LDS.
+__device__ inline void stage_token_rows(int32_t* tok_row, const DevPlan& P, const int32_t* bt,
+                                        int32_t cs, int32_t len) {
+  for (int32_t t = threadIdx.x; t < len; t += blockDim.x) {
+    const int32_t lt = P.flat_to_logical[cs + t];
+    tok_row[t] = bt[lt >> 4] * kPageSize + (lt & (kPageSize - 1));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// VALU partial kernel: up to 16 rows per work-group.  Lanes are grouped LPT
+// per token (each lane holds 16 bytes of the token's K and V row); a wave
+// covers TPW tokens per step and the 4 waves interleave over the chunk.
+// Each lane group keeps its own online-softmax state; groups and waves are
+// merged at the end.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
+  constexpr int EPL = Elem<T>::kPerLoad;
+  constexpr int LPT = D / EPL;
+  constexpr int TPW = 64 / LPT;
+  constexpr int NW = 4;
+  constexpr int R = kValuRows;
+  __shared__ int32_t tok_row[kMaxChunkTokens];
+  __shared__ uint32_t masks[R * (kMaxChunkTokens / 32)];
+  __shared__ float red[NW][R][D + 2];
+
+  const DevPlan& P = a.plan;
+  const int g = blockIdx.x % a.hkv;
+  const int4 item = P.valu_items[blockIdx.x / a.hkv];
+  const int32_t c = item.x, rb = item.y, nr = item.z;
+  const int32_t cs = P.chunk_start[c], len = P.chunk_start[c + 1] - cs;
+  const int32_t gofs = P.group_offsets[c];
+  const bool full = P.chunk_full[c] != 0;
+  const int W = P.mask_words;
+  const int j0 = rb / a.grp;
+  const int nslot = (rb + nr - 1) / a.grp - j0 + 1;
+
+  stage_token_rows(tok_row, P, a.block_table, cs, len);
+  if (!full)
+    for (int i = threadIdx.x; i < nslot * W; i += blockDim.x)
+      masks[i] = P.slot_mask[static_cast<size_t>(gofs + j0) * W + i];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tg = lane / LPT, li = lane % LPT;
+  constexpr int EB = sizeof(T);
+
+  float qv[R][EPL];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < nr) {
+      const int row = rb + r;
+      const int32_t qi = P.slot_query[gofs + row / a.grp];
+      const int head = g * a.grp + row % a.grp;
+      float tmp[EPL];
+      Elem<T>::unpack(load16(a.q, (static_cast<int64_t>(qi) * a.hq + head) * D + li * EPL, EB), tmp);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[r][e] = tmp[e] * a.scale_log2;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[r][e] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  float m[R], l[R], o[R][EPL];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = kNegInf;
+    l[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[r][e] = 0.f;
+  }
+
+  const int64_t head_off = static_cast<int64_t>(g) * D + li * EPL;
+  auto fetch = [&](int t, u32x4& kr, u32x4& vr) {
+    if (t < len) {
+      const int64_t off = static_cast<int64_t>(tok_row[t]) * a.hkv * D + head_off;
+      kr = load16(a.k, off, EB);
+      vr = load16(a.v, off, EB);
+    } else {
+      kr = u32x4{0, 0, 0, 0};
+      vr = u32x4{0, 0, 0, 0};
+    }
+  };
+
+  constexpr int STRIDE = NW * TPW;
+  int t = w * TPW + tg;
+  u32x4 kr, vr, kn, vn;
+  fetch(t, kr, vr);
+  for (int base = 0; base < len; base += STRIDE, t += STRIDE) {
+    fetch(t + STRIDE, kn, vn);
+    float kf[EPL], vf[EPL];
+    Elem<T>::unpack(kr, kf);
+    Elem<T>::unpack(vr, vf);
+    const bool valid = t < len;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r >= nr) continue;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s = fmaf(qv[r][e], kf[e], s);
+#pragma unroll
+      for (int x = LPT / 2; x >= 1; x >>= 1) s += __shfl_xor(s, x);
+      bool vis = valid;
+      if (!full && valid) {
+        const int j = (rb + r) / a.grp - j0;
+        vis = (masks[j * W + (t >> 5)] >> (t & 31)) & 1u;
+      }
+      if (vis) {
+        const float mn = fmaxf(m[r], s);
+        const float alpha = exp2f(m[r] - mn);  // m = -inf gives 0
+        const float p = exp2f(s - mn);
+        l[r] = l[r] * alpha + p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e] * alpha);
+        m[r] = mn;
+      }
+    }
+    kr = kn;
+    vr = vn;
+  }
+
+  // Merge the lane groups of this wave, then the waves.
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= nr) continue;
+    float mx = m[r];
+#pragma unroll
+    for (int x = LPT; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+    const float f = (m[r] == kNegInf) ? 0.f : exp2f(m[r] - mx);
+    float lsum = l[r] * f;
+#pragma unroll
+    for (int x = LPT; x < 64; x <<= 1) lsum += __shfl_xor(lsum, x);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float ov = o[r][e] * f;
+#pragma unroll
+      for (int x = LPT; x < 64; x <<= 1) ov += __shfl_xor(ov, x);
+      o[r][e] = ov;
+    }
+    if (tg == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red[w][r][li * EPL + e] = o[r][e];
+      if (li == 0) {
+        red[w][r][D] = mx;
+        red[w][r][D + 1] = lsum;
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
+    const int r = idx / D, e = idx % D;
+    float mx = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, red[ww][r][D]);
+    float ov = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float mw = red[ww][r][D];
+      const float f = (mw == kNegInf) ? 0.f : exp2f(mw - mx);
+      ov += f * red[ww][r][e];
+      lsum += f * red[ww][r][D + 1];
+    }
+    const int row = rb + r;
+    const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
+    a.po[sh * D + e] = ov;
+    if (e == 0) {
+      a.pm[sh] = mx == kNegInf ? kNegInf : mx * kLn2;
+      a.pl[sh] = lsum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA partial kernel (bf16).  Work-group = 4 waves on one (chunk, KV head,
+// block of up to 64 rows).  Wave w takes the chunk's 32-token steps w, w+4,
+// ...; for each step it computes S^T = K Q^T (16x16x32 MFMA: A = K rows, B =
+// Q^T) for 2 token tiles x 4 row tiles, applies the mask and the online
+// softmax on the S^T fragments in registers, and accumulates
+// O^T += V^T P^T (A = V^T read from LDS, B = P^T straight from the S^T
+// fragments).  K tile rows are permuted so that every lane ends up holding 8
+// consecutive tokens of one row, which is the B-operand layout of the PV
+// product.  V is transposed through a wave-private LDS tile.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
+  constexpr int NW = 4;
+  constexpr int NRT = kMfmaRows / 16;  // row tiles per wave
+  constexpr int KS = D / 32;           // k-steps of S = K Q^T
+  constexpr int DT = D / 16;           // d-tiles of O^T
+  constexpr int VT_STRIDE = 40;        // bf16 per V^T row: 32 tokens + 8 padding (80 bytes)
+  constexpr int UNITS = D / 64;        // 4-token x 8-d V pieces per lane per step
+  constexpr int VT_BYTES = NW * D * VT_STRIDE * 2;
+  constexpr int RED_BYTES = NW * kMfmaRows * 32 * 4;
+  __shared__ int32_t tok_row[kMaxChunkTokens];
+  __shared__ __attribute__((aligned(16))) char smem[VT_BYTES > RED_BYTES ? VT_BYTES : RED_BYTES];
+  __shared__ float stats[NW][kMfmaRows][3];
+
+  const DevPlan& P = a.plan;
+  const int g = blockIdx.x % a.hkv;
+  const int4 item = P.mfma_items[blockIdx.x / a.hkv];
+  const int32_t c = item.x, rb = item.y, nr = item.z;
+  const int32_t cs = P.chunk_start[c], len = P.chunk_start[c + 1] - cs;
+  const int32_t gofs = P.group_offsets[c];
+  const bool full = P.chunk_full[c] != 0;
+  const int W = P.mask_words;
+
+  stage_token_rows(tok_row, P, a.block_table, cs, len);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lj = lane >> 4;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k);
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v);
+
+  // Q^T fragments (B operand of S^T = K Q^T) and each row's slot.
+  bf16x8 qf[NRT][KS];
+  int32_t slot_of[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int r = rt * 16 + lr;
+    slot_of[rt] = -1;
+    if (r < nr) {
+      const int row = rb + r;
+      slot_of[rt] = gofs + row / a.grp;
+      const int32_t qi = P.slot_query[slot_of[rt]];
+      const int head = g * a.grp + row % a.grp;
+      const uint16_t* src = qp + (static_cast<int64_t>(qi) * a.hq + head) * D + lj * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[rt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 32));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+  }
+  __syncthreads();
+
+  f32x4 o[DT][NRT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NRT], m_true[NRT], l_part[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    m_run[rt] = kNegInf;
+    m_true[rt] = kNegInf;
+    l_part[rt] = 0.f;
+  }
+
+  const int64_t hstride = static_cast<int64_t>(a.hkv) * D;
+  const int64_t goff = static_cast<int64_t>(g) * D;
+  // K rows held by this lane in the two 16-token tiles of a step.
+  const int tk0 = 8 * (lr >> 2) + (lr & 3);
+  const int tk1 = tk0 + 4;
+
+  auto load_k = [&](int base, bf16x8 (&kf)[2][KS]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = base + (tt ? tk1 : tk0);
+      if (t < len) {
+        const uint16_t* src = kp + tok_row[t] * hstride + goff + lj * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kf[tt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 32));
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[tt][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      }
+    }
+  };
+  // V pieces: unit u covers tokens 4*qd .. 4*qd+3 of the step and d 8*dc .. 8*dc+7.
+  auto load_v = [&](int base, u32x4 (&vr)[UNITS][4]) {
+#pragma unroll
+    for (int u = 0; u < UNITS; ++u) {
+      const int unit = u * 64 + lane;
+      const int dc = unit % (D / 8), qd = unit / (D / 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = base + 4 * qd + i;
+        if (t < len)
+          vr[u][i] = *reinterpret_cast<const u32x4*>(vp + tok_row[t] * hstride + goff + dc * 8);
+        else
+          vr[u][i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto load_mask = [&](int base, uint32_t (&mw)[NRT]) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+      mw[rt] = (full || slot_of[rt] < 0) ? 0u
+               : P.slot_mask[static_cast<size_t>(slot_of[rt]) * W + (base >> 5)];
+  };
+
+  uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + w * D * VT_STRIDE;
+  const int nsteps = (len + 31) / 32;
+  bf16x8 kf[2][KS];
+  u32x4 vr[UNITS][4];
+  uint32_t mw[NRT];
+  if (w < nsteps) {
+    load_k(w * 32, kf);
+    load_v(w * 32, vr);
+    load_mask(w * 32, mw);
+  }
+  for (int step = w; step < nsteps; step += NW) {
+    const int base = step * 32;
+    // V^T for this step into the wave's LDS tile (pairs of tokens packed per dword).
+#pragma unroll
+    for (int u = 0; u < UNITS; ++u) {
+      const int unit = u * 64 + lane;
+      const int dc = unit % (D / 8), qd = unit / (D / 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wd = e >> 1;
+        uint32_t lo, hi;
+        if (e & 1) {
+          lo = (vr[u][0][wd] >> 16) | (vr[u][1][wd] & 0xffff0000u);
+          hi = (vr[u][2][wd] >> 16) | (vr[u][3][wd] & 0xffff0000u);
+        } else {
+          lo = (vr[u][0][wd] & 0xffffu) | (vr[u][1][wd] << 16);
+          hi = (vr[u][2][wd] & 0xffffu) | (vr[u][3][wd] << 16);
+        }
+        *reinterpret_cast<u32x2*>(vt + (dc * 8 + e) * VT_STRIDE + qd * 4) = u32x2{lo, hi};
+      }
+    }
+    const bool more = step + NW < nsteps;
+    if (more) load_v(base + NW * 32, vr);
+    uint32_t mw_cur[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) mw_cur[rt] = mw[rt];
+    if (more) load_mask(base + NW * 32, mw);
+
+    // S^T = K Q^T for 2 token tiles x NRT row tiles.
+    f32x4 s[2][NRT];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[rt][ks], acc, 0, 0, 0);
+        s[tt][rt] = acc;
+      }
+    if (more) load_k(base + NW * 32, kf);
+
+    // Mask, online softmax; P^T fragments as bf16.  Lane holds tokens
+    // base + 8*lj + e (e = 0..7) of row lr in each row tile.
+    bf16x8 pb[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      if (rt * 16 >= nr) {
+        pb[rt] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+        continue;
+      }
+      const uint32_t bits = (mw_cur[rt] >> (8 * lj)) & 0xffu;
+      float z[8];
+      float mx = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float sv = (e < 4 ? s[0][rt][e] : s[1][rt][e - 4]) * a.scale_log2;
+        const int t = base + 8 * lj + e;
+        const bool vis = slot_of[rt] >= 0 && t < len && (full || ((bits >> e) & 1u));
+        z[e] = vis ? sv : kNegInf;
+        mx = fmaxf(mx, z[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m_true[rt] = fmaxf(m_true[rt], mx);
+      const bool raise = mx > m_run[rt] + kRescaleSlack || (m_run[rt] == kNegInf && mx != kNegInf);
+      if (__any(raise)) {
+        const float mn = raise ? mx : m_run[rt];
+        const float alpha = raise ? exp2f(m_run[rt] - mn) : 1.f;
+        m_run[rt] = mn;
+        l_part[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+      }
+      f32x8 p;
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = z[e] == kNegInf ? 0.f : exp2f(z[e] - m_run[rt]);
+        ls += p[e];
+      }
+      l_part[rt] += ls;
+      pb[rt] = __builtin_convertvector(p, bf16x8);
+    }
+
+    // O^T += V^T P^T.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V^T writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + (dt * 16 + lr) * VT_STRIDE + lj * 8);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+        if (rt * 16 < nr) o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rt], o[dt][rt], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // Combine the four waves: true max, per-wave weights, summed l and O.
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    float ls = l_part[rt];
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    if (lj == 0) {
+      stats[w][rt * 16 + lr][0] = m_run[rt];
+      stats[w][rt * 16 + lr][1] = m_true[rt];
+      stats[w][rt * 16 + lr][2] = ls;
+    }
+  }
+  __syncthreads();
+  float wself[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int r = rt * 16 + lr;
+    float mx = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, stats[ww][r][1]);
+    wself[rt] = (m_run[rt] == kNegInf) ? 0.f : exp2f(m_run[rt] - mx);
+  }
+  // Reuse the V^T tiles as the reduction buffer: 32 d-values per pass.
+  float* red = reinterpret_cast<float*>(smem);  // [NW][64 rows][32]
+  for (int pass = 0; pass < DT / 2; ++pass) {
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int dt = pass * 2 + h;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          red[(w * kMfmaRows + rt * 16 + lr) * 32 + h * 16 + lj * 4 + i] = o[dt][rt][i] * wself[rt];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nr * 32; idx += blockDim.x) {
+      const int r = idx >> 5, e = idx & 31;
+      float ov = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) ov += red[(ww * kMfmaRows + r) * 32 + e];
+      const int row = rb + r;
+      const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
+      a.po[sh * D + pass * 32 + e] = ov;
+    }
+  }
+  for (int r = threadIdx.x; r < nr; r += blockDim.x) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, stats[ww][r][1]);
+    float ls = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float mr = stats[ww][r][0];
+      ls += (mr == kNegInf) ? 0.f : exp2f(mr - mx) * stats[ww][r][2];
+    }
+    const int row = rb + r;
+    const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
+    a.pm[sh] = mx == kNegInf ? kNegInf : mx * kLn2;
+    a.pl[sh] = ls;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge kernel: one wave per (query, query head); lanes split head_dim.
+// out = sum_s o_s exp(m_s - M) / sum_s l_s exp(m_s - M), M = max_s m_s.
+// ---------------------------------------------------------------------------
+struct MergeArgs {
+  const float* po;
+  const float* pm;
+  const float* pl;
+  void* out;
+  const int32_t* query_slot_offsets;
+  const int32_t* query_slots;
+  int32_t nq, hq;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.nq * a.hq) return;
+  const int qi = pair / a.hq, h = pair % a.hq;
+  const int s0 = a.query_slot_offsets[qi], s1 = a.query_slot_offsets[qi + 1];
+  float mx = kNegInf;
+  for (int i = s0 + lane; i < s1; i += 64)
+    mx = fmaxf(mx, a.pm[static_cast<int64_t>(a.query_slots[i]) * a.hq + h]);
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float lsum = 0.f;
+  for (int i0 = s0; i0 < s1; i0 += 64) {
+    const int n = min(64, s1 - i0);
+    int64_t sh_mine = 0;
+    float w_mine = 0.f;
+    if (lane < n) {
+      sh_mine = static_cast<int64_t>(a.query_slots[i0 + lane]) * a.hq + h;
+      const float mv = a.pm[sh_mine];
+      w_mine = mv == kNegInf ? 0.f : __expf(mv - mx);
+      lsum += w_mine * a.pl[sh_mine];
+    }
+    for (int j = 0; j < n; ++j) {
+      const float wj = __shfl(w_mine, j);
+      const int64_t sh = __shfl(sh_mine, j);
+      const float* src = a.po + sh * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, src[e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) lsum += __shfl_xor(lsum, x);
+  const float inv = 1.f / lsum;
+  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) Elem<T>::store(a.out, ob + e, acc[e] * inv);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+static DevPlan make_dev_plan(const deft_plan* p) {
+  const int32_t* b = static_cast<const int32_t*>(p->dev);
+  const ImageLayout& L = p->layout;
+  DevPlan d;
+  d.chunk_start = b + L.chunk_start;
+  d.group_offsets = b + L.group_offsets;
+  d.chunk_full = b + L.chunk_full;
+  d.slot_query = b + L.slot_query;
+  d.slot_mask = reinterpret_cast<const uint32_t*>(b + L.slot_mask);
+  d.flat_to_logical = b + L.flat_to_logical;
+  d.query_slot_offsets = b + L.query_slot_offsets;
+  d.query_slots = b + L.query_slots;
+  d.mfma_items = reinterpret_cast<const int4*>(b + L.mfma_items);
+  d.valu_items = reinterpret_cast<const int4*>(b + L.valu_items);
+  d.n_mfma = L.n_mfma;
+  d.n_valu = L.n_valu;
+  d.mask_words = p->mask_words;
+  d.num_queries = p->num_queries;
+  return d;
+}
+
+static int hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DEFT_OK;
+  return fail(DEFT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+static bool same_desc(const deft_attn_desc& x, const deft_attn_desc& y) {
+  return x.dtype == y.dtype && x.num_q_heads == y.num_q_heads && x.num_kv_heads == y.num_kv_heads &&
+         x.head_dim == y.head_dim && x.page_size == y.page_size && x.num_pages == y.num_pages;
+}
+
+static int check_ready(const deft_plan* p, const deft_attn_desc* d) {
+  if (!p) return fail(DEFT_ERR_INVALID_ARGUMENT, "plan is NULL");
+  int rc = check_desc(p, d);
+  if (rc) return rc;
+  if (!p->uploaded) return fail(DEFT_ERR_INVALID_ARGUMENT, "plan has no device image: call deft_plan_upload");
+  if (!same_desc(p->desc, *d))
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "desc differs from the desc the plan was uploaded for");
+  if (static_cast<int64_t>(d->num_pages) * kPageSize > INT32_MAX)
+    return fail(DEFT_ERR_UNSUPPORTED, "num_pages * page_size must fit in int32");
+  return DEFT_OK;
+}
+
+template <typename T, int D>
+static int launch_partials(const PartialArgs& pa, hipStream_t st) {
+  const int hkv = pa.hkv;
+  if (pa.plan.n_mfma > 0) {
+    if constexpr (sizeof(T) == 2) {
+      hipLaunchKernelGGL(mfma_partial<D>, dim3(pa.plan.n_mfma * hkv), dim3(256), 0, st, pa);
+      int rc = hip_check(hipGetLastError(), "launch of mfma_partial");
+      if (rc) return rc;
+    } else {
+      return fail(DEFT_ERR_UNSUPPORTED, "MFMA work for fp32 inputs");
+    }
+  }
+  if (pa.plan.n_valu > 0) {
+    hipLaunchKernelGGL((valu_partial<T, D>), dim3(pa.plan.n_valu * hkv), dim3(256), 0, st, pa);
+    int rc = hip_check(hipGetLastError(), "launch of valu_partial");
+    if (rc) return rc;
+  }
+  return DEFT_OK;
+}
+
+static int run_partials(const void* q, const void* k, const void* v, const int32_t* bt,
+                        const deft_plan* p, const deft_attn_desc* d, float* po, float* pm,
+                        float* pl, hipStream_t st) {
+  if (!q || !k || !v || !bt || !po || !pm || !pl)
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "device pointers must not be NULL");
+  PartialArgs pa;
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.block_table = bt;
+  pa.po = po;
+  pa.pm = pm;
+  pa.pl = pl;
+  pa.plan = make_dev_plan(p);
+  pa.hq = d->num_q_heads;
+  pa.hkv = d->num_kv_heads;
+  pa.grp = d->num_q_heads / d->num_kv_heads;
+  pa.scale_log2 = kLog2e / std::sqrt(static_cast<float>(d->head_dim));
+  if (d->dtype == DEFT_DTYPE_BF16)
+    return d->head_dim == 128 ? launch_partials<uint16_t, 128>(pa, st) : launch_partials<uint16_t, 64>(pa, st);
+  return d->head_dim == 128 ? launch_partials<float, 128>(pa, st) : launch_partials<float, 64>(pa, st);
+}
+
+static int run_merge(const deft_plan* p, const deft_attn_desc* d, const float* po, const float* pm,
+                     const float* pl, void* out, hipStream_t st) {
+  if (!po || !pm || !pl || !out) return fail(DEFT_ERR_INVALID_ARGUMENT, "device pointers must not be NULL");
+  MergeArgs ma;
+  ma.po = po;
+  ma.pm = pm;
+  ma.pl = pl;
+  ma.out = out;
+  const DevPlan dp = make_dev_plan(p);
+  ma.query_slot_offsets = dp.query_slot_offsets;
+  ma.query_slots = dp.query_slots;
+  ma.nq = p->num_queries;
+  ma.hq = d->num_q_heads;
+  const int blocks = (ma.nq * ma.hq + 3) / 4;
+  if (d->dtype == DEFT_DTYPE_BF16) {
+    if (d->head_dim == 128) hipLaunchKernelGGL((lse_merge<uint16_t, 128>), dim3(blocks), dim3(256), 0, st, ma);
+    else hipLaunchKernelGGL((lse_merge<uint16_t, 64>), dim3(blocks), dim3(256), 0, st, ma);
+  } else {
+    if (d->head_dim == 128) hipLaunchKernelGGL((lse_merge<float, 128>), dim3(blocks), dim3(256), 0, st, ma);
+    else hipLaunchKernelGGL((lse_merge<float, 64>), dim3(blocks), dim3(256), 0, st, ma);
+  }
+  return hip_check(hipGetLastError(), "launch of lse_merge");
+}
+
+}  // namespace deft
+
+using deft::fail;
+
+extern "C" {
+
+int deft_plan_upload(deft_plan* p, const deft_attn_desc* d, void* dev_plan, size_t bytes, void* stream) {
+  if (!p || !dev_plan) return fail(DEFT_ERR_INVALID_ARGUMENT, "plan and dev_plan must not be NULL");
+  if (reinterpret_cast<uintptr_t>(dev_plan) % 256 != 0)
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "dev_plan must be 256-byte aligned");
+  deft::ImageLayout L{};
+  int rc = deft::build_image(p, d, &p->staging, &L);
+  if (rc) return rc;
+  if (bytes < 4 * L.total_words) return fail(DEFT_ERR_INVALID_ARGUMENT, "dev_plan buffer too small");
+  rc = deft::hip_check(hipMemcpyAsync(dev_plan, p->staging.data(), 4 * L.total_words,
+                                      hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)),
+                       "hipMemcpyAsync of the plan image");
+  if (rc) return rc;
+  p->layout = L;
+  p->desc = *d;
+  p->dev = dev_plan;
+  p->dev_bytes = bytes;
+  p->uploaded = true;
+  return DEFT_OK;
+}
+
+int deft_partial_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const deft_plan* plan,
+                           const deft_attn_desc* desc, float* part_o, float* part_m, float* part_l,
+                           void* stream) {
+  int rc = deft::check_ready(plan, desc);
+  if (rc) return rc;
+  return deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, part_o, part_m, part_l,
+                            static_cast<hipStream_t>(stream));
+}
+
+int deft_lse_merge(const deft_plan* plan, const deft_attn_desc* desc, const float* part_o,
+                   const float* part_m, const float* part_l, void* out, void* stream) {
+  int rc = deft::check_ready(plan, desc);
+  if (rc) return rc;
+  return deft::run_merge(plan, desc, part_o, part_m, part_l, out, static_cast<hipStream_t>(stream));
+}
+
+int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_table, const deft_plan* plan, void* out,
+                        const deft_attn_desc* desc, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  int rc = deft::check_ready(plan, desc);
+  if (rc) return rc;
+  if (!workspace || !out) return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace and out must not be NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  const size_t need = deft::workspace_bytes_for(plan, desc);
+  if (workspace_bytes < need) return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace too small");
+  const size_t sh = static_cast<size_t>(plan->num_slots) * desc->num_q_heads;
+  auto align = [](size_t n) { return (n + 63) & ~static_cast<size_t>(63); };
+  float* po = static_cast<float*>(workspace);
+  float* pm = po + align(sh * desc->head_dim);
+  float* pl = pm + align(sh);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, po, pm, pl, st);
+  if (rc) return rc;
+  return deft::run_merge(plan, desc, po, pm, pl, out, st);
+}
+
+}  // extern "C"

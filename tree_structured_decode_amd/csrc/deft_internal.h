@@ -1,0 +1,67 @@
+// Internal declarations shared by the host planner and the HIP launchers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "deft.h"
+
+namespace deft {
+
+// Largest chunk the attention kernels stage (token row indices and masks of
+// one chunk live in LDS).
+constexpr int kMaxChunkTokens = 4096;
+constexpr int kPageSize = 16;
+
+// Row blocking of the work lists.  A "row" is one (slot, query head) pair of
+// a chunk: rows of chunk c are r = j * G + hh for the chunk's j-th slot and
+// the hh-th query head of the KV head being processed (G = Hq / Hkv).
+constexpr int kMfmaRows = 64;      // rows per MFMA work item (4 tiles of 16)
+constexpr int kMfmaMinRows = 16;   // a chunk needs this many rows to use MFMA
+constexpr int kValuRows = 16;      // rows per VALU work item
+
+struct WorkItem {                  // matches int4 on the device
+  int32_t chunk;
+  int32_t row_begin;
+  int32_t row_count;
+  int32_t pad;
+};
+
+// Offsets (in 4-byte words) of each array inside the device image.
+struct ImageLayout {
+  size_t chunk_start, group_offsets, chunk_full, slot_query, slot_mask, flat_to_logical,
+      query_slot_offsets, query_slots, mfma_items, valu_items, total_words;
+  int32_t n_mfma, n_valu;
+};
+
+void set_error(const std::string& msg);
+int fail(int code, const std::string& msg);
+
+}  // namespace deft
+
+struct deft_plan {
+  int32_t num_nodes = 0, num_queries = 0, chunk_tokens = 0, total_tokens = 0;
+  int32_t num_chunks = 0, num_slots = 0, mask_words = 0;
+  std::vector<int32_t> node_start, flat_node_order, node_flat_start, flat_to_logical;
+  std::vector<int32_t> chunk_start, group_offsets, slot_query, query_slot_offsets, query_slots;
+  std::vector<uint32_t> slot_mask;
+  std::vector<uint8_t> chunk_full;
+
+  // Device image for the last uploaded desc.
+  bool uploaded = false;
+  deft_attn_desc desc{};
+  void* dev = nullptr;
+  size_t dev_bytes = 0;
+  deft::ImageLayout layout{};
+  std::vector<int32_t> staging;
+};
+
+namespace deft {
+// Validates desc against the plan; fills the work lists and layout for it.
+int build_image(deft_plan* p, const deft_attn_desc* desc, std::vector<int32_t>* image,
+                ImageLayout* layout);
+int check_desc(const deft_plan* p, const deft_attn_desc* desc);
+size_t workspace_bytes_for(const deft_plan* p, const deft_attn_desc* desc);
+}  // namespace deft

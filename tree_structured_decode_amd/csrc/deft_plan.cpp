@@ -1,0 +1,331 @@
+// Host tree planner: Flattened Tree KV Splitting and KV-Guided Grouping.
+//
+// Sources (DeFT, arXiv 2404.00242, abstract; "DeFT Guide: Flash Tree-Attention
+// for LLM Serving", sections "1. KV-Guided Grouping", "2. Flattened Tree KV
+// Splitting", "Tree-Constrained Attention Formulation").  The tree's KV is
+// laid out in one linear (flat) index space, cut into equal chunks of
+// chunk_tokens, and for every chunk the queries that need any of its tokens
+// form one group, so the chunk is loaded once for all of them.  Readings
+// where the pages leave the details open:
+//   - flat order is a depth-first pre-order, roots and children by ascending
+//     id, so every subtree (and every node's segment) is one flat interval;
+//   - chunks are fixed windows from flat index 0 and may cross node
+//     boundaries; only the last one may be short;
+//   - a chunk's group is every query that sees at least one of its tokens,
+//     in ascending query index; one "slot" per (chunk, query);
+//   - bit t of a slot's mask row is set iff the chunk's t-th token belongs to
+//     a node on the query's root-to-node path (its own node included).
+//
+// Method: a query's visible tokens are the segments of its path nodes, and
+// in pre-order those segments appear at increasing flat positions.  Walking
+// each path from the root down therefore touches chunks in ascending order,
+// which yields the groups, the per-query merge lists and the mask bit runs
+// in one pass over the paths, with no per-token visibility test.
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "deft_internal.h"
+
+namespace deft {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int fail(int code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+static int build_plan(deft_plan* p, const int32_t* parents, const int32_t* seg_lens,
+                      int32_t n, const int32_t* query_nodes, int32_t nq, int32_t c) {
+  // Logical layout: segments in node-id order.
+  p->node_start.resize(n);
+  int64_t run = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    p->node_start[i] = static_cast<int32_t>(run);
+    run += seg_lens[i];
+  }
+  const int32_t total = static_cast<int32_t>(run);
+
+  // Children in CSR form; filling in ascending i keeps each list ascending.
+  std::vector<int32_t> child_off(n + 1, 0), child(n), roots;
+  for (int32_t i = 0; i < n; ++i) {
+    if (parents[i] < 0) roots.push_back(i); else child_off[parents[i] + 1]++;
+  }
+  for (int32_t i = 0; i < n; ++i) child_off[i + 1] += child_off[i];
+  {
+    std::vector<int32_t> fill(child_off.begin(), child_off.end() - 1);
+    for (int32_t i = 0; i < n; ++i)
+      if (parents[i] >= 0) child[fill[parents[i]]++] = i;
+  }
+
+  // Depth-first pre-order with an explicit stack (push in reverse to pop ascending).
+  p->flat_node_order.clear();
+  p->flat_node_order.reserve(n);
+  std::vector<int32_t> stack(roots.rbegin(), roots.rend());
+  while (!stack.empty()) {
+    int32_t x = stack.back();
+    stack.pop_back();
+    p->flat_node_order.push_back(x);
+    for (int32_t k = child_off[x + 1] - 1; k >= child_off[x]; --k) stack.push_back(child[k]);
+  }
+  p->node_flat_start.resize(n);
+  p->flat_to_logical.resize(total);
+  int32_t f = 0;
+  for (int32_t x : p->flat_node_order) {
+    p->node_flat_start[x] = f;
+    for (int32_t i = 0; i < seg_lens[x]; ++i) p->flat_to_logical[f + i] = p->node_start[x] + i;
+    f += seg_lens[x];
+  }
+
+  // Equal chunks from flat index 0.
+  const int32_t nc = static_cast<int32_t>((static_cast<int64_t>(total) + c - 1) / c);
+  p->chunk_start.resize(nc + 1);
+  for (int32_t k = 0; k <= nc; ++k)
+    p->chunk_start[k] = static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(k) * c, total));
+  const int32_t words = (c + 31) / 32;
+
+  // Pass 1: for every query (ascending), the chunks its path touches, in
+  // ascending chunk order; a query's position inside each chunk's group is
+  // the number of lower queries already placed there.
+  std::vector<int32_t> group_count(nc, 0);
+  std::vector<int32_t> touch_off(nq + 1, 0);
+  std::vector<int32_t> touch_chunk, touch_pos;
+  std::vector<int32_t> path;
+  for (int32_t q = 0; q < nq; ++q) {
+    path.clear();
+    for (int32_t x = query_nodes[q]; x >= 0; x = parents[x]) path.push_back(x);
+    int32_t last = -1;
+    for (auto it = path.rbegin(); it != path.rend(); ++it) {
+      const int64_t a = p->node_flat_start[*it];
+      const int64_t b = a + seg_lens[*it];
+      for (int64_t k = a / c; k <= (b - 1) / c; ++k) {
+        if (static_cast<int32_t>(k) == last) continue;
+        last = static_cast<int32_t>(k);
+        touch_chunk.push_back(last);
+        touch_pos.push_back(group_count[last]++);
+      }
+    }
+    touch_off[q + 1] = static_cast<int32_t>(touch_chunk.size());
+  }
+  p->group_offsets.assign(nc + 1, 0);
+  for (int32_t k = 0; k < nc; ++k) p->group_offsets[k + 1] = p->group_offsets[k] + group_count[k];
+  const int32_t S = p->group_offsets[nc];
+
+  // Pass 2: slots, merge lists, mask bit runs.
+  p->slot_query.assign(S, 0);
+  p->slot_mask.assign(static_cast<size_t>(S) * words, 0u);
+  p->query_slot_offsets.assign(touch_off.begin(), touch_off.end());
+  p->query_slots.assign(S, 0);
+  std::vector<int64_t> slot_bits(S, 0);
+  for (int32_t q = 0; q < nq; ++q) {
+    for (int32_t t = touch_off[q]; t < touch_off[q + 1]; ++t) {
+      const int32_t s = p->group_offsets[touch_chunk[t]] + touch_pos[t];
+      p->slot_query[s] = q;
+      p->query_slots[t] = s;
+    }
+    path.clear();
+    for (int32_t x = query_nodes[q]; x >= 0; x = parents[x]) path.push_back(x);
+    int32_t t = touch_off[q];
+    for (auto it = path.rbegin(); it != path.rend(); ++it) {
+      const int64_t a = p->node_flat_start[*it];
+      const int64_t b = a + seg_lens[*it];
+      while (t < touch_off[q + 1] && static_cast<int64_t>(touch_chunk[t] + 1) * c <= a) ++t;
+      for (int32_t u = t; u < touch_off[q + 1]; ++u) {
+        const int64_t cs = static_cast<int64_t>(touch_chunk[u]) * c;
+        if (cs >= b) break;
+        const int64_t lo = std::max(a, cs) - cs, hi = std::min(b, cs + c) - cs;  // [lo, hi) in chunk
+        const int32_t s = p->group_offsets[touch_chunk[u]] + touch_pos[u];
+        uint32_t* row = &p->slot_mask[static_cast<size_t>(s) * words];
+        for (int64_t bit = lo; bit < hi;) {
+          const int64_t w = bit >> 5, off = bit & 31;
+          const int64_t take = std::min<int64_t>(32 - off, hi - bit);
+          const uint32_t ones = take == 32 ? 0xffffffffu : ((1u << take) - 1u);
+          row[w] |= ones << off;
+          bit += take;
+        }
+        slot_bits[s] += hi - lo;
+      }
+    }
+  }
+  p->chunk_full.assign(nc, 0);
+  for (int32_t k = 0; k < nc; ++k) {
+    const int64_t len = p->chunk_start[k + 1] - p->chunk_start[k];
+    bool full = p->group_offsets[k + 1] > p->group_offsets[k];
+    for (int32_t s = p->group_offsets[k]; s < p->group_offsets[k + 1] && full; ++s)
+      full = slot_bits[s] == len;
+    p->chunk_full[k] = full ? 1 : 0;
+  }
+
+  p->num_nodes = n;
+  p->num_queries = nq;
+  p->chunk_tokens = c;
+  p->total_tokens = total;
+  p->num_chunks = nc;
+  p->num_slots = S;
+  p->mask_words = words;
+  return DEFT_OK;
+}
+
+int check_desc(const deft_plan* p, const deft_attn_desc* d) {
+  if (!d) return fail(DEFT_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->page_size < 1 ||
+      d->num_pages < 1)
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "desc shapes must be positive");
+  if (d->dtype != DEFT_DTYPE_F32 && d->dtype != DEFT_DTYPE_BF16)
+    return fail(DEFT_ERR_UNSUPPORTED, "dtype must be DEFT_DTYPE_F32 or DEFT_DTYPE_BF16");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(DEFT_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->page_size != kPageSize) return fail(DEFT_ERR_UNSUPPORTED, "page_size must be 16");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(DEFT_ERR_UNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
+  if (p && p->chunk_tokens > kMaxChunkTokens)
+    return fail(DEFT_ERR_UNSUPPORTED, "chunk_tokens above 4096 is not supported by the kernels");
+  return DEFT_OK;
+}
+
+static size_t align_words(size_t w) { return (w + 63) & ~static_cast<size_t>(63); }  // 256 B
+
+size_t workspace_bytes_for(const deft_plan* p, const deft_attn_desc* d) {
+  const size_t sh = static_cast<size_t>(p->num_slots) * d->num_q_heads;
+  return 4 * (align_words(sh * d->head_dim) + 2 * align_words(sh));
+}
+
+int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* image,
+                ImageLayout* L) {
+  int rc = check_desc(p, d);
+  if (rc) return rc;
+  const int32_t G = d->num_q_heads / d->num_kv_heads;
+  std::vector<WorkItem> mfma, valu;
+  for (int32_t k = 0; k < p->num_chunks; ++k) {
+    const int32_t rows = (p->group_offsets[k + 1] - p->group_offsets[k]) * G;
+    if (rows == 0) continue;
+    const bool use_mfma = d->dtype == DEFT_DTYPE_BF16 && rows >= kMfmaMinRows;
+    const int32_t blk = use_mfma ? kMfmaRows : kValuRows;
+    for (int32_t r = 0; r < rows; r += blk)
+      (use_mfma ? mfma : valu).push_back({k, r, std::min(blk, rows - r), 0});
+  }
+  size_t w = 0;
+  auto take = [&](size_t n) { size_t at = w; w = align_words(w + n); return at; };
+  const int32_t nc = p->num_chunks, S = p->num_slots, W = p->mask_words;
+  L->chunk_start = take(nc + 1);
+  L->group_offsets = take(nc + 1);
+  L->chunk_full = take(nc);
+  L->slot_query = take(S);
+  L->slot_mask = take(static_cast<size_t>(S) * W);
+  L->flat_to_logical = take(p->total_tokens);
+  L->query_slot_offsets = take(p->num_queries + 1);
+  L->query_slots = take(S);
+  L->mfma_items = take(4 * mfma.size());
+  L->valu_items = take(4 * valu.size());
+  L->total_words = w;
+  L->n_mfma = static_cast<int32_t>(mfma.size());
+  L->n_valu = static_cast<int32_t>(valu.size());
+  if (!image) return DEFT_OK;
+  try {
+    image->assign(w, 0);
+  } catch (const std::bad_alloc&) {
+    return fail(DEFT_ERR_NO_MEMORY, "host allocation of the plan image failed");
+  }
+  int32_t* im = image->data();
+  std::copy(p->chunk_start.begin(), p->chunk_start.end(), im + L->chunk_start);
+  std::copy(p->group_offsets.begin(), p->group_offsets.end(), im + L->group_offsets);
+  for (int32_t k = 0; k < nc; ++k) im[L->chunk_full + k] = p->chunk_full[k];
+  std::copy(p->slot_query.begin(), p->slot_query.end(), im + L->slot_query);
+  std::memcpy(im + L->slot_mask, p->slot_mask.data(), 4 * p->slot_mask.size());
+  std::copy(p->flat_to_logical.begin(), p->flat_to_logical.end(), im + L->flat_to_logical);
+  std::copy(p->query_slot_offsets.begin(), p->query_slot_offsets.end(), im + L->query_slot_offsets);
+  std::copy(p->query_slots.begin(), p->query_slots.end(), im + L->query_slots);
+  std::memcpy(im + L->mfma_items, mfma.data(), sizeof(WorkItem) * mfma.size());
+  std::memcpy(im + L->valu_items, valu.data(), sizeof(WorkItem) * valu.size());
+  return DEFT_OK;
+}
+
+}  // namespace deft
+
+using deft::fail;
+
+extern "C" {
+
+int deft_plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                     const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
+                     deft_plan** out_plan) {
+  deft::set_error("");
+  if (!out_plan) return fail(DEFT_ERR_INVALID_ARGUMENT, "out_plan is NULL");
+  *out_plan = nullptr;
+  if (chunk_tokens < 1) return fail(DEFT_ERR_INVALID_ARGUMENT, "chunk_tokens must be >= 1");
+  if (num_nodes < 1 || num_queries < 1)
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "need at least one node and one query");
+  if (!parents || !seg_lens || !query_nodes)
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "tree arrays must not be NULL");
+  for (int32_t i = 0; i < num_nodes; ++i) {
+    if (parents[i] < -1 || parents[i] >= i)
+      return fail(DEFT_ERR_INVALID_TREE,
+                  "parents[" + std::to_string(i) + "] must be -1 or in [0, " + std::to_string(i) + ")");
+    if (seg_lens[i] < 1)
+      return fail(DEFT_ERR_INVALID_TREE, "seg_lens[" + std::to_string(i) + "] must be >= 1");
+  }
+  for (int32_t q = 0; q < num_queries; ++q)
+    if (query_nodes[q] < 0 || query_nodes[q] >= num_nodes)
+      return fail(DEFT_ERR_INVALID_TREE, "query_nodes[" + std::to_string(q) + "] out of range");
+  int64_t total = 0;
+  for (int32_t i = 0; i < num_nodes; ++i) total += seg_lens[i];
+  if (total > INT32_MAX) return fail(DEFT_ERR_INVALID_TREE, "total tokens exceed 2^31 - 1");
+  deft_plan* p = new (std::nothrow) deft_plan();
+  if (!p) return fail(DEFT_ERR_NO_MEMORY, "host allocation failed");
+  int rc;
+  try {
+    rc = deft::build_plan(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens);
+  } catch (const std::bad_alloc&) {
+    rc = fail(DEFT_ERR_NO_MEMORY, "host allocation failed while planning");
+  }
+  if (rc) {
+    delete p;
+    return rc;
+  }
+  *out_plan = p;
+  return DEFT_OK;
+}
+
+void deft_plan_destroy(deft_plan* plan) { delete plan; }
+
+int deft_plan_export(const deft_plan* p, deft_plan_view* v) {
+  if (!p || !v) return fail(DEFT_ERR_INVALID_ARGUMENT, "plan and view must not be NULL");
+  v->num_nodes = p->num_nodes;
+  v->num_queries = p->num_queries;
+  v->chunk_tokens = p->chunk_tokens;
+  v->total_tokens = p->total_tokens;
+  v->num_chunks = p->num_chunks;
+  v->num_slots = p->num_slots;
+  v->mask_words = p->mask_words;
+  v->node_start = p->node_start.data();
+  v->flat_node_order = p->flat_node_order.data();
+  v->node_flat_start = p->node_flat_start.data();
+  v->flat_to_logical = p->flat_to_logical.data();
+  v->chunk_start = p->chunk_start.data();
+  v->group_offsets = p->group_offsets.data();
+  v->slot_query = p->slot_query.data();
+  v->slot_mask = p->slot_mask.data();
+  v->chunk_full = p->chunk_full.data();
+  v->query_slot_offsets = p->query_slot_offsets.data();
+  v->query_slots = p->query_slots.data();
+  return DEFT_OK;
+}
+
+int deft_plan_device_bytes(deft_plan* p, const deft_attn_desc* d, size_t* plan_bytes,
+                           size_t* workspace_bytes) {
+  if (!p) return fail(DEFT_ERR_INVALID_ARGUMENT, "plan is NULL");
+  deft::ImageLayout L{};
+  int rc = deft::build_image(p, d, nullptr, &L);
+  if (rc) return rc;
+  if (plan_bytes) *plan_bytes = 4 * L.total_words;
+  if (workspace_bytes) *workspace_bytes = deft::workspace_bytes_for(p, d);
+  return DEFT_OK;
+}
+
+const char* deft_last_error(void) { return deft::g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+"""Convenience wrapper: owns a plan plus the caller-side device buffers
+(plan image and workspace, allocated through torch) and calls the C ABI."""
+from __future__ import annotations
+
+import torch
+
+from . import deft as D
+
+
+class TreeAttention:
+    """Plan a tree once, then run tree attention over paged KV.
+
+    desc: a deft_attn_desc (see deft.make_desc).  Device buffers are torch
+    tensors on `device`; the plan image is uploaded on `stream`.
+    """
+
+    def __init__(self, parents, seg_lens, query_nodes, chunk_tokens: int, desc, device="cuda",
+                 stream=None):
+        self.desc = desc
+        self.plan = D.deft_plan_create(parents, seg_lens, query_nodes, chunk_tokens)
+        plan_bytes, ws_bytes = D.deft_plan_device_bytes(self.plan, desc)
+        self.plan_bytes, self.workspace_bytes = plan_bytes, ws_bytes
+        self.dev_plan = torch.empty(max(plan_bytes, 256), dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=device)
+        D.deft_plan_upload(self.plan, desc, self.dev_plan, stream)
+
+    def view(self) -> dict:
+        return D.deft_plan_export(self.plan)
+
+    def __call__(self, q, k_cache, v_cache, block_table, out=None, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        D.deft_tree_attention(q, k_cache, v_cache, block_table, self.plan, out, self.desc,
+                              self.workspace, stream)
+        return out
+
+    def partials(self, q, k_cache, v_cache, block_table, stream=None):
+        """Per-slot (O, m, l) from the partial kernel alone, fp32 device tensors."""
+        s = self.plan_view_counts()
+        hq, d = self.desc.num_q_heads, self.desc.head_dim
+        po = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
+        pm = torch.empty((s, hq), dtype=torch.float32, device=q.device)
+        pl = torch.empty((s, hq), dtype=torch.float32, device=q.device)
+        D.deft_partial_attention(q, k_cache, v_cache, block_table, self.plan, self.desc, po, pm, pl, stream)
+        return po, pm, pl
+
+    def plan_view_counts(self) -> int:
+        return int(D.deft_plan_export(self.plan)["num_slots"])
