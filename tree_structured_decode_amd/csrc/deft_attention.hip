@@ -82,6 +82,8 @@ struct PartialArgs {
   float scale_log2;  // log2(e) / sqrt(d)
 };
 
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 
 __device__ inline uint16_t f32_to_bf16(float f) {
@@ -117,12 +119,43 @@ __device__ inline u32x4 load16(const void* base, int64_t elem_off, int elem_byte
 }
 
 // Pool row (page * 16 + slot) of every flat token of the chunk, into LDS.
+// All flat-to-logical loads are issued before any block-table load so the
+// two dependent lookups cost two memory latencies, not two per token.  With
+// RPI > 0 the rows of each 32-token step are stored permuted, entry
+// (t % RPI) * (32 / RPI) + (t % 32) / RPI, which puts the rows one lane of a
+// direct-to-LDS load sequence needs next to each other.
+template <int RPI, int N>
+__device__ inline void stage_token_rows_n(int32_t* tok_row, const DevPlan& P, const int32_t* bt,
+                                          int32_t cs, int32_t len) {
+  // N fixed loads per thread, no branches between them; indices past the
+  // chunk end re-read its last token and are not stored.
+  int32_t lt[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k)
+    lt[k] = P.flat_to_logical[cs + min(static_cast<int>(threadIdx.x) + k * 256, len - 1)];
+  int32_t pg[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) pg[k] = bt[lt[k] >> 4];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int t = threadIdx.x + k * 256;
+    if (t < len) {
+      int at = t;
+      if constexpr (RPI > 0) at = (t & ~31) + (t % RPI) * (32 / RPI) + (t & 31) / RPI;
+      tok_row[at] = pg[k] * kPageSize + (lt[k] & (kPageSize - 1));
+    }
+  }
+}
+template <int RPI = 0>
 __device__ inline void stage_token_rows(int32_t* tok_row, const DevPlan& P, const int32_t* bt,
                                         int32_t cs, int32_t len) {
-  for (int32_t t = threadIdx.x; t < len; t += blockDim.x) {
-    const int32_t lt = P.flat_to_logical[cs + t];
-    tok_row[t] = bt[lt >> 4] * kPageSize + (lt & (kPageSize - 1));
-  }
+  static_assert(kMaxChunkTokens == 16 * 256, "staging batches assume 256 threads");
+  const int nk = (len + 255) / 256;
+  if (nk <= 1) stage_token_rows_n<RPI, 1>(tok_row, P, bt, cs, len);
+  else if (nk <= 2) stage_token_rows_n<RPI, 2>(tok_row, P, bt, cs, len);
+  else if (nk <= 4) stage_token_rows_n<RPI, 4>(tok_row, P, bt, cs, len);
+  else if (nk <= 8) stage_token_rows_n<RPI, 8>(tok_row, P, bt, cs, len);
+  else stage_token_rows_n<RPI, 16>(tok_row, P, bt, cs, len);
 }
 
 // ---------------------------------------------------------------------------
@@ -293,26 +326,72 @@ __global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
 // ---------------------------------------------------------------------------
 // MFMA partial kernel (bf16).  Work-group = 4 waves on one (chunk, KV head,
 // block of up to 64 rows).  Wave w takes the chunk's 32-token steps w, w+4,
-// ...; for each step it computes S^T = K Q^T (16x16x32 MFMA: A = K rows, B =
-// Q^T) for 2 token tiles x 4 row tiles, applies the mask and the online
-// softmax on the S^T fragments in registers, and accumulates
-// O^T += V^T P^T (A = V^T read from LDS, B = P^T straight from the S^T
-// fragments).  K tile rows are permuted so that every lane ends up holding 8
-// consecutive tokens of one row, which is the B-operand layout of the PV
-// product.  V is transposed through a wave-private LDS tile.
+// ...; each wave owns a private two-stage LDS ring that direct-to-LDS loads
+// (no VGPRs) fill one step ahead: the step's K rows, V rows and the mask word
+// of each of the 64 rows.  Per step:
+//   S^T = K Q^T   16x16x32 MFMA, A = K rows (LDS), B = Q^T (registers), for
+//                 2 token tiles x 4 row tiles;
+//   mask, online softmax on the S^T fragments in registers;
+//   O^T += V^T P^T  A = V^T built by LDS transpose reads of the token-major
+//                 V rows, B = P^T taken straight from the S^T fragments.
+// K tile rows are permuted so every lane ends up holding 8 consecutive tokens
+// of one row, which is the B-operand layout of the PV product.  Rows in LDS
+// are stored with their 16-byte chunks XOR-swizzled by the row index.
 // ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lptr_t;
+// Direct-to-LDS loads, written as inline asm: lane i's bytes land at LDS
+// address lds + size * i (M0 holds the wave-uniform LDS base).  The compiler
+// sees no LDS write here, so it adds no waits of its own for them; callers
+// order them with explicit s_waitcnt vmcnt (they count as vector-memory loads).
+__device__ inline uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lptr_t)p));
+}
+__device__ inline void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ inline void lds_dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+}
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
+// operations are outstanding / until all LDS operations are done.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 0xc07f;
+
+// max over the 4 lanes that hold the same row (lanes l, l^16, l^32, l^48)
+__device__ inline float rowmax4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float rowsum4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
   constexpr int NW = 4;
-  constexpr int NRT = kMfmaRows / 16;  // row tiles per wave
-  constexpr int KS = D / 32;           // k-steps of S = K Q^T
-  constexpr int DT = D / 16;           // d-tiles of O^T
-  constexpr int VT_STRIDE = 40;        // bf16 per V^T row: 32 tokens + 8 padding (80 bytes)
-  constexpr int UNITS = D / 64;        // 4-token x 8-d V pieces per lane per step
-  constexpr int VT_BYTES = NW * D * VT_STRIDE * 2;
-  constexpr int RED_BYTES = NW * kMfmaRows * 32 * 4;
-  __shared__ int32_t tok_row[kMaxChunkTokens];
-  __shared__ __attribute__((aligned(16))) char smem[VT_BYTES > RED_BYTES ? VT_BYTES : RED_BYTES];
+  constexpr int NRT = kMfmaRows / 16;   // row tiles per wave
+  constexpr int KS = D / 32;            // k-steps of S = K Q^T
+  constexpr int DT = D / 16;            // d-tiles of O^T
+  constexpr int CH = D / 8;             // 16-byte chunks per token row
+  constexpr int ROWB = D * 2;           // bytes per token row
+  constexpr int TILE_B = 32 * ROWB;     // K (or V) bytes of one 32-token step
+  constexpr int NI = TILE_B / 1024;     // 1 KB direct loads per tile
+  constexpr int RPI = 64 / CH;          // token rows per direct load
+  constexpr int STAGE_B = 2 * TILE_B + 256;   // K, V, 64 mask words
+  constexpr int NSTAGE = 2;
+  constexpr int RING_B = NW * NSTAGE * STAGE_B;
+  constexpr int RED_B = NW * DT * NRT * 64 * 16;   // every wave's O^T fragments
+  constexpr int LOADS_PER_STAGE = 2 * NI + 1;
+  static_assert(NI == 8 || NI == 4, "token rows per lane come in groups of 4 or 8");
+  __shared__ __attribute__((aligned(1024))) char smem[RING_B > RED_B ? RING_B : RED_B];
+  __shared__ __attribute__((aligned(16))) int32_t tok_row[kMaxChunkTokens];
   __shared__ float stats[NW][kMfmaRows][3];
 
   const DevPlan& P = a.plan;
@@ -321,28 +400,25 @@ __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
   const int32_t c = item.x, rb = item.y, nr = item.z;
   const int32_t cs = P.chunk_start[c], len = P.chunk_start[c + 1] - cs;
   const int32_t gofs = P.group_offsets[c];
-  const bool full = P.chunk_full[c] != 0;
   const int W = P.mask_words;
 
-  stage_token_rows(tok_row, P, a.block_table, cs, len);
+  stage_token_rows<RPI>(tok_row, P, a.block_table, cs, len);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lj = lane >> 4;
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const uint16_t* kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* vp = static_cast<const uint16_t*>(a.v);
 
-  // Q^T fragments (B operand of S^T = K Q^T) and each row's slot.
+  // Q^T fragments (B operand of S^T = K Q^T).
   bf16x8 qf[NRT][KS];
-  int32_t slot_of[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int r = rt * 16 + lr;
-    slot_of[rt] = -1;
     if (r < nr) {
       const int row = rb + r;
-      slot_of[rt] = gofs + row / a.grp;
-      const int32_t qi = P.slot_query[slot_of[rt]];
+      const int32_t qi = P.slot_query[gofs + row / a.grp];
       const int head = g * a.grp + row % a.grp;
       const uint16_t* src = qp + (static_cast<int64_t>(qi) * a.hq + head) * D + lj * 8;
 #pragma unroll
@@ -353,7 +429,49 @@ __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
       for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
   }
+  // This lane's row for the mask loads (lane i <-> row i); rows past nr reuse row 0.
+  const int32_t mask_slot = gofs + (rb + (lane < nr ? lane : 0)) / a.grp;
   __syncthreads();
+
+  const int64_t hstride = static_cast<int64_t>(a.hkv) * D;
+  const int64_t goff = static_cast<int64_t>(g) * D;
+  char* ring = smem + w * NSTAGE * STAGE_B;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  const int lrow = lane / CH;            // row of each direct load this lane fetches
+  const int lch = lane % CH;             // its 16-byte LDS slot in that row
+
+  // Direct loads of one step into a stage: load n fetches rows n*RPI + lrow;
+  // lane (lrow, lch) fetches chunk lch ^ (R % CH) of row R, so LDS slot p of
+  // row R holds chunk p ^ (R % CH).  Tokens past the chunk end re-read its last
+  // token (finite values; the mask zeroes their weight).
+  auto issue = [&](int stage, int step) {
+    const uint32_t kd = ring_lds + stage * STAGE_B;
+    const uint32_t vd = kd + TILE_B;
+    const int base = step * 32;
+    int32_t rows[NI];
+    if (base + 32 <= len) {
+      const int32_t* tr = tok_row + base + lrow * NI;   // the permuted layout
+#pragma unroll
+      for (int n = 0; n < NI; n += 4) {
+        const int4 v4 = *reinterpret_cast<const int4*>(tr + n);
+        rows[n] = v4.x; rows[n + 1] = v4.y; rows[n + 2] = v4.z; rows[n + 3] = v4.w;
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const int t = min(base + n * RPI + lrow, len - 1);
+        rows[n] = tok_row[(t & ~31) + (t % RPI) * (32 / RPI) + (t & 31) / RPI];
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int R = n * RPI + lrow;
+      const int64_t off = static_cast<int64_t>(rows[n]) * hstride + goff + ((lch ^ (R % CH)) * 8);
+      lds_dma16(kp + off, kd + n * 1024);
+      lds_dma16(vp + off, vd + n * 1024);
+    }
+    lds_dma4(P.slot_mask + static_cast<size_t>(mask_slot) * W + step, vd + TILE_B);
+  };
 
   f32x4 o[DT][NRT];
 #pragma unroll
@@ -367,204 +485,155 @@ __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
     m_true[rt] = kNegInf;
     l_part[rt] = 0.f;
   }
-
-  const int64_t hstride = static_cast<int64_t>(a.hkv) * D;
-  const int64_t goff = static_cast<int64_t>(g) * D;
-  // K rows held by this lane in the two 16-token tiles of a step.
-  const int tk0 = 8 * (lr >> 2) + (lr & 3);
-  const int tk1 = tk0 + 4;
-
-  auto load_k = [&](int base, bf16x8 (&kf)[2][KS]) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int t = base + (tt ? tk1 : tk0);
-      if (t < len) {
-        const uint16_t* src = kp + tok_row[t] * hstride + goff + lj * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kf[tt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 32));
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[tt][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-      }
-    }
-  };
-  // V pieces: unit u covers tokens 4*qd .. 4*qd+3 of the step and d 8*dc .. 8*dc+7.
-  auto load_v = [&](int base, u32x4 (&vr)[UNITS][4]) {
-#pragma unroll
-    for (int u = 0; u < UNITS; ++u) {
-      const int unit = u * 64 + lane;
-      const int dc = unit % (D / 8), qd = unit / (D / 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = base + 4 * qd + i;
-        if (t < len)
-          vr[u][i] = *reinterpret_cast<const u32x4*>(vp + tok_row[t] * hstride + goff + dc * 8);
-        else
-          vr[u][i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto load_mask = [&](int base, uint32_t (&mw)[NRT]) {
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-      mw[rt] = (full || slot_of[rt] < 0) ? 0u
-               : P.slot_mask[static_cast<size_t>(slot_of[rt]) * W + (base >> 5)];
-  };
-
-  uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + w * D * VT_STRIDE;
+  const float cl2 = a.scale_log2;
+  // K rows this lane reads for the A operand, per token tile.
+  const int rk0 = 8 * (lr >> 2) + (lr & 3);
   const int nsteps = (len + 31) / 32;
-  bf16x8 kf[2][KS];
-  u32x4 vr[UNITS][4];
-  uint32_t mw[NRT];
-  if (w < nsteps) {
-    load_k(w * 32, kf);
-    load_v(w * 32, vr);
-    load_mask(w * 32, mw);
-  }
-  for (int step = w; step < nsteps; step += NW) {
-    const int base = step * 32;
-    // V^T for this step into the wave's LDS tile (pairs of tokens packed per dword).
-#pragma unroll
-    for (int u = 0; u < UNITS; ++u) {
-      const int unit = u * 64 + lane;
-      const int dc = unit % (D / 8), qd = unit / (D / 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1;
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = (vr[u][0][wd] >> 16) | (vr[u][1][wd] & 0xffff0000u);
-          hi = (vr[u][2][wd] >> 16) | (vr[u][3][wd] & 0xffff0000u);
-        } else {
-          lo = (vr[u][0][wd] & 0xffffu) | (vr[u][1][wd] << 16);
-          hi = (vr[u][2][wd] & 0xffffu) | (vr[u][3][wd] << 16);
-        }
-        *reinterpret_cast<u32x2*>(vt + (dc * 8 + e) * VT_STRIDE + qd * 4) = u32x2{lo, hi};
-      }
-    }
-    const bool more = step + NW < nsteps;
-    if (more) load_v(base + NW * 32, vr);
-    uint32_t mw_cur[NRT];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) mw_cur[rt] = mw[rt];
-    if (more) load_mask(base + NW * 32, mw);
+  const int mine = w < nsteps ? (nsteps - w + NW - 1) / NW : 0;
 
-    // S^T = K Q^T for 2 token tiles x NRT row tiles.
+  if (mine > 0) issue(0, w);
+  if (mine > 1) issue(1, w + NW);
+  for (int i = 0; i < mine; ++i) {
+    const int step = w + i * NW;
+    const int base = step * 32;
+    const int stage = i & 1;
+    if (i + 1 < mine) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS_PER_STAGE));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    asm volatile("" ::: "memory");
+    const char* kb = ring + stage * STAGE_B;
+    const char* vb = kb + TILE_B;
+    const uint32_t* mb = reinterpret_cast<const uint32_t*>(vb + TILE_B);
+
+    // S^T = K Q^T; all K fragments of the step are read first.
+    bf16x8 kf[KS][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int R = rk0 + 4 * tt;
+        kf[ks][tt] = *reinterpret_cast<const bf16x8*>(kb + R * ROWB + (((ks * 4 + lj) ^ (R % CH)) * 16));
+      }
+    uint32_t mrow[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) mrow[rt] = mb[rt * 16 + lr];
     f32x4 s[2][NRT];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < NRT; ++rt) s[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[rt][ks], acc, 0, 0, 0);
-        s[tt][rt] = acc;
-      }
-    if (more) load_k(base + NW * 32, kf);
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+          s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][tt], qf[rt][ks], s[tt][rt], 0, 0, 0);
 
-    // Mask, online softmax; P^T fragments as bf16.  Lane holds tokens
-    // base + 8*lj + e (e = 0..7) of row lr in each row tile.
+    // Mask and online softmax.  Lane holds tokens base + 8*lj + e of row
+    // rt*16 + lr; scores stay in raw units, exp2 folds in scale * log2(e).
     bf16x8 pb[NRT];
+    const int valid_e = len - base - 8 * lj;   // tokens of this lane's 8 that exist
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      if (rt * 16 >= nr) {
-        pb[rt] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-        continue;
-      }
-      const uint32_t bits = (mw_cur[rt] >> (8 * lj)) & 0xffu;
+      const bool row_ok = rt * 16 + lr < nr;
+      const uint32_t bits = row_ok ? (mrow[rt] >> (8 * lj)) & 0xffu : 0u;
       float z[8];
       float mx = kNegInf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float sv = (e < 4 ? s[0][rt][e] : s[1][rt][e - 4]) * a.scale_log2;
-        const int t = base + 8 * lj + e;
-        const bool vis = slot_of[rt] >= 0 && t < len && (full || ((bits >> e) & 1u));
+        const float sv = e < 4 ? s[0][rt][e] : s[1][rt][e - 4];
+        const bool vis = ((bits >> e) & 1u) && e < valid_e;
         z[e] = vis ? sv : kNegInf;
         mx = fmaxf(mx, z[e]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = rowmax4(mx);
       m_true[rt] = fmaxf(m_true[rt], mx);
-      const bool raise = mx > m_run[rt] + kRescaleSlack || (m_run[rt] == kNegInf && mx != kNegInf);
+      const bool raise = mx > m_run[rt] + kRescaleSlack / cl2 || (m_run[rt] == kNegInf && mx != kNegInf);
       if (__any(raise)) {
         const float mn = raise ? mx : m_run[rt];
-        const float alpha = raise ? exp2f(m_run[rt] - mn) : 1.f;
+        const float alpha = raise ? fast_exp2((m_run[rt] - mn) * cl2) : 1.f;
         m_run[rt] = mn;
         l_part[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
       }
+      // a row with nothing visible yet keeps m = -inf; its z are all -inf too
+      const float mc = m_run[rt] == kNegInf ? 0.f : m_run[rt] * cl2;
       f32x8 p;
       float ls = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = z[e] == kNegInf ? 0.f : exp2f(z[e] - m_run[rt]);
+        p[e] = fast_exp2(fmaf(z[e], cl2, -mc));   // z = -inf gives 0
         ls += p[e];
       }
       l_part[rt] += ls;
       pb[rt] = __builtin_convertvector(p, bf16x8);
     }
 
-    // O^T += V^T P^T.
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V^T writes are done
-    __builtin_amdgcn_wave_barrier();
+    // O^T += V^T P^T.  V^T fragments come from LDS transpose reads of the
+    // token-major rows: within each 16-lane group, ds_read_b64_tr_b16 hands
+    // lane i element (i % 4) of the 8 bytes that lane 4k + i/4 addresses, as
+    // its k-th element.  Lane (lr, lj) addresses row 8lj + 4h + lr/4 at d
+    // 16dt + 4(lr % 4), so it receives V[8lj + 4h + k][16dt + lr], k = 0..3.
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + (dt * 16 + lr) * VT_STRIDE + lj * 8);
+      u32x2 half[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int R = 8 * lj + 4 * h + (lr >> 2);
+        const int ch = (2 * dt + ((lr & 3) >> 1)) ^ (R % CH);
+        half[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                      (lds_s16x4_t)(vb + R * ROWB + ch * 16 + 8 * (lr & 1))));
+      }
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
-        if (rt * 16 < nr) o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rt], o[dt][rt], 0, 0, 0);
+        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rt], o[dt][rt], 0, 0, 0);
     }
-    __builtin_amdgcn_wave_barrier();
+    // this stage's LDS reads are complete before it is refilled
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("" ::: "memory");
+    if (i + 2 < mine) issue(stage, step + 2 * NW);
   }
 
   // Combine the four waves: true max, per-wave weights, summed l and O.
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    float ls = l_part[rt];
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
+    const float ls = rowsum4(l_part[rt]);
     if (lj == 0) {
       stats[w][rt * 16 + lr][0] = m_run[rt];
       stats[w][rt * 16 + lr][1] = m_true[rt];
       stats[w][rt * 16 + lr][2] = ls;
     }
   }
-  __syncthreads();
-  float wself[NRT];
+  __syncthreads();   // every wave is past its loop: the ring is free
+  // Each wave stores its O^T fragments scaled by exp2(m_run - M) (M the row's
+  // true max over the waves) as f32x4 at red[w][dt][rt][lane].
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int r = rt * 16 + lr;
     float mx = kNegInf;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, stats[ww][r][1]);
-    wself[rt] = (m_run[rt] == kNegInf) ? 0.f : exp2f(m_run[rt] - mx);
+    const float f = (m_run[rt] == kNegInf) ? 0.f : fast_exp2((m_run[rt] - mx) * cl2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) red[((w * DT + dt) * NRT + rt) * 64 + lane] = o[dt][rt] * f;
   }
-  // Reuse the V^T tiles as the reduction buffer: 32 d-values per pass.
-  float* red = reinterpret_cast<float*>(smem);  // [NW][64 rows][32]
-  for (int pass = 0; pass < DT / 2; ++pass) {
-    __syncthreads();
+  __syncthreads();
+  // Sum over the waves; thread -> (dt, rt, lane) f32x4 = 4 consecutive d of one row.
+  for (int idx = threadIdx.x; idx < DT * NRT * 64; idx += blockDim.x) {
+    const int ln = idx & 63, rt = (idx >> 6) % NRT, dt = (idx >> 6) / NRT;
+    const int r = rt * 16 + (ln & 15);
+    if (r >= nr) continue;
+    f32x4 acc = red[(dt * NRT + rt) * 64 + ln];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int dt = pass * 2 + h;
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          red[(w * kMfmaRows + rt * 16 + lr) * 32 + h * 16 + lj * 4 + i] = o[dt][rt][i] * wself[rt];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < nr * 32; idx += blockDim.x) {
-      const int r = idx >> 5, e = idx & 31;
-      float ov = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) ov += red[(ww * kMfmaRows + r) * 32 + e];
-      const int row = rb + r;
-      const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
-      a.po[sh * D + pass * 32 + e] = ov;
-    }
+    for (int ww = 1; ww < NW; ++ww) acc += red[((ww * DT + dt) * NRT + rt) * 64 + ln];
+    const int row = rb + r;
+    const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
+    *reinterpret_cast<f32x4*>(a.po + sh * D + dt * 16 + (ln >> 4) * 4) = acc;
   }
   for (int r = threadIdx.x; r < nr; r += blockDim.x) {
     float mx = kNegInf;
@@ -574,11 +643,11 @@ __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
       const float mr = stats[ww][r][0];
-      ls += (mr == kNegInf) ? 0.f : exp2f(mr - mx) * stats[ww][r][2];
+      ls += (mr == kNegInf) ? 0.f : fast_exp2((mr - mx) * cl2) * stats[ww][r][2];
     }
     const int row = rb + r;
     const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
-    a.pm[sh] = mx == kNegInf ? kNegInf : mx * kLn2;
+    a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
     a.pl[sh] = ls;
   }
 }
