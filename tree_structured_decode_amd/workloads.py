@@ -287,7 +287,7 @@ def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = 
         tp, depths = medusa_token_tree(rng, (4, 3, 2, 2), 64)
         p, s, qn = prefix_plus_token_tree(4096, tp)
         scale = 1.0 if unscaled else 1.0 / math.sqrt(128)
-        return make_workload(WORKLOADS[2], p, s, qn, chunk_tokens=chunk_tokens or 512,
+        return make_workload(WORKLOADS[2], p, s, qn, chunk_tokens=chunk_tokens or 520,
                              hq=32, hkv=8, d=128, dtype=torch.bfloat16, seed=seed,
                              placement=placement or "identity", value_scale=scale,
                              meta={"depths": depths})
