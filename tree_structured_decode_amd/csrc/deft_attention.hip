@@ -324,19 +324,22 @@ __global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA partial kernel (bf16).  Work-group = 4 waves on one (chunk, KV head,
-// block of up to 64 rows).  Wave w takes the chunk's 32-token steps w, w+4,
-// ...; each wave owns a private two-stage LDS ring that direct-to-LDS loads
-// (no VGPRs) fill one step ahead: the step's K rows, V rows and the mask word
-// of each of the 64 rows.  Per step:
+// MFMA partial kernel (bf16).  Work-group = 8 waves (two per SIMD) on one
+// (chunk, KV head, block of up to 64 rows).  Wave w owns row half h = w & 1
+// (rows 32h .. 32h+31, two 16-row tiles) and token split sp = w >> 1: it takes
+// the chunk's 32-token steps sp, sp+4, ...  The two waves of a split share a
+// two-stage LDS ring; per step one of them loads the K rows and the 64 rows'
+// mask words, the other the V rows, by direct-to-LDS loads (no VGPRs), one
+// step ahead, with one work-group barrier per step.  Per step and wave:
 //   S^T = K Q^T   16x16x32 MFMA, A = K rows (LDS), B = Q^T (registers), for
-//                 2 token tiles x 4 row tiles;
+//                 2 token tiles x 2 row tiles;
 //   mask, online softmax on the S^T fragments in registers;
-//   O^T += V^T P^T  A = V^T built by LDS transpose reads of the token-major
-//                 V rows, B = P^T taken straight from the S^T fragments.
+//   O^T += V^T P^T  A = V^T from LDS transpose reads of the token-major V
+//                 rows, B = P^T taken straight from the S^T fragments.
 // K tile rows are permuted so every lane ends up holding 8 consecutive tokens
 // of one row, which is the B-operand layout of the PV product.  Rows in LDS
-// are stored with their 16-byte chunks XOR-swizzled by the row index.
+// are stored with their 16-byte chunks XOR-swizzled by the row index.  The
+// four token splits of each row half are merged through LDS at the end.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lptr_t;
 // Direct-to-LDS loads, written as inline asm: lane i's bytes land at LDS
@@ -374,9 +377,11 @@ __device__ inline float rowsum4(float x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
-  constexpr int NW = 4;
-  constexpr int NRT = kMfmaRows / 16;   // row tiles per wave
+__global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
+  constexpr int NWAVE = 8;
+  constexpr int NSPLIT = 4;
+  constexpr int NRT = 2;                // row tiles per wave
+  constexpr int WROWS = NRT * 16;       // rows per wave
   constexpr int KS = D / 32;            // k-steps of S = K Q^T
   constexpr int DT = D / 16;            // d-tiles of O^T
   constexpr int CH = D / 8;             // 16-byte chunks per token row
@@ -385,14 +390,13 @@ __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
   constexpr int NI = TILE_B / 1024;     // 1 KB direct loads per tile
   constexpr int RPI = 64 / CH;          // token rows per direct load
   constexpr int STAGE_B = 2 * TILE_B + 256;   // K, V, 64 mask words
-  constexpr int NSTAGE = 2;
-  constexpr int RING_B = NW * NSTAGE * STAGE_B;
-  constexpr int RED_B = NW * DT * NRT * 64 * 16;   // every wave's O^T fragments
-  constexpr int LOADS_PER_STAGE = 2 * NI + 1;
+  constexpr int RING_B = NSPLIT * 2 * STAGE_B;
+  constexpr int RED_B = NWAVE * DT * NRT * 64 * 16;   // every wave's O^T fragments
   static_assert(NI == 8 || NI == 4, "token rows per lane come in groups of 4 or 8");
+  static_assert(kMfmaRows == 2 * WROWS, "a work item is two row halves");
   __shared__ __attribute__((aligned(1024))) char smem[RING_B > RED_B ? RING_B : RED_B];
   __shared__ __attribute__((aligned(16))) int32_t tok_row[kMaxChunkTokens];
-  __shared__ float stats[NW][kMfmaRows][3];
+  __shared__ float stats[NWAVE][WROWS][3];
 
   const DevPlan& P = a.plan;
   const int g = blockIdx.x % a.hkv;
@@ -401,52 +405,48 @@ __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
   const int32_t cs = P.chunk_start[c], len = P.chunk_start[c + 1] - cs;
   const int32_t gofs = P.group_offsets[c];
   const int W = P.mask_words;
-
-  stage_token_rows<RPI>(tok_row, P, a.block_table, cs, len);
+  const bool full = P.chunk_full[c] != 0;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = w & 1, sp = w >> 1;
   const int lr = lane & 15, lj = lane >> 4;
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const uint16_t* kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* vp = static_cast<const uint16_t*>(a.v);
 
-  // Q^T fragments (B operand of S^T = K Q^T).
+  // Q^T fragments (B operand of S^T = K Q^T) of this wave's 32 rows, loaded
+  // before the token rows so the two latencies overlap.
   bf16x8 qf[NRT][KS];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    const int r = rt * 16 + lr;
-    if (r < nr) {
-      const int row = rb + r;
-      const int32_t qi = P.slot_query[gofs + row / a.grp];
-      const int head = g * a.grp + row % a.grp;
-      const uint16_t* src = qp + (static_cast<int64_t>(qi) * a.hq + head) * D + lj * 8;
+    const int r = min(WROWS * h + rt * 16 + lr, nr - 1);   // rows past nr load a valid row; masked later
+    const int row = rb + r;
+    const int32_t qi = P.slot_query[gofs + row / a.grp];
+    const int head = g * a.grp + row % a.grp;
+    const uint16_t* src = qp + (static_cast<int64_t>(qi) * a.hq + head) * D + lj * 8;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[rt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 32));
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qf[rt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 32));
   }
-  // This lane's row for the mask loads (lane i <-> row i); rows past nr reuse row 0.
+  stage_token_rows<RPI>(tok_row, P, a.block_table, cs, len);
+  // Row of the mask word this lane loads (lane i <-> row i of the block).
   const int32_t mask_slot = gofs + (rb + (lane < nr ? lane : 0)) / a.grp;
   __syncthreads();
 
   const int64_t hstride = static_cast<int64_t>(a.hkv) * D;
   const int64_t goff = static_cast<int64_t>(g) * D;
-  char* ring = smem + w * NSTAGE * STAGE_B;
+  char* ring = smem + sp * 2 * STAGE_B;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
   const int lrow = lane / CH;            // row of each direct load this lane fetches
   const int lch = lane % CH;             // its 16-byte LDS slot in that row
 
-  // Direct loads of one step into a stage: load n fetches rows n*RPI + lrow;
-  // lane (lrow, lch) fetches chunk lch ^ (R % CH) of row R, so LDS slot p of
-  // row R holds chunk p ^ (R % CH).  Tokens past the chunk end re-read its last
-  // token (finite values; the mask zeroes their weight).
+  // This wave's half of a step's loads (h = 0: K rows and mask words; h = 1:
+  // V rows).  Load n fetches rows n*RPI + lrow; lane (lrow, lch) fetches chunk
+  // lch ^ (R % CH) of row R, so LDS slot p of row R holds chunk p ^ (R % CH).
+  // Tokens past the chunk end re-read its last token (finite values; masked).
   auto issue = [&](int stage, int step) {
     const uint32_t kd = ring_lds + stage * STAGE_B;
-    const uint32_t vd = kd + TILE_B;
     const int base = step * 32;
     int32_t rows[NI];
     if (base + 32 <= len) {
@@ -463,14 +463,15 @@ __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
         rows[n] = tok_row[(t & ~31) + (t % RPI) * (32 / RPI) + (t & 31) / RPI];
       }
     }
+    const uint16_t* src = h ? vp : kp;
+    const uint32_t dst = kd + h * TILE_B;
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
       const int R = n * RPI + lrow;
       const int64_t off = static_cast<int64_t>(rows[n]) * hstride + goff + ((lch ^ (R % CH)) * 8);
-      lds_dma16(kp + off, kd + n * 1024);
-      lds_dma16(vp + off, vd + n * 1024);
+      lds_dma16(src + off, dst + n * 1024);
     }
-    lds_dma4(P.slot_mask + static_cast<size_t>(mask_slot) * W + step, vd + TILE_B);
+    if (h == 0) lds_dma4(P.slot_mask + static_cast<size_t>(mask_slot) * W + step, kd + 2 * TILE_B);
   };
 
   f32x4 o[DT][NRT];
@@ -489,33 +490,25 @@ __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
   // K rows this lane reads for the A operand, per token tile.
   const int rk0 = 8 * (lr >> 2) + (lr & 3);
   const int nsteps = (len + 31) / 32;
-  const int mine = w < nsteps ? (nsteps - w + NW - 1) / NW : 0;
+  const int iters = (nsteps + NSPLIT - 1) / NSPLIT;   // the same for every wave
 
-  if (mine > 0) issue(0, w);
-  if (mine > 1) issue(1, w + NW);
-  for (int i = 0; i < mine; ++i) {
-    const int step = w + i * NW;
-    const int base = step * 32;
+  if (sp < nsteps) issue(0, sp);
+  for (int i = 0; i < iters; ++i) {
+    const int step = sp + i * NSPLIT;
     const int stage = i & 1;
-    if (i + 1 < mine) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS_PER_STAGE));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    asm volatile("" ::: "memory");
+    // This wave's loads for `step` are done; the barrier makes the partner's
+    // visible and guarantees every wave has finished step i-1, so the other
+    // stage can be refilled with step i+1.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (step + NSPLIT < nsteps) issue(stage ^ 1, step + NSPLIT);
+    if (step >= nsteps) continue;
+    const int base = step * 32;
     const char* kb = ring + stage * STAGE_B;
     const char* vb = kb + TILE_B;
-    const uint32_t* mb = reinterpret_cast<const uint32_t*>(vb + TILE_B);
+    const uint32_t* mb = reinterpret_cast<const uint32_t*>(kb + 2 * TILE_B);
 
-    // S^T = K Q^T; all K fragments of the step are read first.
-    bf16x8 kf[KS][2];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int R = rk0 + 4 * tt;
-        kf[ks][tt] = *reinterpret_cast<const bf16x8*>(kb + R * ROWB + (((ks * 4 + lj) ^ (R % CH)) * 16));
-      }
-    uint32_t mrow[NRT];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) mrow[rt] = mb[rt * 16 + lr];
+    // S^T = K Q^T
     f32x4 s[2][NRT];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -524,33 +517,46 @@ __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt) {
+        const int R = rk0 + 4 * tt;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + R * ROWB + (((ks * 4 + lj) ^ (R % CH)) * 16));
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
-          s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][tt], qf[rt][ks], s[tt][rt], 0, 0, 0);
+          s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][ks], s[tt][rt], 0, 0, 0);
+      }
 
     // Mask and online softmax.  Lane holds tokens base + 8*lj + e of row
-    // rt*16 + lr; scores stay in raw units, exp2 folds in scale * log2(e).
+    // 32h + rt*16 + lr; scores stay in raw units, exp2 folds in scale*log2(e).
+    // The running max m_run of a row (shared by its 4 lanes) only rises when
+    // some lane sees a score above m_run + slack; only then are the 4 lanes
+    // reduced.  The true max is tracked per lane and reduced at the end.
     bf16x8 pb[NRT];
     const int valid_e = len - base - 8 * lj;   // tokens of this lane's 8 that exist
+    const bool all_visible = full && valid_e >= 8;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      const bool row_ok = rt * 16 + lr < nr;
-      const uint32_t bits = row_ok ? (mrow[rt] >> (8 * lj)) & 0xffu : 0u;
+      const int rl = WROWS * h + rt * 16 + lr;   // row within the block
+      const bool row_ok = rl < nr;
       float z[8];
-      float mx = kNegInf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float sv = e < 4 ? s[0][rt][e] : s[1][rt][e - 4];
-        const bool vis = ((bits >> e) & 1u) && e < valid_e;
-        z[e] = vis ? sv : kNegInf;
-        mx = fmaxf(mx, z[e]);
+      for (int e = 0; e < 8; ++e) z[e] = e < 4 ? s[0][rt][e] : s[1][rt][e - 4];
+      if (!all_visible) {
+        const uint32_t bits = row_ok ? (mb[rl] >> (8 * lj)) & 0xffu : 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = (((bits >> e) & 1u) && e < valid_e) ? z[e] : kNegInf;
+      } else if (!row_ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = kNegInf;
       }
-      mx = rowmax4(mx);
+      float mx = z[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
       m_true[rt] = fmaxf(m_true[rt], mx);
-      const bool raise = mx > m_run[rt] + kRescaleSlack / cl2 || (m_run[rt] == kNegInf && mx != kNegInf);
-      if (__any(raise)) {
-        const float mn = raise ? mx : m_run[rt];
+      const bool high = mx > m_run[rt] + kRescaleSlack / cl2 || (m_run[rt] == kNegInf && mx != kNegInf);
+      if (__any(high)) {
+        const float rmx = rowmax4(mx);
+        const bool raise = rmx > m_run[rt] + kRescaleSlack / cl2 || (m_run[rt] == kNegInf && rmx != kNegInf);
+        const float mn = raise ? rmx : m_run[rt];
         const float alpha = raise ? fast_exp2((m_run[rt] - mn) * cl2) : 1.f;
         m_run[rt] = mn;
         l_part[rt] *= alpha;
@@ -573,77 +579,76 @@ __global__ __launch_bounds__(256) void mfma_partial(PartialArgs a) {
     // O^T += V^T P^T.  V^T fragments come from LDS transpose reads of the
     // token-major rows: within each 16-lane group, ds_read_b64_tr_b16 hands
     // lane i element (i % 4) of the 8 bytes that lane 4k + i/4 addresses, as
-    // its k-th element.  Lane (lr, lj) addresses row 8lj + 4h + lr/4 at d
-    // 16dt + 4(lr % 4), so it receives V[8lj + 4h + k][16dt + lr], k = 0..3.
+    // its k-th element.  Lane (lr, lj) addresses row 8lj + 4h' + lr/4 at d
+    // 16dt + 4(lr % 4), so it receives V[8lj + 4h' + k][16dt + lr], k = 0..3.
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       u32x2 half[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int R = 8 * lj + 4 * h + (lr >> 2);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int R = 8 * lj + 4 * hh + (lr >> 2);
         const int ch = (2 * dt + ((lr & 3) >> 1)) ^ (R % CH);
-        half[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                      (lds_s16x4_t)(vb + R * ROWB + ch * 16 + 8 * (lr & 1))));
+        half[hh] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                       (lds_s16x4_t)(vb + R * ROWB + ch * 16 + 8 * (lr & 1))));
       }
       const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
         o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rt], o[dt][rt], 0, 0, 0);
     }
-    // this stage's LDS reads are complete before it is refilled
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    asm volatile("" ::: "memory");
-    if (i + 2 < mine) issue(stage, step + 2 * NW);
   }
 
-  // Combine the four waves: true max, per-wave weights, summed l and O.
+  // Combine the four token splits of each row half: true max, per-split
+  // weights, summed l and O.
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const float ls = rowsum4(l_part[rt]);
+    const float mt = rowmax4(m_true[rt]);
     if (lj == 0) {
       stats[w][rt * 16 + lr][0] = m_run[rt];
-      stats[w][rt * 16 + lr][1] = m_true[rt];
+      stats[w][rt * 16 + lr][1] = mt;
       stats[w][rt * 16 + lr][2] = ls;
     }
   }
   __syncthreads();   // every wave is past its loop: the ring is free
   // Each wave stores its O^T fragments scaled by exp2(m_run - M) (M the row's
-  // true max over the waves) as f32x4 at red[w][dt][rt][lane].
+  // true max over the splits) as f32x4 at red[w][dt][rt][lane].
   f32x4* red = reinterpret_cast<f32x4*>(smem);
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int r = rt * 16 + lr;
     float mx = kNegInf;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, stats[ww][r][1]);
+    for (int q = 0; q < NSPLIT; ++q) mx = fmaxf(mx, stats[2 * q + h][r][1]);
     const float f = (m_run[rt] == kNegInf) ? 0.f : fast_exp2((m_run[rt] - mx) * cl2);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) red[((w * DT + dt) * NRT + rt) * 64 + lane] = o[dt][rt] * f;
   }
   __syncthreads();
-  // Sum over the waves; thread -> (dt, rt, lane) f32x4 = 4 consecutive d of one row.
-  for (int idx = threadIdx.x; idx < DT * NRT * 64; idx += blockDim.x) {
-    const int ln = idx & 63, rt = (idx >> 6) % NRT, dt = (idx >> 6) / NRT;
-    const int r = rt * 16 + (ln & 15);
+  // Sum over the splits; thread -> (half, dt, rt, lane) f32x4 = 4 consecutive d of one row.
+  for (int idx = threadIdx.x; idx < 2 * DT * NRT * 64; idx += blockDim.x) {
+    const int ln = idx & 63, rt = (idx >> 6) % NRT, dt = ((idx >> 6) / NRT) % DT, hh = (idx >> 6) / (NRT * DT);
+    const int r = WROWS * hh + rt * 16 + (ln & 15);
     if (r >= nr) continue;
-    f32x4 acc = red[(dt * NRT + rt) * 64 + ln];
+    f32x4 acc = red[((hh * DT + dt) * NRT + rt) * 64 + ln];
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) acc += red[((ww * DT + dt) * NRT + rt) * 64 + ln];
+    for (int q = 1; q < NSPLIT; ++q) acc += red[(((2 * q + hh) * DT + dt) * NRT + rt) * 64 + ln];
     const int row = rb + r;
     const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
     *reinterpret_cast<f32x4*>(a.po + sh * D + dt * 16 + (ln >> 4) * 4) = acc;
   }
   for (int r = threadIdx.x; r < nr; r += blockDim.x) {
+    const int hh = r / WROWS, rw = r % WROWS;
     float mx = kNegInf;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, stats[ww][r][1]);
+    for (int q = 0; q < NSPLIT; ++q) mx = fmaxf(mx, stats[2 * q + hh][rw][1]);
     float ls = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float mr = stats[ww][r][0];
-      ls += (mr == kNegInf) ? 0.f : fast_exp2((mr - mx) * cl2) * stats[ww][r][2];
+    for (int q = 0; q < NSPLIT; ++q) {
+      const float mr = stats[2 * q + hh][rw][0];
+      ls += (mr == kNegInf) ? 0.f : fast_exp2((mr - mx) * cl2) * stats[2 * q + hh][rw][2];
     }
     const int row = rb + r;
     const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
@@ -761,7 +766,7 @@ static int launch_partials(const PartialArgs& pa, hipStream_t st) {
   const int hkv = pa.hkv;
   if (pa.plan.n_mfma > 0) {
     if constexpr (sizeof(T) == 2) {
-      hipLaunchKernelGGL(mfma_partial<D>, dim3(pa.plan.n_mfma * hkv), dim3(256), 0, st, pa);
+      hipLaunchKernelGGL(mfma_partial<D>, dim3(pa.plan.n_mfma * hkv), dim3(512), 0, st, pa);
       int rc = hip_check(hipGetLastError(), "launch of mfma_partial");
       if (rc) return rc;
     } else {
