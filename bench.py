@@ -185,11 +185,13 @@ def main():
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     view = D.deft_plan_export(plan)
     S = view["num_slots"]
-    po = workspace.view(torch.float32)
-    align = lambda n: (n + 63) // 64 * 64
-    part_o = po[:S * hq * d]
-    part_m = po[align(S * hq * d):align(S * hq * d) + S * hq]
-    part_l = po[align(S * hq * d) + align(S * hq):align(S * hq * d) + align(S * hq) + S * hq]
+    # separate partial buffers for timing the two kernels alone, in the format
+    # deft_tree_attention uses internally
+    bf16 = wl.dtype == torch.bfloat16
+    fmt = D.DEFT_PARTIAL_BF16_NORM if bf16 else D.DEFT_PARTIAL_F32
+    part_o = torch.empty((S, hq, d), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
+    part_m = torch.empty((S, hq), dtype=torch.float32, device=dev)
+    part_l = torch.empty((S, hq), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     up0, up1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     up0.record()
@@ -200,10 +202,12 @@ def main():
 
     def step(i, what="both"):
         r = i % copies
-        if what in ("both", "partial"):
-            D.deft_partial_attention(qs[r], kc, vc, bts[r], plan, desc, part_o, part_m, part_l)
-        if what in ("both", "merge"):
-            D.deft_lse_merge(plan, desc, part_o, part_m, part_l, outs[r])
+        if what == "both":
+            D.deft_tree_attention(qs[r], kc, vc, bts[r], plan, outs[r], desc, workspace)
+        elif what == "partial":
+            D.deft_partial_attention(qs[r], kc, vc, bts[r], plan, desc, part_o, part_m, part_l, fmt)
+        else:
+            D.deft_lse_merge(plan, desc, part_o, part_m, part_l, outs[r], fmt)
 
     for i in range(args.warmup):
         step(i)
@@ -214,7 +218,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"profile_run": wl.name, "chunk_tokens": wl.chunk_tokens, "steps": args.steps,
                           "copies": copies, "kv_bytes": kv_bytes, "q_bytes": q_bytes,
-                          "partial_bytes": S * hq * (d + 2) * 4, "source_hash": source_hash()}),
+                          "partial_bytes": S * hq * (d * (2 if bf16 else 4) + 8), "source_hash": source_hash()}),
               flush=True)
         return
     for i in range(copies):          # an eager pass over every copy is the reference
@@ -261,6 +265,10 @@ def main():
     _, part_ms = timed(g_part)
     g_merge = capture("merge", 0, args.steps)
     _, merge_ms = timed(g_merge)
+    # the merge graph leaves outs[] holding merge-only results; restore the reference state
+    for i in range(copies):
+        step(i)
+    torch.cuda.synchronize()
     copies_saved = copies
     copies = 1                        # warm: the same copy every step, labelled as such
     g_warm = capture("both", 0, args.steps)
@@ -274,7 +282,7 @@ def main():
     paths = path_lengths(wl.parents, wl.seg_lens, wl.query_nodes)
     flops = 4.0 * d * hq * float(sum(paths))
     naive_kv = float(sum(paths)) * 2 * hkv * d * eb
-    part_bytes = S * hq * (d + 2) * 4
+    part_bytes = S * hq * (d * (2 if wl.dtype == torch.bfloat16 else 4) + 8)
     algo_step = kv_bytes + 2 * q_bytes
     mean_part = part_ms * 1e3 / args.steps
     mean_merge = merge_ms * 1e3 / args.steps

@@ -74,6 +74,10 @@ extern "C" {
 #define DEFT_DTYPE_F32   0
 #define DEFT_DTYPE_BF16  1
 
+/* Formats of the per-slot partial O (see deft_partial_attention). */
+#define DEFT_PARTIAL_F32        0  /* fp32, unnormalised: sum exp(s - m) v */
+#define DEFT_PARTIAL_BF16_NORM  1  /* bf16, divided by l: the softmax-weighted mean over the slot */
+
 typedef struct deft_plan deft_plan;   /* opaque, host-owned */
 
 /*
@@ -154,7 +158,9 @@ int deft_plan_export(const deft_plan* plan, deft_plan_view* out_view);
 /*
  * Sizes the caller must allocate for a given attention shape:
  *   *plan_bytes       device image of the plan (deft_plan_upload)
- *   *workspace_bytes  per-slot partial results (deft_tree_attention)
+ *   *workspace_bytes  per-slot partial results of deft_tree_attention: part_o
+ *                     in its internal format, then part_m and part_l, each
+ *                     padded to 256 bytes
  * Either output pointer may be NULL.  UNSUPPORTED if desc is outside this
  * build (head_dim not 64/128, page_size != 16, Hq % Hkv != 0, chunk_tokens
  * > 4096); INVALID_ARGUMENT for non-positive shapes.
@@ -176,8 +182,9 @@ int deft_plan_upload(deft_plan* plan, const deft_attn_desc* desc, void* dev_plan
 /*
  * Tree attention for one decode step: the partial-attention kernel (every
  * chunk's KV streamed once per KV head for all its grouped queries and their
- * query heads, bitmask applied, unnormalised per-slot partials written to
- * the workspace) followed by the log-sum-exp merge kernel.
+ * query heads, bitmask applied, per-slot partials written to the workspace in
+ * format DEFT_PARTIAL_BF16_NORM for bf16 inputs, DEFT_PARTIAL_F32 for fp32
+ * inputs) followed by the log-sum-exp merge kernel.
  * q, k_cache, v_cache, block_table, out, workspace: device pointers.
  * desc must equal the desc of the last deft_plan_upload.  workspace_bytes
  * must be at least the size from deft_plan_device_bytes.  block_table
@@ -195,21 +202,28 @@ int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
  * query head h, over the chunk's tokens visible to q:
  *   part_m[s*Hq + h]          max of the scaled scores (natural-log domain)
  *   part_l[s*Hq + h]          sum of exp(score - m)
- *   part_o[(s*Hq + h)*d + e]  sum of exp(score - m) * v[e]  (unnormalised)
- * all fp32, device pointers of S*Hq*d, S*Hq, S*Hq floats.
+ *   part_o[(s*Hq + h)*d + e]  partial_format DEFT_PARTIAL_F32: fp32
+ *                             sum of exp(score - m) * v[e] (unnormalised);
+ *                             DEFT_PARTIAL_BF16_NORM: that sum divided by l,
+ *                             rounded to bf16 (bf16 inputs only; this is the
+ *                             format deft_tree_attention uses for them)
+ * part_m and part_l are fp32 arrays of S*Hq floats, part_o holds S*Hq*d
+ * elements of the chosen format; all device pointers.
  */
 int deft_partial_attention(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const deft_plan* plan,
-                           const deft_attn_desc* desc, float* part_o, float* part_m,
-                           float* part_l, void* stream);
+                           const deft_attn_desc* desc, void* part_o, float* part_m,
+                           float* part_l, int32_t partial_format, void* stream);
 
 /*
  * The merge kernel on its own: for every query q and head h, over q's slots
- * M = max m_s, L = sum l_s exp(m_s - M), out = sum o_s exp(m_s - M) / L,
+ * M = max m_s, L = sum l_s exp(m_s - M), out = sum o_s exp(m_s - M) / L
+ * (with bf16-normalised partials: out = sum l_s exp(m_s - M) o_s / L),
  * rounded to desc->dtype.  Partials in the layout of deft_partial_attention.
  */
-int deft_lse_merge(const deft_plan* plan, const deft_attn_desc* desc, const float* part_o,
-                   const float* part_m, const float* part_l, void* out, void* stream);
+int deft_lse_merge(const deft_plan* plan, const deft_attn_desc* desc, const void* part_o,
+                   const float* part_m, const float* part_l, int32_t partial_format, void* out,
+                   void* stream);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* deft_last_error(void);

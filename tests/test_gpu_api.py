@@ -1,0 +1,56 @@
+"""Host-side argument checks of the attention entry points on a GPU process.
+
+Each call here is rejected before any kernel is launched; the library must
+report the error code and leave the device untouched.
+"""
+import pytest
+import torch
+
+from tree_structured_decode_amd import deft as D
+from tree_structured_decode_amd import workloads as W
+from tree_structured_decode_amd.runner import TreeAttention
+
+from gpu_helpers import DEV, gpu_inputs, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(cfg):
+    wl = W.standard_workload(cfg)
+    desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens, desc, device=DEV)
+    return wl, desc, ta
+
+
+def test_partial_format_checked():
+    say("api: partial formats")
+    wl, desc, ta = _setup(1)          # fp32 inputs
+    q, kc, vc, bt = gpu_inputs(wl)
+    s, hq, d = ta.plan_view_counts(), wl.num_q_heads, wl.head_dim
+    po = torch.empty((s, hq, d), dtype=torch.float32, device=DEV)
+    pm = torch.empty((s, hq), dtype=torch.float32, device=DEV)
+    pl = torch.empty((s, hq), dtype=torch.float32, device=DEV)
+    for fmt in (D.DEFT_PARTIAL_BF16_NORM, 7, -1):
+        with pytest.raises(D.DeftError) as e:
+            D.deft_partial_attention(q, kc, vc, bt, ta.plan, desc, po, pm, pl, fmt)
+        assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT
+        with pytest.raises(D.DeftError) as e:
+            D.deft_lse_merge(ta.plan, desc, po, pm, pl, q, fmt)
+        assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT
+    torch.cuda.synchronize()
+
+
+def test_workspace_and_desc_checked():
+    say("api: workspace and desc")
+    wl, desc, ta = _setup(2)
+    q, kc, vc, bt = gpu_inputs(wl)
+    out = torch.empty_like(q)
+    small = torch.empty(ta.workspace_bytes - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(D.DeftError) as e:
+        D.deft_tree_attention(q, kc, vc, bt, ta.plan, out, desc, small)
+    assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT
+    other = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads // 2, wl.head_dim, wl.num_pages)
+    with pytest.raises(D.DeftError) as e:
+        D.deft_tree_attention(q, kc, vc, bt, ta.plan, out, other, ta.workspace)
+    assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT
+    torch.cuda.synchronize()

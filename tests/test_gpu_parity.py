@@ -24,10 +24,13 @@ pytestmark = pytest.mark.gpu
 def _rms_check(got, want, what):
     """Scale-aware check for bf16 outputs whose magnitude is far below 2e-2.
 
-    Rounding the output to bf16 costs up to 2^-9 of each value and rounding the
-    probabilities to bf16 before PV adds a little more, so the largest error
-    stays below 2^-7 of the largest output and the mean error below 2^-8 of the
-    mean output.  An all-zero or badly mixed output fails this at any scale.
+    Each rounding to bf16 (unit roundoff 2^-8) costs at most 2^-8 of the value
+    and about a quarter of that on average.  The path rounds the probabilities
+    before PV, each chunk's O / l (bf16 internal partials) and the output; the
+    partial errors of different chunks are independent and shrink in the
+    weighted mean, so the largest error stays below 2^-7 of the largest output
+    and the mean error below 2^-8 of the mean output.  An all-zero or badly
+    mixed output fails this at any scale.
     """
     err = np.abs(got - want)
     top, mean = float(np.abs(want).max()), float(np.abs(want).mean())
@@ -104,7 +107,10 @@ def test_zero_keys_give_segment_weighted_mean(dtype):
     for i, node in enumerate(qn):
         path = OA.path_nodes(p, node)
         want = sum(s[x] * pattern[x] for x in path) / sum(s[x] for x in path)
-        rel = 1e-5 if dtype == torch.float32 else 2 ** -8
+        # bf16: all contributions are positive, so each rounding to bf16 costs at
+        # most its unit roundoff 2^-8 relative: once for a chunk's O / l in the
+        # internal partial format, once for the output.
+        rel = 1e-5 if dtype == torch.float32 else 2 ** -7 + 2 ** -12
         np.testing.assert_allclose(got[i], np.broadcast_to(want, got[i].shape), rtol=rel, atol=1e-6)
 
 
@@ -142,6 +148,34 @@ def test_partials_match_oracle(cfg, c):
     po = po.double().cpu().numpy()
     scale = np.maximum(l[:, :, None], 1.0)     # O is a sum of up to l-weighted values
     check_close(po / scale, o / scale, tol, "O / l")
+
+
+@pytest.mark.parametrize("cfg,c", [(3, 512), (2, 520)])
+def test_bf16_normalised_partials_match_oracle(cfg, c):
+    """The internal partial format of bf16 inputs: O / l rounded to bf16."""
+    wl = W.standard_workload(cfg, unscaled=True) if cfg == 2 else W.standard_workload(cfg)
+    if cfg == 2:
+        wl.q = wl.q[:, :8].contiguous()
+        wl.k_tokens = wl.k_tokens[:, :2].contiguous()
+        wl.v_tokens = wl.v_tokens[:, :2].contiguous()
+        wl.num_q_heads, wl.num_kv_heads = 8, 2
+    say("bf16 partials", cfg, c)
+    q, kc, vc, bt = gpu_inputs(wl)
+    desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    from tree_structured_decode_amd.runner import TreeAttention
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, c, desc, device=DEV)
+    po, pm, pl = ta.partials(q, kc, vc, bt, partial_format=D.DEFT_PARTIAL_BF16_NORM)
+    torch.cuda.synchronize()
+    plan = ref_plan(wl.parents, wl.seg_lens, wl.query_nodes, c)
+    ids, kp, vp = W.compact_pool(wl)
+    o, m, l = OA.chunk_partials(wl.q, kp, vp, wl.block_table, wl.parents, wl.seg_lens,
+                                wl.query_nodes, plan, page_ids=ids)
+    check_close(pm.double().cpu().numpy(), m, 2e-2, "m")
+    check_close(pl.double().cpu().numpy(), l, 2e-2, "l")
+    got = po.double().cpu().numpy()
+    want = o / l[:, :, None]
+    check_close(got, want, 2e-2, "O / l")
+    _rms_check(got, want, "O / l")
 
 
 def test_deterministic_and_writes_every_slot():

@@ -118,7 +118,10 @@ def test_device_bytes_and_unsupported_shapes():
     ok = D.make_desc(torch.bfloat16, 8, 2, 128, 100)
     pb, wb = D.deft_plan_device_bytes(plan, ok)
     slots = D.deft_plan_export(plan)["num_slots"]
-    assert pb > 0 and wb >= slots * 8 * (128 + 2) * 4
+    # bf16 inputs keep bf16 O / l plus fp32 m and l per (slot, head)
+    assert pb > 0 and wb >= slots * 8 * (128 * 2 + 8)
+    _, wb32 = D.deft_plan_device_bytes(plan, D.make_desc(torch.float32, 8, 2, 128, 100))
+    assert wb32 >= slots * 8 * (128 + 2) * 4
     for desc, code in [
         (D.make_desc(torch.bfloat16, 8, 2, 96, 100), D.DEFT_ERR_UNSUPPORTED),
         (D.make_desc(torch.bfloat16, 8, 3, 128, 100), D.DEFT_ERR_UNSUPPORTED),

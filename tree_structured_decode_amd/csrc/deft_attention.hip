@@ -74,11 +74,12 @@ struct PartialArgs {
   const void* k;
   const void* v;
   const int32_t* block_table;
-  float* po;
+  float* po;         // partial O: fp32 unnormalised, or bf16 divided by l (po_bf16)
   float* pm;
   float* pl;
   DevPlan plan;
   int32_t hq, hkv, grp;
+  int32_t po_bf16;   // 1: store O / l rounded to bf16 (internal workspace format)
   float scale_log2;  // log2(e) / sqrt(d)
 };
 
@@ -315,7 +316,8 @@ __global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
     }
     const int row = rb + r;
     const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
-    a.po[sh * D + e] = ov;
+    if (a.po_bf16) reinterpret_cast<uint16_t*>(a.po)[sh * D + e] = f32_to_bf16(ov / lsum);
+    else a.po[sh * D + e] = ov;
     if (e == 0) {
       a.pm[sh] = mx == kNegInf ? kNegInf : mx * kLn2;
       a.pl[sh] = lsum;
@@ -397,6 +399,7 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[RING_B > RED_B ? RING_B : RED_B];
   __shared__ __attribute__((aligned(16))) int32_t tok_row[kMaxChunkTokens];
   __shared__ float stats[NWAVE][WROWS][3];
+  __shared__ float row_ml[kMfmaRows][2];
 
   const DevPlan& P = a.plan;
   const int g = blockIdx.x % a.hkv;
@@ -613,8 +616,29 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
     }
   }
   __syncthreads();   // every wave is past its loop: the ring is free
-  // Each wave stores its O^T fragments scaled by exp2(m_run - M) (M the row's
-  // true max over the splits) as f32x4 at red[w][dt][rt][lane].
+  // Per row of the block: true max M over the splits and the total l.
+  for (int r = threadIdx.x; r < kMfmaRows; r += blockDim.x) {
+    const int hh = r / WROWS, rw = r % WROWS;
+    float mx = kNegInf;
+#pragma unroll
+    for (int q = 0; q < NSPLIT; ++q) mx = fmaxf(mx, stats[2 * q + hh][rw][1]);
+    float ls = 0.f;
+#pragma unroll
+    for (int q = 0; q < NSPLIT; ++q) {
+      const float mr = stats[2 * q + hh][rw][0];
+      ls += (mr == kNegInf) ? 0.f : fast_exp2((mr - mx) * cl2) * stats[2 * q + hh][rw][2];
+    }
+    row_ml[r][0] = mx;
+    row_ml[r][1] = ls;
+    if (r < nr) {
+      const int row = rb + r;
+      const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
+      a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
+      a.pl[sh] = ls;
+    }
+  }
+  // Each wave stores its O^T fragments scaled by exp2(m_run - M) as f32x4 at
+  // red[w][dt][rt][lane].
   f32x4* red = reinterpret_cast<f32x4*>(smem);
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
@@ -637,29 +661,25 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
     for (int q = 1; q < NSPLIT; ++q) acc += red[(((2 * q + hh) * DT + dt) * NRT + rt) * 64 + ln];
     const int row = rb + r;
     const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
-    *reinterpret_cast<f32x4*>(a.po + sh * D + dt * 16 + (ln >> 4) * 4) = acc;
-  }
-  for (int r = threadIdx.x; r < nr; r += blockDim.x) {
-    const int hh = r / WROWS, rw = r % WROWS;
-    float mx = kNegInf;
-#pragma unroll
-    for (int q = 0; q < NSPLIT; ++q) mx = fmaxf(mx, stats[2 * q + hh][rw][1]);
-    float ls = 0.f;
-#pragma unroll
-    for (int q = 0; q < NSPLIT; ++q) {
-      const float mr = stats[2 * q + hh][rw][0];
-      ls += (mr == kNegInf) ? 0.f : fast_exp2((mr - mx) * cl2) * stats[2 * q + hh][rw][2];
+    const int64_t at = sh * D + dt * 16 + (ln >> 4) * 4;
+    if (a.po_bf16) {
+      const float inv = 1.f / row_ml[r][1];
+      const uint32_t lo = f32_to_bf16(acc[0] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[1] * inv)) << 16);
+      const uint32_t hi = f32_to_bf16(acc[2] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[3] * inv)) << 16);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + at) = u32x2{lo, hi};
+    } else {
+      *reinterpret_cast<f32x4*>(a.po + at) = acc;
     }
-    const int row = rb + r;
-    const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
-    a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
-    a.pl[sh] = ls;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel: one wave per (query, query head); lanes split head_dim.
-// out = sum_s o_s exp(m_s - M) / sum_s l_s exp(m_s - M), M = max_s m_s.
+// Merge kernel: 16 lanes per (query, query head), each lane 8 (d = 128) or
+// 4 (d = 64) consecutive elements; a query's slots are loaded in batches of
+// up to 8 before any is accumulated.  With M = max_s m_s and
+// w_s = exp(m_s - M):
+//   fp32 unnormalised partials   out = sum_s w_s O_s / sum_s w_s l_s
+//   bf16 partials holding O_s/l_s out = sum_s w_s l_s (O_s/l_s) / sum_s w_s l_s
 // ---------------------------------------------------------------------------
 struct MergeArgs {
   const float* po;
@@ -668,50 +688,69 @@ struct MergeArgs {
   void* out;
   const int32_t* query_slot_offsets;
   const int32_t* query_slots;
-  int32_t nq, hq;
+  int32_t nq, hq, po_bf16;
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= a.nq * a.hq) return;
+  constexpr int LPP = 16;          // lanes per (query, head)
+  constexpr int EPL = D / LPP;     // elements per lane
+  constexpr int BATCH = 8;
+  const int pair = (blockIdx.x * 256 + threadIdx.x) / LPP;
+  const int sub = threadIdx.x % LPP;
+  if (pair >= a.nq * a.hq) return;           // whole 16-lane groups leave together
   const int qi = pair / a.hq, h = pair % a.hq;
   const int s0 = a.query_slot_offsets[qi], s1 = a.query_slot_offsets[qi + 1];
   float mx = kNegInf;
-  for (int i = s0 + lane; i < s1; i += 64)
-    mx = fmaxf(mx, a.pm[static_cast<int64_t>(a.query_slots[i]) * a.hq + h]);
+  for (int i = s0; i < s1; ++i) mx = fmaxf(mx, a.pm[static_cast<int64_t>(a.query_slots[i]) * a.hq + h]);
+  float acc[EPL];
 #pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
-  float acc[PER];
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  for (int i0 = s0; i0 < s1; i0 += BATCH) {
+    float wt[BATCH];
+    float vals[BATCH][EPL];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float lsum = 0.f;
-  for (int i0 = s0; i0 < s1; i0 += 64) {
-    const int n = min(64, s1 - i0);
-    int64_t sh_mine = 0;
-    float w_mine = 0.f;
-    if (lane < n) {
-      sh_mine = static_cast<int64_t>(a.query_slots[i0 + lane]) * a.hq + h;
-      const float mv = a.pm[sh_mine];
-      w_mine = mv == kNegInf ? 0.f : __expf(mv - mx);
-      lsum += w_mine * a.pl[sh_mine];
+    for (int j = 0; j < BATCH; ++j) {
+      const int i = min(i0 + j, s1 - 1);
+      const int64_t sh = static_cast<int64_t>(a.query_slots[i]) * a.hq + h;
+      const float mv = a.pm[sh], lv = a.pl[sh];
+      const float wj = (i0 + j < s1 && mv != kNegInf) ? __expf(mv - mx) : 0.f;
+      if (a.po_bf16) {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(a.po) + sh * D + sub * EPL;
+        if constexpr (EPL == 8) {
+          const u32x4 r = *reinterpret_cast<const u32x4*>(src);
+          Elem<uint16_t>::unpack(r, vals[j]);
+        } else {
+          const u32x2 r = *reinterpret_cast<const u32x2*>(src);
+          for (int e = 0; e < 2; ++e) {
+            vals[j][2 * e] = __uint_as_float(r[e] << 16);
+            vals[j][2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
+          }
+        }
+        wt[j] = wj * lv;
+      } else {
+        const float* src = a.po + sh * D + sub * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+          const f32x4 r = *reinterpret_cast<const f32x4*>(src + e);
+          for (int k = 0; k < 4; ++k) vals[j][e + k] = r[k];
+        }
+        wt[j] = wj;
+        wsum += wj * lv;
+      }
     }
-    for (int j = 0; j < n; ++j) {
-      const float wj = __shfl(w_mine, j);
-      const int64_t sh = __shfl(sh_mine, j);
-      const float* src = a.po + sh * D + lane * PER;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, src[e], acc[e]);
+    for (int j = 0; j < BATCH; ++j) {
+      if (a.po_bf16) wsum += wt[j];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wt[j], vals[j][e], acc[e]);
     }
   }
+  const float inv = 1.f / wsum;
+  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + sub * EPL;
 #pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) lsum += __shfl_xor(lsum, x);
-  const float inv = 1.f / lsum;
-  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + lane * PER;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) Elem<T>::store(a.out, ob + e, acc[e] * inv);
+  for (int e = 0; e < EPL; ++e) Elem<T>::store(a.out, ob + e, acc[e] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -783,7 +822,7 @@ static int launch_partials(const PartialArgs& pa, hipStream_t st) {
 
 static int run_partials(const void* q, const void* k, const void* v, const int32_t* bt,
                         const deft_plan* p, const deft_attn_desc* d, float* po, float* pm,
-                        float* pl, hipStream_t st) {
+                        float* pl, bool po_bf16, hipStream_t st) {
   if (!q || !k || !v || !bt || !po || !pm || !pl)
     return fail(DEFT_ERR_INVALID_ARGUMENT, "device pointers must not be NULL");
   PartialArgs pa;
@@ -798,6 +837,7 @@ static int run_partials(const void* q, const void* k, const void* v, const int32
   pa.hq = d->num_q_heads;
   pa.hkv = d->num_kv_heads;
   pa.grp = d->num_q_heads / d->num_kv_heads;
+  pa.po_bf16 = po_bf16 ? 1 : 0;
   pa.scale_log2 = kLog2e / std::sqrt(static_cast<float>(d->head_dim));
   if (d->dtype == DEFT_DTYPE_BF16)
     return d->head_dim == 128 ? launch_partials<uint16_t, 128>(pa, st) : launch_partials<uint16_t, 64>(pa, st);
@@ -805,7 +845,7 @@ static int run_partials(const void* q, const void* k, const void* v, const int32
 }
 
 static int run_merge(const deft_plan* p, const deft_attn_desc* d, const float* po, const float* pm,
-                     const float* pl, void* out, hipStream_t st) {
+                     const float* pl, void* out, bool po_bf16, hipStream_t st) {
   if (!po || !pm || !pl || !out) return fail(DEFT_ERR_INVALID_ARGUMENT, "device pointers must not be NULL");
   MergeArgs ma;
   ma.po = po;
@@ -817,7 +857,8 @@ static int run_merge(const deft_plan* p, const deft_attn_desc* d, const float* p
   ma.query_slots = dp.query_slots;
   ma.nq = p->num_queries;
   ma.hq = d->num_q_heads;
-  const int blocks = (ma.nq * ma.hq + 3) / 4;
+  ma.po_bf16 = po_bf16 ? 1 : 0;
+  const int blocks = (ma.nq * ma.hq + 15) / 16;
   if (d->dtype == DEFT_DTYPE_BF16) {
     if (d->head_dim == 128) hipLaunchKernelGGL((lse_merge<uint16_t, 128>), dim3(blocks), dim3(256), 0, st, ma);
     else hipLaunchKernelGGL((lse_merge<uint16_t, 64>), dim3(blocks), dim3(256), 0, st, ma);
@@ -854,21 +895,34 @@ int deft_plan_upload(deft_plan* p, const deft_attn_desc* d, void* dev_plan, size
   return DEFT_OK;
 }
 
+static int check_format(const deft_attn_desc* desc, int32_t fmt) {
+  if (fmt == DEFT_PARTIAL_F32) return DEFT_OK;
+  if (fmt == DEFT_PARTIAL_BF16_NORM && desc->dtype == DEFT_DTYPE_BF16) return DEFT_OK;
+  return fail(DEFT_ERR_INVALID_ARGUMENT, "partial_format must be DEFT_PARTIAL_F32, or DEFT_PARTIAL_BF16_NORM for bf16 inputs");
+}
+
 int deft_partial_attention(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const deft_plan* plan,
-                           const deft_attn_desc* desc, float* part_o, float* part_m, float* part_l,
-                           void* stream) {
+                           const deft_attn_desc* desc, void* part_o, float* part_m, float* part_l,
+                           int32_t partial_format, void* stream) {
   int rc = deft::check_ready(plan, desc);
   if (rc) return rc;
-  return deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, part_o, part_m, part_l,
+  rc = check_format(desc, partial_format);
+  if (rc) return rc;
+  return deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, static_cast<float*>(part_o),
+                            part_m, part_l, partial_format == DEFT_PARTIAL_BF16_NORM,
                             static_cast<hipStream_t>(stream));
 }
 
-int deft_lse_merge(const deft_plan* plan, const deft_attn_desc* desc, const float* part_o,
-                   const float* part_m, const float* part_l, void* out, void* stream) {
+int deft_lse_merge(const deft_plan* plan, const deft_attn_desc* desc, const void* part_o,
+                   const float* part_m, const float* part_l, int32_t partial_format, void* out,
+                   void* stream) {
   int rc = deft::check_ready(plan, desc);
   if (rc) return rc;
-  return deft::run_merge(plan, desc, part_o, part_m, part_l, out, static_cast<hipStream_t>(stream));
+  rc = check_format(desc, partial_format);
+  if (rc) return rc;
+  return deft::run_merge(plan, desc, static_cast<const float*>(part_o), part_m, part_l, out,
+                         partial_format == DEFT_PARTIAL_BF16_NORM, static_cast<hipStream_t>(stream));
 }
 
 int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
@@ -882,15 +936,18 @@ int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
     return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   const size_t need = deft::workspace_bytes_for(plan, desc);
   if (workspace_bytes < need) return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace too small");
+  // Internal partial format: bf16 O / l for bf16 inputs, fp32 unnormalised O otherwise.
+  const bool po_bf16 = desc->dtype == DEFT_DTYPE_BF16;
   const size_t sh = static_cast<size_t>(plan->num_slots) * desc->num_q_heads;
   auto align = [](size_t n) { return (n + 63) & ~static_cast<size_t>(63); };
   float* po = static_cast<float*>(workspace);
-  float* pm = po + align(sh * desc->head_dim);
+  const size_t o_words = deft::partial_o_words(plan, desc);
+  float* pm = po + align(o_words);
   float* pl = pm + align(sh);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, po, pm, pl, st);
+  rc = deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, po, pm, pl, po_bf16, st);
   if (rc) return rc;
-  return deft::run_merge(plan, desc, po, pm, pl, out, st);
+  return deft::run_merge(plan, desc, po, pm, pl, out, po_bf16, st);
 }
 
 }  // extern "C"

@@ -63,5 +63,8 @@ namespace deft {
 int build_image(deft_plan* p, const deft_attn_desc* desc, std::vector<int32_t>* image,
                 ImageLayout* layout);
 int check_desc(const deft_plan* p, const deft_attn_desc* desc);
+// Workspace: partial O (bf16 O / l for bf16 inputs, fp32 unnormalised O for
+// fp32 inputs), then part_m and part_l, each 256-byte aligned.
+size_t partial_o_words(const deft_plan* p, const deft_attn_desc* desc);
 size_t workspace_bytes_for(const deft_plan* p, const deft_attn_desc* desc);
 }  // namespace deft

@@ -189,9 +189,14 @@ int check_desc(const deft_plan* p, const deft_attn_desc* d) {
 
 static size_t align_words(size_t w) { return (w + 63) & ~static_cast<size_t>(63); }  // 256 B
 
+size_t partial_o_words(const deft_plan* p, const deft_attn_desc* d) {
+  const size_t n = static_cast<size_t>(p->num_slots) * d->num_q_heads * d->head_dim;
+  return d->dtype == DEFT_DTYPE_BF16 ? (n + 1) / 2 : n;
+}
+
 size_t workspace_bytes_for(const deft_plan* p, const deft_attn_desc* d) {
   const size_t sh = static_cast<size_t>(p->num_slots) * d->num_q_heads;
-  return 4 * (align_words(sh * d->head_dim) + 2 * align_words(sh));
+  return 4 * (align_words(partial_o_words(p, d)) + 2 * align_words(sh));
 }
 
 int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* image,

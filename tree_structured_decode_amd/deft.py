@@ -28,6 +28,8 @@ DEFT_ERR_HIP = -4
 DEFT_ERR_NO_MEMORY = -5
 DEFT_DTYPE_F32 = 0
 DEFT_DTYPE_BF16 = 1
+DEFT_PARTIAL_F32 = 0
+DEFT_PARTIAL_BF16_NORM = 1
 
 EXPORTED_SYMBOLS = (
     "deft_plan_create", "deft_plan_destroy", "deft_plan_export", "deft_plan_device_bytes",
@@ -84,8 +86,9 @@ def lib() -> ctypes.CDLL:
     L.deft_tree_attention.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.POINTER(deft_attn_desc),
                                       _P, ctypes.c_size_t, _P]
     L.deft_partial_attention.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(deft_attn_desc),
-                                         _P, _P, _P, _P]
-    L.deft_lse_merge.argtypes = [_P, ctypes.POINTER(deft_attn_desc), _P, _P, _P, _P, _P]
+                                         _P, _P, _P, ctypes.c_int32, _P]
+    L.deft_lse_merge.argtypes = [_P, ctypes.POINTER(deft_attn_desc), _P, _P, _P, ctypes.c_int32,
+                                 _P, _P]
     L.deft_last_error.restype = ctypes.c_char_p
     for name in ("deft_plan_create", "deft_plan_export", "deft_plan_device_bytes", "deft_plan_upload",
                  "deft_tree_attention", "deft_partial_attention", "deft_lse_merge"):
@@ -204,12 +207,13 @@ def deft_tree_attention(q, k_cache, v_cache, block_table, plan: Plan, out, desc,
 
 
 def deft_partial_attention(q, k_cache, v_cache, block_table, plan: Plan, desc, part_o, part_m,
-                           part_l, stream=None):
+                           part_l, partial_format=DEFT_PARTIAL_F32, stream=None):
     _check(lib().deft_partial_attention(_dev(q), _dev(k_cache), _dev(v_cache), _dev(block_table),
                                         plan.handle, ctypes.byref(desc), _dev(part_o), _dev(part_m),
-                                        _dev(part_l), _stream(stream)))
+                                        _dev(part_l), int(partial_format), _stream(stream)))
 
 
-def deft_lse_merge(plan: Plan, desc, part_o, part_m, part_l, out, stream=None):
+def deft_lse_merge(plan: Plan, desc, part_o, part_m, part_l, out, partial_format=DEFT_PARTIAL_F32,
+                   stream=None):
     _check(lib().deft_lse_merge(plan.handle, ctypes.byref(desc), _dev(part_o), _dev(part_m),
-                                _dev(part_l), _dev(out), _stream(stream)))
+                                _dev(part_l), int(partial_format), _dev(out), _stream(stream)))

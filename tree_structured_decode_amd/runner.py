@@ -34,14 +34,17 @@ class TreeAttention:
                               self.workspace, stream)
         return out
 
-    def partials(self, q, k_cache, v_cache, block_table, stream=None):
-        """Per-slot (O, m, l) from the partial kernel alone, fp32 device tensors."""
+    def partials(self, q, k_cache, v_cache, block_table, partial_format=D.DEFT_PARTIAL_F32, stream=None):
+        """Per-slot (O, m, l) from the partial kernel alone, as device tensors
+        (O fp32 unnormalised, or bf16 divided by l)."""
         s = self.plan_view_counts()
         hq, d = self.desc.num_q_heads, self.desc.head_dim
-        po = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
+        odt = torch.bfloat16 if partial_format == D.DEFT_PARTIAL_BF16_NORM else torch.float32
+        po = torch.empty((s, hq, d), dtype=odt, device=q.device)
         pm = torch.empty((s, hq), dtype=torch.float32, device=q.device)
         pl = torch.empty((s, hq), dtype=torch.float32, device=q.device)
-        D.deft_partial_attention(q, k_cache, v_cache, block_table, self.plan, self.desc, po, pm, pl, stream)
+        D.deft_partial_attention(q, k_cache, v_cache, block_table, self.plan, self.desc, po, pm, pl,
+                                 partial_format, stream)
         return po, pm, pl
 
     def plan_view_counts(self) -> int:
