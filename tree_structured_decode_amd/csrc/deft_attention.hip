@@ -674,12 +674,14 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel: 16 lanes per (query, query head), each lane 8 (d = 128) or
-// 4 (d = 64) consecutive elements; a query's slots are loaded in batches of
-// up to 8 before any is accumulated.  With M = max_s m_s and
-// w_s = exp(m_s - M):
+// Merge kernel: one wave per (query, query head).  Lane i of the wave reads
+// the metadata (slot id, m, l) of the query's i-th slot, so a query's whole
+// slot list costs one round of dependent loads; the partial O rows are then
+// read by four 16-lane groups, group g taking slots g, g + 4, ..., each lane
+// D/16 consecutive elements.  With M = max_s m_s and w_s = exp(m_s - M):
 //   fp32 unnormalised partials   out = sum_s w_s O_s / sum_s w_s l_s
 //   bf16 partials holding O_s/l_s out = sum_s w_s l_s (O_s/l_s) / sum_s w_s l_s
+// Queries with more than 64 slots take several rounds, rescaled online.
 // ---------------------------------------------------------------------------
 struct MergeArgs {
   const float* po;
@@ -691,66 +693,126 @@ struct MergeArgs {
   int32_t nq, hq, po_bf16;
 };
 
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) x = fmaxf(x, __shfl_xor(x, k));
+  return x;
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) x += __shfl_xor(x, k);
+  return x;
+}
+
+// EPL consecutive elements of one partial O row (slot-head sh), as fp32.
+template <int D, int EPL>
+__device__ inline void load_partial_row(const MergeArgs& a, int64_t sh, int sub, float* v) {
+  if (a.po_bf16) {
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.po) + sh * D + sub * EPL;
+    if constexpr (EPL == 8) {
+      Elem<uint16_t>::unpack(*reinterpret_cast<const u32x4*>(src), v);
+    } else {
+      const u32x2 r = *reinterpret_cast<const u32x2*>(src);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        v[2 * e] = __uint_as_float(r[e] << 16);
+        v[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float* src = a.po + sh * D + sub * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const f32x4 r = *reinterpret_cast<const f32x4*>(src + e);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[e + k] = r[k];
+    }
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
-  constexpr int LPP = 16;          // lanes per (query, head)
-  constexpr int EPL = D / LPP;     // elements per lane
-  constexpr int BATCH = 8;
-  const int pair = (blockIdx.x * 256 + threadIdx.x) / LPP;
-  const int sub = threadIdx.x % LPP;
-  if (pair >= a.nq * a.hq) return;           // whole 16-lane groups leave together
+  constexpr int EPL = D / 16;      // elements per lane
+  constexpr int KU = 4;            // slots per group read before any is accumulated
+  constexpr int PER_G = EPL / 4;   // output elements each lane stores
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.nq * a.hq) return;           // whole waves leave together
   const int qi = pair / a.hq, h = pair % a.hq;
+  const int grp = lane >> 4, sub = lane & 15;
   const int s0 = a.query_slot_offsets[qi], s1 = a.query_slot_offsets[qi + 1];
-  float mx = kNegInf;
-  for (int i = s0; i < s1; ++i) mx = fmaxf(mx, a.pm[static_cast<int64_t>(a.query_slots[i]) * a.hq + h]);
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  float wsum = 0.f;
-  for (int i0 = s0; i0 < s1; i0 += BATCH) {
-    float wt[BATCH];
-    float vals[BATCH][EPL];
+  float mrun = kNegInf, wsum = 0.f;
+  for (int i0 = s0; i0 < s1; i0 += 64) {
+    const int n = min(64, s1 - i0);
+    // lanes past the list re-read its first slot and get weight 0
+    const int slot = a.query_slots[i0 + (lane < n ? lane : 0)];
+    const int64_t sh = static_cast<int64_t>(slot) * a.hq + h;
+    const float mv = lane < n ? a.pm[sh] : kNegInf;
+    const float lv = lane < n ? a.pl[sh] : 0.f;
+    // first KU slots of each group, issued before the reductions
+    float vals[KU][EPL];
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int i = min(i0 + j, s1 - 1);
-      const int64_t sh = static_cast<int64_t>(a.query_slots[i]) * a.hq + h;
-      const float mv = a.pm[sh], lv = a.pl[sh];
-      const float wj = (i0 + j < s1 && mv != kNegInf) ? __expf(mv - mx) : 0.f;
-      if (a.po_bf16) {
-        const uint16_t* src = reinterpret_cast<const uint16_t*>(a.po) + sh * D + sub * EPL;
-        if constexpr (EPL == 8) {
-          const u32x4 r = *reinterpret_cast<const u32x4*>(src);
-          Elem<uint16_t>::unpack(r, vals[j]);
-        } else {
-          const u32x2 r = *reinterpret_cast<const u32x2*>(src);
-          for (int e = 0; e < 2; ++e) {
-            vals[j][2 * e] = __uint_as_float(r[e] << 16);
-            vals[j][2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
-          }
-        }
-        wt[j] = wj * lv;
-      } else {
-        const float* src = a.po + sh * D + sub * EPL;
-#pragma unroll
-        for (int e = 0; e < EPL; e += 4) {
-          const f32x4 r = *reinterpret_cast<const f32x4*>(src + e);
-          for (int k = 0; k < 4; ++k) vals[j][e + k] = r[k];
-        }
-        wt[j] = wj;
-        wsum += wj * lv;
-      }
+    for (int u = 0; u < KU; ++u) {
+      const int j = grp + 4 * u;
+      const int sj = __shfl(slot, j < n ? j : 0);
+      load_partial_row<D, EPL>(a, static_cast<int64_t>(sj) * a.hq + h, sub, vals[u]);
     }
+    const float mnew = fmaxf(mrun, wave_max(mv));
+    const float w = mv == kNegInf ? 0.f : __expf(mv - mnew);
+    const float wl = w * lv;
+    const float wt = a.po_bf16 ? wl : w;      // weight of the stored O row
+    const float rescale = mrun == kNegInf ? 0.f : __expf(mrun - mnew);
+    mrun = mnew;
+    wsum = wsum * rescale + wave_sum(wl);
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      if (a.po_bf16) wsum += wt[j];
+    for (int e = 0; e < EPL; ++e) acc[e] *= rescale;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wt[j], vals[j][e], acc[e]);
+    for (int u = 0; u < KU; ++u) {
+      const int j = grp + 4 * u;
+      const float wj = __shfl(wt, j < n ? j : 63);
+      const float wu = j < n ? wj : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wu, vals[u][e], acc[e]);
+    }
+    for (int j0 = 4 * KU; j0 < n; j0 += 4) {
+      const int j = j0 + grp;
+      const int sj = __shfl(slot, j < n ? j : 0);
+      const float wj = __shfl(wt, j < n ? j : 63);
+      float v[EPL];
+      load_partial_row<D, EPL>(a, static_cast<int64_t>(sj) * a.hq + h, sub, v);
+      const float wu = j < n ? wj : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wu, v[e], acc[e]);
     }
   }
-  const float inv = 1.f / wsum;
-  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + sub * EPL;
+  // sum the four groups; every group then holds the full row
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) Elem<T>::store(a.out, ob + e, acc[e] * inv);
+  for (int e = 0; e < EPL; ++e) {
+    acc[e] += __shfl_xor(acc[e], 16);
+    acc[e] += __shfl_xor(acc[e], 32);
+  }
+  const float inv = 1.f / wsum;
+  // group g stores elements [g * PER_G, (g + 1) * PER_G) of each lane's EPL
+  float x[PER_G];
+#pragma unroll
+  for (int k = 0; k < PER_G; ++k) {
+    x[k] = acc[k];
+#pragma unroll
+    for (int g = 1; g < 4; ++g) x[k] = grp == g ? acc[g * PER_G + k] : x[k];
+    x[k] *= inv;
+  }
+  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + sub * EPL + grp * PER_G;
+  if constexpr (sizeof(T) == 2 && PER_G == 2) {
+    const uint32_t pk = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + ob) = pk;
+  } else {
+#pragma unroll
+    for (int k = 0; k < PER_G; ++k) Elem<T>::store(a.out, ob + k, x[k]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -858,7 +920,7 @@ static int run_merge(const deft_plan* p, const deft_attn_desc* d, const float* p
   ma.nq = p->num_queries;
   ma.hq = d->num_q_heads;
   ma.po_bf16 = po_bf16 ? 1 : 0;
-  const int blocks = (ma.nq * ma.hq + 15) / 16;
+  const int blocks = (ma.nq * ma.hq + 3) / 4;
   if (d->dtype == DEFT_DTYPE_BF16) {
     if (d->head_dim == 128) hipLaunchKernelGGL((lse_merge<uint16_t, 128>), dim3(blocks), dim3(256), 0, st, ma);
     else hipLaunchKernelGGL((lse_merge<uint16_t, 64>), dim3(blocks), dim3(256), 0, st, ma);
