@@ -378,6 +378,18 @@ __device__ inline float rowsum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Two-wave rendezvous through LDS: publish `i` in *mine, then wait until
+// *theirs reaches `i`.  Both waves of a pair run the same iteration count,
+// so every wait ends; the spin is also bounded so that a broken pairing can
+// only produce wrong values, never a wave that does not finish.
+__device__ inline void pair_sync(int32_t* mine, int32_t* theirs, int32_t i, int lane) {
+  if (lane == 0) __hip_atomic_store(mine, i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  for (int spin = 0; spin < (1 << 20); ++spin) {
+    if (__hip_atomic_load(theirs, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= i) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   constexpr int NWAVE = 8;
@@ -400,6 +412,7 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) int32_t tok_row[kMaxChunkTokens];
   __shared__ float stats[NWAVE][WROWS][3];
   __shared__ float row_ml[kMfmaRows][2];
+  __shared__ int32_t pair_ready[NSPLIT][2];
 
   const DevPlan& P = a.plan;
   const int g = blockIdx.x % a.hkv;
@@ -435,6 +448,7 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   stage_token_rows<RPI>(tok_row, P, a.block_table, cs, len);
   // Row of the mask word this lane loads (lane i <-> row i of the block).
   const int32_t mask_slot = gofs + (rb + (lane < nr ? lane : 0)) / a.grp;
+  if (threadIdx.x < 2 * NSPLIT) pair_ready[threadIdx.x >> 1][threadIdx.x & 1] = -1;
   __syncthreads();
 
   const int64_t hstride = static_cast<int64_t>(a.hkv) * D;
@@ -499,11 +513,13 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   for (int i = 0; i < iters; ++i) {
     const int step = sp + i * NSPLIT;
     const int stage = i & 1;
-    // This wave's loads for `step` are done; the barrier makes the partner's
-    // visible and guarantees every wave has finished step i-1, so the other
-    // stage can be refilled with step i+1.
+    // This wave's loads for `step` are done.  Only the two waves of a split
+    // share a ring, so they synchronise with each other instead of the whole
+    // work-group: each publishes "my half of iteration i is in LDS and I have
+    // finished iteration i-1", then waits for the partner to say the same, after
+    // which the other stage can be refilled with step i+1.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
+    pair_sync(&pair_ready[sp][h], &pair_ready[sp][h ^ 1], i, lane);
     if (step + NSPLIT < nsteps) issue(stage ^ 1, step + NSPLIT);
     if (step >= nsteps) continue;
     const int base = step * 32;
@@ -511,7 +527,9 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
     const char* vb = kb + TILE_B;
     const uint32_t* mb = reinterpret_cast<const uint32_t*>(kb + 2 * TILE_B);
 
-    // S^T = K Q^T
+    // S^T = K Q^T.  Waves raise their issue priority around MFMA runs so that
+    // the SIMD's other wave fills the gaps with its softmax arithmetic.
+    __builtin_amdgcn_s_setprio(1);
     f32x4 s[2][NRT];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -528,6 +546,7 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
           s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][ks], s[tt][rt], 0, 0, 0);
       }
 
+    __builtin_amdgcn_s_setprio(0);
     // Mask and online softmax.  Lane holds tokens base + 8*lj + e of row
     // 32h + rt*16 + lr; scores stay in raw units, exp2 folds in scale*log2(e).
     // The running max m_run of a row (shared by its 4 lanes) only rises when
@@ -586,6 +605,7 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
     // 16dt + 4(lr % 4), so it receives V[8lj + 4h' + k][16dt + lr], k = 0..3.
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       u32x2 half[2];
@@ -601,6 +621,7 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
       for (int rt = 0; rt < NRT; ++rt)
         o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rt], o[dt][rt], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Combine the four token splits of each row half: true max, per-split
