@@ -35,6 +35,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 #include <vector>
 
 #include "deft_internal.h"
@@ -119,44 +120,45 @@ __device__ inline u32x4 load16(const void* base, int64_t elem_off, int elem_byte
   return *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + elem_off * elem_bytes);
 }
 
-// Pool row (page * 16 + slot) of every flat token of the chunk, into LDS.
-// All flat-to-logical loads are issued before any block-table load so the
-// two dependent lookups cost two memory latencies, not two per token.  With
-// RPI > 0 the rows of each 32-token step are stored permuted, entry
-// (t % RPI) * (32 / RPI) + (t % 32) / RPI, which puts the rows one lane of a
-// direct-to-LDS load sequence needs next to each other.
-template <int RPI, int N>
+// Pool row (page * 16 + slot) of every flat token of the chunk, into LDS,
+// stored as row * mul + add.  All flat-to-logical loads are issued before any
+// block-table load so the two dependent lookups cost two memory latencies,
+// not two per token.  With RPI > 0 the rows of each 32-token step are stored
+// permuted, entry (t % RPI) * (32 / RPI) + (t % 32) / RPI, which puts the rows
+// one lane of a direct-to-LDS load sequence needs next to each other.  NT is
+// the work-group size.
+template <int RPI, int NT, int N>
 __device__ inline void stage_token_rows_n(int32_t* tok_row, const DevPlan& P, const int32_t* bt,
-                                          int32_t cs, int32_t len) {
+                                          int32_t cs, int32_t len, int32_t mul, int32_t add) {
   // N fixed loads per thread, no branches between them; indices past the
   // chunk end re-read its last token and are not stored.
   int32_t lt[N];
 #pragma unroll
   for (int k = 0; k < N; ++k)
-    lt[k] = P.flat_to_logical[cs + min(static_cast<int>(threadIdx.x) + k * 256, len - 1)];
+    lt[k] = P.flat_to_logical[cs + min(static_cast<int>(threadIdx.x) + k * NT, len - 1)];
   int32_t pg[N];
 #pragma unroll
   for (int k = 0; k < N; ++k) pg[k] = bt[lt[k] >> 4];
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    const int t = threadIdx.x + k * 256;
+    const int t = threadIdx.x + k * NT;
     if (t < len) {
       int at = t;
       if constexpr (RPI > 0) at = (t & ~31) + (t % RPI) * (32 / RPI) + (t & 31) / RPI;
-      tok_row[at] = pg[k] * kPageSize + (lt[k] & (kPageSize - 1));
+      tok_row[at] = (pg[k] * kPageSize + (lt[k] & (kPageSize - 1))) * mul + add;
     }
   }
 }
-template <int RPI = 0>
+template <int RPI, int NT>
 __device__ inline void stage_token_rows(int32_t* tok_row, const DevPlan& P, const int32_t* bt,
-                                        int32_t cs, int32_t len) {
-  static_assert(kMaxChunkTokens == 16 * 256, "staging batches assume 256 threads");
-  const int nk = (len + 255) / 256;
-  if (nk <= 1) stage_token_rows_n<RPI, 1>(tok_row, P, bt, cs, len);
-  else if (nk <= 2) stage_token_rows_n<RPI, 2>(tok_row, P, bt, cs, len);
-  else if (nk <= 4) stage_token_rows_n<RPI, 4>(tok_row, P, bt, cs, len);
-  else if (nk <= 8) stage_token_rows_n<RPI, 8>(tok_row, P, bt, cs, len);
-  else stage_token_rows_n<RPI, 16>(tok_row, P, bt, cs, len);
+                                        int32_t cs, int32_t len, int32_t mul = 1, int32_t add = 0) {
+  static_assert(kMaxChunkTokens <= 16 * NT, "at most 16 staging batches");
+  const int nk = (len + NT - 1) / NT;
+  if (nk <= 1) stage_token_rows_n<RPI, NT, 1>(tok_row, P, bt, cs, len, mul, add);
+  else if (nk <= 2) stage_token_rows_n<RPI, NT, 2>(tok_row, P, bt, cs, len, mul, add);
+  else if (nk <= 4) stage_token_rows_n<RPI, NT, 4>(tok_row, P, bt, cs, len, mul, add);
+  else if (nk <= 8) stage_token_rows_n<RPI, NT, 8>(tok_row, P, bt, cs, len, mul, add);
+  else stage_token_rows_n<RPI, NT, 16>(tok_row, P, bt, cs, len, mul, add);
 }
 
 // ---------------------------------------------------------------------------
@@ -179,16 +181,16 @@ __global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
 
   const DevPlan& P = a.plan;
   const int g = blockIdx.x % a.hkv;
-  const int4 item = P.valu_items[blockIdx.x / a.hkv];
-  const int32_t c = item.x, rb = item.y, nr = item.z;
-  const int32_t cs = P.chunk_start[c], len = P.chunk_start[c + 1] - cs;
-  const int32_t gofs = P.group_offsets[c];
-  const bool full = P.chunk_full[c] != 0;
+  const int4 it0 = P.valu_items[2 * (blockIdx.x / a.hkv)];
+  const int4 it1 = P.valu_items[2 * (blockIdx.x / a.hkv) + 1];
+  const int32_t rb = it0.y, nr = it0.z, cs = it0.w;
+  const int32_t len = it1.x, gofs = it1.y;
+  const bool full = it1.z != 0;
   const int W = P.mask_words;
   const int j0 = rb / a.grp;
   const int nslot = (rb + nr - 1) / a.grp - j0 + 1;
 
-  stage_token_rows(tok_row, P, a.block_table, cs, len);
+  stage_token_rows<0, 256>(tok_row, P, a.block_table, cs, len);
   if (!full)
     for (int i = threadIdx.x; i < nslot * W; i += blockDim.x)
       masks[i] = P.slot_mask[static_cast<size_t>(gofs + j0) * W + i];
@@ -416,12 +418,12 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
 
   const DevPlan& P = a.plan;
   const int g = blockIdx.x % a.hkv;
-  const int4 item = P.mfma_items[blockIdx.x / a.hkv];
-  const int32_t c = item.x, rb = item.y, nr = item.z;
-  const int32_t cs = P.chunk_start[c], len = P.chunk_start[c + 1] - cs;
-  const int32_t gofs = P.group_offsets[c];
+  const int4 it0 = P.mfma_items[2 * (blockIdx.x / a.hkv)];
+  const int4 it1 = P.mfma_items[2 * (blockIdx.x / a.hkv) + 1];
+  const int32_t rb = it0.y, nr = it0.z, cs = it0.w;
+  const int32_t len = it1.x, gofs = it1.y;
+  const bool full = it1.z != 0;
   const int W = P.mask_words;
-  const bool full = P.chunk_full[c] != 0;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -431,28 +433,31 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   const uint16_t* kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* vp = static_cast<const uint16_t*>(a.v);
 
-  // Q^T fragments (B operand of S^T = K Q^T) of this wave's 32 rows, loaded
-  // before the token rows so the two latencies overlap.
+  // The queries of this wave's rows are looked up before the token rows are
+  // staged, so both dependent lookups overlap; rows past nr read a valid row
+  // and are masked later.
+  int32_t sq[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+    sq[rt] = P.slot_query[gofs + (rb + min(WROWS * h + rt * 16 + lr, nr - 1)) / a.grp];
+  // token rows are stored as rows of this KV head: pool row * Hkv + g
+  stage_token_rows<RPI, 512>(tok_row, P, a.block_table, cs, len, a.hkv, g);
+  // Q^T fragments (B operand of S^T = K Q^T) of this wave's 32 rows.
   bf16x8 qf[NRT][KS];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    const int r = min(WROWS * h + rt * 16 + lr, nr - 1);   // rows past nr load a valid row; masked later
-    const int row = rb + r;
-    const int32_t qi = P.slot_query[gofs + row / a.grp];
+    const int row = rb + min(WROWS * h + rt * 16 + lr, nr - 1);
     const int head = g * a.grp + row % a.grp;
-    const uint16_t* src = qp + (static_cast<int64_t>(qi) * a.hq + head) * D + lj * 8;
+    const uint16_t* src = qp + (static_cast<int64_t>(sq[rt]) * a.hq + head) * D + lj * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[rt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 32));
   }
-  stage_token_rows<RPI>(tok_row, P, a.block_table, cs, len);
   // Row of the mask word this lane loads (lane i <-> row i of the block).
   const int32_t mask_slot = gofs + (rb + (lane < nr ? lane : 0)) / a.grp;
   if (threadIdx.x < 2 * NSPLIT) pair_ready[threadIdx.x >> 1][threadIdx.x & 1] = -1;
   __syncthreads();
 
-  const int64_t hstride = static_cast<int64_t>(a.hkv) * D;
-  const int64_t goff = static_cast<int64_t>(g) * D;
   char* ring = smem + sp * 2 * STAGE_B;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
   const int lrow = lane / CH;            // row of each direct load this lane fetches
@@ -461,9 +466,15 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   // This wave's half of a step's loads (h = 0: K rows and mask words; h = 1:
   // V rows).  Load n fetches rows n*RPI + lrow; lane (lrow, lch) fetches chunk
   // lch ^ (R % CH) of row R, so LDS slot p of row R holds chunk p ^ (R % CH).
+  // The swizzle depends on n only through n % NSW, so each lane keeps NSW base
+  // pointers and a load address is one shift-add of the staged head row.
   // Tokens past the chunk end re-read its last token (finite values; masked).
-  auto issue = [&](int stage, int step) {
-    const uint32_t kd = ring_lds + stage * STAGE_B;
+  constexpr int NSW = RPI < CH ? CH / RPI : 1;
+  const char* lbase[NSW];
+#pragma unroll
+  for (int c = 0; c < NSW; ++c)
+    lbase[c] = reinterpret_cast<const char*>(h ? vp : kp) + (lch ^ ((c * RPI + lrow) % CH)) * 16;
+  auto load_ptrs = [&](int step, const char** ptr) {
     const int base = step * 32;
     int32_t rows[NI];
     if (base + 32 <= len) {
@@ -480,16 +491,11 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
         rows[n] = tok_row[(t & ~31) + (t % RPI) * (32 / RPI) + (t & 31) / RPI];
       }
     }
-    const uint16_t* src = h ? vp : kp;
-    const uint32_t dst = kd + h * TILE_B;
 #pragma unroll
-    for (int n = 0; n < NI; ++n) {
-      const int R = n * RPI + lrow;
-      const int64_t off = static_cast<int64_t>(rows[n]) * hstride + goff + ((lch ^ (R % CH)) * 8);
-      lds_dma16(src + off, dst + n * 1024);
-    }
-    if (h == 0) lds_dma4(P.slot_mask + static_cast<size_t>(mask_slot) * W + step, kd + 2 * TILE_B);
+    for (int n = 0; n < NI; ++n)
+      ptr[n] = lbase[n % NSW] + (static_cast<uint64_t>(static_cast<uint32_t>(rows[n])) * ROWB);
   };
+  const uint32_t* mask_src = P.slot_mask + static_cast<size_t>(mask_slot) * W;
 
   f32x4 o[DT][NRT];
 #pragma unroll
@@ -504,54 +510,88 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
     l_part[rt] = 0.f;
   }
   const float cl2 = a.scale_log2;
-  // K rows this lane reads for the A operand, per token tile.
-  const int rk0 = 8 * (lr >> 2) + (lr & 3);
   const int nsteps = (len + 31) / 32;
   const int iters = (nsteps + NSPLIT - 1) / NSPLIT;   // the same for every wave
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-  if (sp < nsteps) issue(0, sp);
-  for (int i = 0; i < iters; ++i) {
+  // LDS byte offsets (within a stage) of this lane's operand fragments: K
+  // fragment n = (ks, tt) for S, and the two halves of V^T d-tile dt for PV.
+  const int rk0 = 8 * (lr >> 2) + (lr & 3);   // K rows of this lane, per token tile
+  int koff[2 * KS], voff[DT][2];
+#pragma unroll
+  for (int n = 0; n < 2 * KS; ++n) {
+    const int ks = n >> 1, R = rk0 + 4 * (n & 1);
+    koff[n] = R * ROWB + (((ks * 4 + lj) ^ (R % CH)) * 16);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int R = 8 * lj + 4 * hh + (lr >> 2);
+      voff[dt][hh] = TILE_B + R * ROWB + (((2 * dt + ((lr & 3) >> 1)) ^ (R % CH)) * 16) + 8 * (lr & 1);
+    }
+
+  if (sp < nsteps) {
+    const char* ptr[NI];
+    load_ptrs(sp, ptr);
+#pragma unroll
+    for (int n = 0; n < NI; ++n) lds_dma16(ptr[n], ring_lds + h * TILE_B + n * 1024);
+    if (h == 0) lds_dma4(mask_src + sp, ring_lds + 2 * TILE_B);
+  }
+  static_assert(2 * KS == NI && DT == NI, "the next step's loads are spread one per two MFMA groups");
+
+  // One step on ring stage STG (a compile-time constant, so every LDS address
+  // is a per-lane base plus an immediate offset).
+  auto step_body = [&](auto stg, int i) {
+    constexpr int STG = decltype(stg)::value;
     const int step = sp + i * NSPLIT;
-    const int stage = i & 1;
     // This wave's loads for `step` are done.  Only the two waves of a split
     // share a ring, so they synchronise with each other instead of the whole
     // work-group: each publishes "my half of iteration i is in LDS and I have
-    // finished iteration i-1", then waits for the partner to say the same, after
-    // which the other stage can be refilled with step i+1.
+    // finished iteration i-1", then waits for the partner to say the same,
+    // after which the other stage can be refilled with step i+1.
+    // (The wait for all loads also covers the Q loads, so the compiler
+    // places none in the loop.)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     pair_sync(&pair_ready[sp][h], &pair_ready[sp][h ^ 1], i, lane);
-    if (step + NSPLIT < nsteps) issue(stage ^ 1, step + NSPLIT);
-    if (step >= nsteps) continue;
+    if (step >= nsteps) return;
+    const bool next = step + NSPLIT < nsteps;
     const int base = step * 32;
-    const char* kb = ring + stage * STAGE_B;
-    const char* vb = kb + TILE_B;
+    const char* kb = ring + STG * STAGE_B;
     const uint32_t* mb = reinterpret_cast<const uint32_t*>(kb + 2 * TILE_B);
+    const uint32_t nd = ring_lds + (STG ^ 1) * STAGE_B + h * TILE_B;   // this wave's half of the other stage
+    // The next step's loads are spread over this step's MFMAs (one after
+    // every second MFMA group), so the wave keeps the matrix unit busy while
+    // the memory pipeline takes them.
+    const char* ptr[NI];
+    if (next) load_ptrs(step + NSPLIT, ptr);
 
-    // S^T = K Q^T.  Waves raise their issue priority around MFMA runs so that
-    // the SIMD's other wave fills the gaps with its softmax arithmetic.
+    // S^T = K Q^T; fragment n = (ks, tt) is read one group ahead of its MFMAs.
+    // Waves raise their issue priority around MFMA runs so that the SIMD's
+    // other wave fills the gaps with its softmax arithmetic.
     __builtin_amdgcn_s_setprio(1);
-    f32x4 s[2][NRT];
+    f32x4 sacc[2][NRT];
+    bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + koff[0]);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int n = 0; n < 2 * KS; ++n) {
+      const bf16x8 kn = *reinterpret_cast<const bf16x8*>(kb + koff[n + 1 < 2 * KS ? n + 1 : n]);
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) s[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int R = rk0 + 4 * tt;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + R * ROWB + (((ks * 4 + lj) ^ (R % CH)) * 16));
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-          s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][ks], s[tt][rt], 0, 0, 0);
-      }
-
+      for (int rt = 0; rt < NRT; ++rt)
+        sacc[n & 1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            kf, qf[rt][n >> 1], n < 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[n & 1][rt], 0, 0, 0);
+      if (next && (n & 1)) lds_dma16(ptr[n >> 1], nd + (n >> 1) * 1024);
+      kf = kn;
+    }
     __builtin_amdgcn_s_setprio(0);
+
     // Mask and online softmax.  Lane holds tokens base + 8*lj + e of row
     // 32h + rt*16 + lr; scores stay in raw units, exp2 folds in scale*log2(e).
     // The running max m_run of a row (shared by its 4 lanes) only rises when
     // some lane sees a score above m_run + slack; only then are the 4 lanes
-    // reduced.  The true max is tracked per lane and reduced at the end.
+    // reduced.  The true max is tracked per lane and reduced at the end.  l
+    // sums the probabilities as rounded to bf16 for the PV product.
     bf16x8 pb[NRT];
     const int valid_e = len - base - 8 * lj;   // tokens of this lane's 8 that exist
     const bool all_visible = full && valid_e >= 8;
@@ -561,7 +601,7 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
       const bool row_ok = rl < nr;
       float z[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = e < 4 ? s[0][rt][e] : s[1][rt][e - 4];
+      for (int e = 0; e < 8; ++e) z[e] = e < 4 ? sacc[0][rt][e] : sacc[1][rt][e - 4];
       if (!all_visible) {
         const uint32_t bits = row_ok ? (mb[rl] >> (8 * lj)) & 0xffu : 0u;
 #pragma unroll
@@ -588,14 +628,15 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
       // a row with nothing visible yet keeps m = -inf; its z are all -inf too
       const float mc = m_run[rt] == kNegInf ? 0.f : m_run[rt] * cl2;
       f32x8 p;
-      float ls = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(fmaf(z[e], cl2, -mc));   // z = -inf gives 0
-        ls += p[e];
-      }
-      l_part[rt] += ls;
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(z[e], cl2, -mc));   // z = -inf gives 0
       pb[rt] = __builtin_convertvector(p, bf16x8);
+      const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+      float ls = l_part[rt];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[rt][e], pb[rt][e + 1]}, one, ls, false);
+      l_part[rt] = ls;
     }
 
     // O^T += V^T P^T.  V^T fragments come from LDS transpose reads of the
@@ -603,25 +644,32 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
     // lane i element (i % 4) of the 8 bytes that lane 4k + i/4 addresses, as
     // its k-th element.  Lane (lr, lj) addresses row 8lj + 4h' + lr/4 at d
     // 16dt + 4(lr % 4), so it receives V[8lj + 4h' + k][16dt + lr], k = 0..3.
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    // Fragments are read one d-tile ahead of their MFMAs.
+    auto vfrag = [&](int dt) {
       u32x2 half[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int R = 8 * lj + 4 * hh + (lr >> 2);
-        const int ch = (2 * dt + ((lr & 3) >> 1)) ^ (R % CH);
+      for (int hh = 0; hh < 2; ++hh)
         half[hh] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                       (lds_s16x4_t)(vb + R * ROWB + ch * 16 + 8 * (lr & 1))));
-      }
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
+                       (lds_s16x4_t)(kb + voff[dt][hh])));
+      return __builtin_bit_cast(bf16x8, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
+    };
+    __builtin_amdgcn_s_setprio(1);
+    bf16x8 vf = vfrag(0);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8 vn = vfrag(dt + 1 < DT ? dt + 1 : dt);
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
         o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rt], o[dt][rt], 0, 0, 0);
+      if (next && (dt & 1)) lds_dma16(ptr[NI / 2 + (dt >> 1)], nd + (NI / 2 + (dt >> 1)) * 1024);
+      vf = vn;
     }
+    if (next && h == 0) lds_dma4(mask_src + step + NSPLIT, ring_lds + (STG ^ 1) * STAGE_B + 2 * TILE_B);
     __builtin_amdgcn_s_setprio(0);
+  };
+  for (int i = 0; i < iters; i += 2) {
+    step_body(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < iters) step_body(std::integral_constant<int, 1>{}, i + 1);
   }
 
   // Combine the four token splits of each row half: true max, per-split
@@ -878,8 +926,8 @@ static int check_ready(const deft_plan* p, const deft_attn_desc* d) {
   if (!p->uploaded) return fail(DEFT_ERR_INVALID_ARGUMENT, "plan has no device image: call deft_plan_upload");
   if (!same_desc(p->desc, *d))
     return fail(DEFT_ERR_INVALID_ARGUMENT, "desc differs from the desc the plan was uploaded for");
-  if (static_cast<int64_t>(d->num_pages) * kPageSize > INT32_MAX)
-    return fail(DEFT_ERR_UNSUPPORTED, "num_pages * page_size must fit in int32");
+  if (static_cast<int64_t>(d->num_pages) * kPageSize * d->num_kv_heads > INT32_MAX)
+    return fail(DEFT_ERR_UNSUPPORTED, "num_pages * page_size * num_kv_heads must fit in int32");
   return DEFT_OK;
 }
 

@@ -22,12 +22,17 @@ constexpr int kMfmaRows = 64;      // rows per MFMA work item (4 tiles of 16)
 constexpr int kMfmaMinRows = 16;   // a chunk needs this many rows to use MFMA
 constexpr int kValuRows = 16;      // rows per VALU work item
 
-struct WorkItem {                  // matches int4 on the device
+struct WorkItem {                  // two int4 on the device
   int32_t chunk;
   int32_t row_begin;
   int32_t row_count;
+  int32_t chunk_start;             // copies of the chunk's metadata, so a
+  int32_t chunk_len;               // work-group reads one record before it
+  int32_t group_offset;            // can start on the chunk's token rows
+  int32_t full;
   int32_t pad;
 };
+static_assert(sizeof(WorkItem) == 32, "work items are read as two int4");
 
 // Offsets (in 4-byte words) of each array inside the device image.
 struct ImageLayout {

@@ -210,8 +210,10 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
     if (rows == 0) continue;
     const bool use_mfma = d->dtype == DEFT_DTYPE_BF16 && rows >= kMfmaMinRows;
     const int32_t blk = use_mfma ? kMfmaRows : kValuRows;
+    const int32_t cs = p->chunk_start[k], len = p->chunk_start[k + 1] - cs;
     for (int32_t r = 0; r < rows; r += blk)
-      (use_mfma ? mfma : valu).push_back({k, r, std::min(blk, rows - r), 0});
+      (use_mfma ? mfma : valu).push_back({k, r, std::min(blk, rows - r), cs, len, p->group_offsets[k],
+                                          p->chunk_full[k] ? 1 : 0, 0});
   }
   size_t w = 0;
   auto take = [&](size_t n) { size_t at = w; w = align_words(w + n); return at; };
@@ -224,8 +226,8 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   L->flat_to_logical = take(p->total_tokens);
   L->query_slot_offsets = take(p->num_queries + 1);
   L->query_slots = take(S);
-  L->mfma_items = take(4 * mfma.size());
-  L->valu_items = take(4 * valu.size());
+  L->mfma_items = take(8 * mfma.size());
+  L->valu_items = take(8 * valu.size());
   L->total_words = w;
   L->n_mfma = static_cast<int32_t>(mfma.size());
   L->n_valu = static_cast<int32_t>(valu.size());
