@@ -204,6 +204,8 @@ def main():
         r = i % copies
         if what == "both":
             D.deft_tree_attention(qs[r], kc, vc, bts[r], plan, outs[r], desc, workspace)
+        elif what == "fused":
+            D.deft_tree_attention_fused(qs[r], kc, vc, bts[r], plan, outs[r], desc, workspace)
         elif what == "partial":
             D.deft_partial_attention(qs[r], kc, vc, bts[r], plan, desc, part_o, part_m, part_l, fmt)
         else:
@@ -265,6 +267,15 @@ def main():
     _, part_ms = timed(g_part)
     g_merge = capture("merge", 0, args.steps)
     _, merge_ms = timed(g_merge)
+    # single-dispatch variant (last work-group of each row merges it): same
+    # results bit for bit, timed the same way
+    g_fused = capture("fused", 0, args.steps)
+    for o in outs:
+        o.fill_(float("nan"))
+    _, fused_ms = timed(g_fused)
+    for r in range(min(copies, args.steps)):
+        assert torch.equal(outs[r], eager[r]), f"fused variant differs from the two-dispatch path (copy {r})"
+    del g_fused
     # the merge graph leaves outs[] holding merge-only results; restore the reference state
     for i in range(copies):
         step(i)
@@ -339,6 +350,7 @@ def main():
         "step_us_events": ev_ms * 1e3 / args.steps,
         "partial_kernel_us_mean": mean_part,
         "merge_kernel_us_mean": mean_merge,
+        "fused_single_dispatch_step_us": fused_ms * 1e3 / args.steps,
         "warm_step_us": warm_ms * 1e3 / args.steps,
         "planner_host_us_median": float(np.median(plan_times) * 1e6),
         "plan_upload_us": upload_us,

@@ -197,6 +197,23 @@ int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
                         void* stream);
 
 /*
+ * deft_tree_attention in one dispatch per partial kernel (the method's
+ * single-pass variant: partial results are merged where they are produced,
+ * "2. Flattened Tree KV Splitting" / "The Online Softmax Tile Accumulation").
+ * Every work-group, after writing its partials, takes a device-scope
+ * acquire-release ticket for each (query, head) row it wrote; the one that
+ * takes a row's last ticket merges that row and writes `out`, then resets the
+ * ticket.  The tickets live in the plan's device image (zero after upload and
+ * after every completed call), so calls that share a plan must not overlap
+ * and the plan is not const here.  Arguments, layouts, workspace and errors
+ * as for deft_tree_attention; results are bitwise equal to it.
+ */
+int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, deft_plan* plan, void* out,
+                              const deft_attn_desc* desc, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * The partial-attention kernel on its own ("The Online Softmax Tile
  * Accumulation" applied per chunk).  For every slot s (chunk c, query q) and
  * query head h, over the chunk's tokens visible to q:

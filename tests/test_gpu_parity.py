@@ -188,6 +188,40 @@ def test_deterministic_and_writes_every_slot():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_two_kernel_and_fused_paths_match(cfg):
+    """deft_partial_attention + deft_lse_merge (two dispatches) against the
+    oracle, against deft_tree_attention_fused (the partial kernels merge each
+    (query, head) row in the same dispatch; three calls on one plan, so its
+    tickets must come back to zero after every call) and deft_tree_attention."""
+    wl = W.standard_workload(cfg)
+    say("two-kernel path", cfg)
+    q, kc, vc, bt = inputs = gpu_inputs(wl)
+    desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    from tree_structured_decode_amd.runner import TreeAttention
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens, desc, device=DEV)
+    bf16 = wl.dtype == torch.bfloat16
+    fmt = D.DEFT_PARTIAL_BF16_NORM if bf16 else D.DEFT_PARTIAL_F32
+    po, pm, pl = ta.partials(q, kc, vc, bt, partial_format=fmt)
+    out2 = torch.full_like(q, float("nan"))
+    D.deft_lse_merge(ta.plan, desc, po, pm, pl, out2, fmt)
+    fused = []
+    for _ in range(3):
+        o = torch.full_like(q, float("nan"))
+        D.deft_tree_attention_fused(q, kc, vc, bt, ta.plan, o, desc, ta.workspace)
+        fused.append(o)
+    o = torch.full_like(q, float("nan"))
+    ta(q, kc, vc, bt, o)
+    fused.append(o)
+    torch.cuda.synchronize()
+    got2 = out2.double().cpu().numpy()
+    want = oracle_out(wl)
+    check_close(got2, want, TOL[wl.dtype], "two-kernel path")
+    for o in fused:
+        # same partials, same merge arithmetic: identical bits
+        assert torch.equal(o, out2)
+
+
 def test_single_node_single_query_and_duplicates():
     for parents, seg, qn in [([-1], [1], [0]), ([-1], [17], [0, 0, 0]), ([-1, 0, 0], [5, 1, 1], [0, 1, 2, 1])]:
         for dtype in (torch.float32, torch.bfloat16):

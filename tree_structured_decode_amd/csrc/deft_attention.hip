@@ -67,7 +67,20 @@ struct DevPlan {
   const int32_t* query_slots;
   const int4* mfma_items;
   const int4* valu_items;
+  int32_t* tickets;          // [Nq * Hq], zero between calls (fused merge)
   int32_t n_mfma, n_valu, mask_words, num_queries;
+};
+
+// Operands of the per-(query, head) merge (the merge kernel and the fused
+// tail of the partial kernels).
+struct MergeArgs {
+  const float* po;
+  const float* pm;
+  const float* pl;
+  void* out;
+  const int32_t* query_slot_offsets;
+  const int32_t* query_slots;
+  int32_t nq, hq, po_bf16;
 };
 
 struct PartialArgs {
@@ -82,6 +95,8 @@ struct PartialArgs {
   int32_t hq, hkv, grp;
   int32_t po_bf16;   // 1: store O / l rounded to bf16 (internal workspace format)
   float scale_log2;  // log2(e) / sqrt(d)
+  int32_t fused;     // 1: merge completed rows in this dispatch (fused_merge_tail)
+  MergeArgs merge;   // used when fused
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -159,6 +174,197 @@ __device__ inline void stage_token_rows(int32_t* tok_row, const DevPlan& P, cons
   else if (nk <= 4) stage_token_rows_n<RPI, NT, 4>(tok_row, P, bt, cs, len, mul, add);
   else if (nk <= 8) stage_token_rows_n<RPI, NT, 8>(tok_row, P, bt, cs, len, mul, add);
   else stage_token_rows_n<RPI, NT, 16>(tok_row, P, bt, cs, len, mul, add);
+}
+
+// ---------------------------------------------------------------------------
+// Merge kernel: one wave per (query, query head).  Lane i of the wave reads
+// the metadata (slot id, m, l) of the query's i-th slot, so a query's whole
+// slot list costs one round of dependent loads; the partial O rows are then
+// read by four 16-lane groups, group g taking slots g, g + 4, ..., each lane
+// D/16 consecutive elements.  With M = max_s m_s and w_s = exp(m_s - M):
+//   fp32 unnormalised partials   out = sum_s w_s O_s / sum_s w_s l_s
+//   bf16 partials holding O_s/l_s out = sum_s w_s l_s (O_s/l_s) / sum_s w_s l_s
+// Queries with more than 64 slots take several rounds, rescaled online.
+// ---------------------------------------------------------------------------
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) x = fmaxf(x, __shfl_xor(x, k));
+  return x;
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) x += __shfl_xor(x, k);
+  return x;
+}
+
+// EPL consecutive elements of one partial O row (slot-head sh), as fp32.
+template <int D, int EPL>
+__device__ inline void load_partial_row(const MergeArgs& a, int64_t sh, int sub, float* v) {
+  if (a.po_bf16) {
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.po) + sh * D + sub * EPL;
+    if constexpr (EPL == 8) {
+      Elem<uint16_t>::unpack(*reinterpret_cast<const u32x4*>(src), v);
+    } else {
+      const u32x2 r = *reinterpret_cast<const u32x2*>(src);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        v[2 * e] = __uint_as_float(r[e] << 16);
+        v[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float* src = a.po + sh * D + sub * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const f32x4 r = *reinterpret_cast<const f32x4*>(src + e);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[e + k] = r[k];
+    }
+  }
+}
+
+// Merge of one (query qi, query head h) by one whole wave.
+template <typename T, int D>
+__device__ void merge_query_head(const MergeArgs& a, int qi, int h) {
+  constexpr int EPL = D / 16;      // elements per lane
+  constexpr int KU = 4;            // slots per group read before any is accumulated
+  constexpr int PER_G = EPL / 4;   // output elements each lane stores
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, sub = lane & 15;
+  const int s0 = a.query_slot_offsets[qi], s1 = a.query_slot_offsets[qi + 1];
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float mrun = kNegInf, wsum = 0.f;
+  for (int i0 = s0; i0 < s1; i0 += 64) {
+    const int n = min(64, s1 - i0);
+    // lanes past the list re-read its first slot and get weight 0
+    const int slot = a.query_slots[i0 + (lane < n ? lane : 0)];
+    const int64_t sh = static_cast<int64_t>(slot) * a.hq + h;
+    const float mv = lane < n ? a.pm[sh] : kNegInf;
+    const float lv = lane < n ? a.pl[sh] : 0.f;
+    // first KU slots of each group, issued before the reductions
+    float vals[KU][EPL];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int j = grp + 4 * u;
+      const int sj = __shfl(slot, j < n ? j : 0);
+      load_partial_row<D, EPL>(a, static_cast<int64_t>(sj) * a.hq + h, sub, vals[u]);
+    }
+    const float mnew = fmaxf(mrun, wave_max(mv));
+    const float w = mv == kNegInf ? 0.f : __expf(mv - mnew);
+    const float wl = w * lv;
+    const float wt = a.po_bf16 ? wl : w;      // weight of the stored O row
+    const float rescale = mrun == kNegInf ? 0.f : __expf(mrun - mnew);
+    mrun = mnew;
+    wsum = wsum * rescale + wave_sum(wl);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= rescale;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int j = grp + 4 * u;
+      const float wj = __shfl(wt, j < n ? j : 63);
+      const float wu = j < n ? wj : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wu, vals[u][e], acc[e]);
+    }
+    for (int j0 = 4 * KU; j0 < n; j0 += 4) {
+      const int j = j0 + grp;
+      const int sj = __shfl(slot, j < n ? j : 0);
+      const float wj = __shfl(wt, j < n ? j : 63);
+      float v[EPL];
+      load_partial_row<D, EPL>(a, static_cast<int64_t>(sj) * a.hq + h, sub, v);
+      const float wu = j < n ? wj : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wu, v[e], acc[e]);
+    }
+  }
+  // sum the four groups; every group then holds the full row
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    acc[e] += __shfl_xor(acc[e], 16);
+    acc[e] += __shfl_xor(acc[e], 32);
+  }
+  const float inv = 1.f / wsum;
+  // group g stores elements [g * PER_G, (g + 1) * PER_G) of each lane's EPL
+  float x[PER_G];
+#pragma unroll
+  for (int k = 0; k < PER_G; ++k) {
+    x[k] = acc[k];
+#pragma unroll
+    for (int g = 1; g < 4; ++g) x[k] = grp == g ? acc[g * PER_G + k] : x[k];
+    x[k] *= inv;
+  }
+  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + sub * EPL + grp * PER_G;
+  if constexpr (sizeof(T) == 2 && PER_G == 2) {
+    const uint32_t pk = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + ob) = pk;
+  } else {
+#pragma unroll
+    for (int k = 0; k < PER_G; ++k) Elem<T>::store(a.out, ob + k, x[k]);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.nq * a.hq) return;           // whole waves leave together
+  merge_query_head<T, D>(a, pair / a.hq, pair % a.hq);
+}
+
+// ---------------------------------------------------------------------------
+// Fused merge (one dispatch for the whole step).  After its partial stores a
+// work-group takes one ticket per (query, query head) row it wrote; the
+// work-group that takes a row's last ticket (every slot of that query has
+// then written its partial) merges the row itself, through the same
+// per-(query, head) merge as the merge kernel, and resets the ticket to zero
+// for the next call.  Tickets are acquire-release atomics at device scope:
+// the release publishes the work-group's partials to the other L2s, the
+// acquire makes the merging work-group read everyone's.  Calls that share a
+// plan (and so its tickets) must not overlap.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__device__ void fused_merge_tail(const MergeArgs& m, const DevPlan& P, int32_t* tickets, int grp,
+                                 int32_t rb, int32_t nr, int32_t gofs, int g, int32_t* last_list,
+                                 int32_t* n_last) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nwave = blockDim.x >> 6;
+  // every wave's partial stores have completed before any ticket is taken
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int r0 = w * 64; r0 < nr; r0 += nwave * 64) {
+    int32_t code = -1;
+    const int r = r0 + lane;
+    if (r < nr) {
+      const int row = rb + r;
+      const int qi = P.slot_query[gofs + row / grp];
+      const int head = g * grp + row % grp;
+      const int need = P.query_slot_offsets[qi + 1] - P.query_slot_offsets[qi];
+      int32_t* t = tickets + static_cast<size_t>(qi) * m.hq + head;
+      const int old = __hip_atomic_fetch_add(t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == need - 1) {
+        __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        code = qi * m.hq + head;
+      }
+    }
+    const uint64_t bal = __ballot(code >= 0);
+    const int pos = __popcll(bal & ((1ull << lane) - 1ull));
+    // rows are taken in blocks of 64 by one wave each, so list slots never collide
+    if (code >= 0) last_list[r0 + pos] = code;
+    if (lane == 0) n_last[r0 / 64] = __popcll(bal);
+  }
+  __syncthreads();
+  // merge the rows this work-group completed, one wave per row
+  const int nblk = (nr + 63) / 64;
+  for (int b = 0; b < nblk; ++b) {
+    const int cnt = n_last[b];
+    for (int k = w; k < cnt; k += nwave) {
+      const int code = last_list[b * 64 + k];
+      merge_query_head<T, D>(m, code / m.hq, code % m.hq);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -324,6 +530,11 @@ __global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
       a.pm[sh] = mx == kNegInf ? kNegInf : mx * kLn2;
       a.pl[sh] = lsum;
     }
+  }
+  if (a.fused) {
+    __shared__ int32_t last_list[kValuRows];
+    __shared__ int32_t n_last[1];
+    fused_merge_tail<T, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, n_last);
   }
 }
 
@@ -740,147 +951,10 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
       *reinterpret_cast<f32x4*>(a.po + at) = acc;
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Merge kernel: one wave per (query, query head).  Lane i of the wave reads
-// the metadata (slot id, m, l) of the query's i-th slot, so a query's whole
-// slot list costs one round of dependent loads; the partial O rows are then
-// read by four 16-lane groups, group g taking slots g, g + 4, ..., each lane
-// D/16 consecutive elements.  With M = max_s m_s and w_s = exp(m_s - M):
-//   fp32 unnormalised partials   out = sum_s w_s O_s / sum_s w_s l_s
-//   bf16 partials holding O_s/l_s out = sum_s w_s l_s (O_s/l_s) / sum_s w_s l_s
-// Queries with more than 64 slots take several rounds, rescaled online.
-// ---------------------------------------------------------------------------
-struct MergeArgs {
-  const float* po;
-  const float* pm;
-  const float* pl;
-  void* out;
-  const int32_t* query_slot_offsets;
-  const int32_t* query_slots;
-  int32_t nq, hq, po_bf16;
-};
-
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) x = fmaxf(x, __shfl_xor(x, k));
-  return x;
-}
-
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) x += __shfl_xor(x, k);
-  return x;
-}
-
-// EPL consecutive elements of one partial O row (slot-head sh), as fp32.
-template <int D, int EPL>
-__device__ inline void load_partial_row(const MergeArgs& a, int64_t sh, int sub, float* v) {
-  if (a.po_bf16) {
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.po) + sh * D + sub * EPL;
-    if constexpr (EPL == 8) {
-      Elem<uint16_t>::unpack(*reinterpret_cast<const u32x4*>(src), v);
-    } else {
-      const u32x2 r = *reinterpret_cast<const u32x2*>(src);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        v[2 * e] = __uint_as_float(r[e] << 16);
-        v[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
-      }
-    }
-  } else {
-    const float* src = a.po + sh * D + sub * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; e += 4) {
-      const f32x4 r = *reinterpret_cast<const f32x4*>(src + e);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) v[e + k] = r[k];
-    }
-  }
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
-  constexpr int EPL = D / 16;      // elements per lane
-  constexpr int KU = 4;            // slots per group read before any is accumulated
-  constexpr int PER_G = EPL / 4;   // output elements each lane stores
-  const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= a.nq * a.hq) return;           // whole waves leave together
-  const int qi = pair / a.hq, h = pair % a.hq;
-  const int grp = lane >> 4, sub = lane & 15;
-  const int s0 = a.query_slot_offsets[qi], s1 = a.query_slot_offsets[qi + 1];
-  float acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  float mrun = kNegInf, wsum = 0.f;
-  for (int i0 = s0; i0 < s1; i0 += 64) {
-    const int n = min(64, s1 - i0);
-    // lanes past the list re-read its first slot and get weight 0
-    const int slot = a.query_slots[i0 + (lane < n ? lane : 0)];
-    const int64_t sh = static_cast<int64_t>(slot) * a.hq + h;
-    const float mv = lane < n ? a.pm[sh] : kNegInf;
-    const float lv = lane < n ? a.pl[sh] : 0.f;
-    // first KU slots of each group, issued before the reductions
-    float vals[KU][EPL];
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int j = grp + 4 * u;
-      const int sj = __shfl(slot, j < n ? j : 0);
-      load_partial_row<D, EPL>(a, static_cast<int64_t>(sj) * a.hq + h, sub, vals[u]);
-    }
-    const float mnew = fmaxf(mrun, wave_max(mv));
-    const float w = mv == kNegInf ? 0.f : __expf(mv - mnew);
-    const float wl = w * lv;
-    const float wt = a.po_bf16 ? wl : w;      // weight of the stored O row
-    const float rescale = mrun == kNegInf ? 0.f : __expf(mrun - mnew);
-    mrun = mnew;
-    wsum = wsum * rescale + wave_sum(wl);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] *= rescale;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int j = grp + 4 * u;
-      const float wj = __shfl(wt, j < n ? j : 63);
-      const float wu = j < n ? wj : 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wu, vals[u][e], acc[e]);
-    }
-    for (int j0 = 4 * KU; j0 < n; j0 += 4) {
-      const int j = j0 + grp;
-      const int sj = __shfl(slot, j < n ? j : 0);
-      const float wj = __shfl(wt, j < n ? j : 63);
-      float v[EPL];
-      load_partial_row<D, EPL>(a, static_cast<int64_t>(sj) * a.hq + h, sub, v);
-      const float wu = j < n ? wj : 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wu, v[e], acc[e]);
-    }
-  }
-  // sum the four groups; every group then holds the full row
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    acc[e] += __shfl_xor(acc[e], 16);
-    acc[e] += __shfl_xor(acc[e], 32);
-  }
-  const float inv = 1.f / wsum;
-  // group g stores elements [g * PER_G, (g + 1) * PER_G) of each lane's EPL
-  float x[PER_G];
-#pragma unroll
-  for (int k = 0; k < PER_G; ++k) {
-    x[k] = acc[k];
-#pragma unroll
-    for (int g = 1; g < 4; ++g) x[k] = grp == g ? acc[g * PER_G + k] : x[k];
-    x[k] *= inv;
-  }
-  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + sub * EPL + grp * PER_G;
-  if constexpr (sizeof(T) == 2 && PER_G == 2) {
-    const uint32_t pk = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + ob) = pk;
-  } else {
-#pragma unroll
-    for (int k = 0; k < PER_G; ++k) Elem<T>::store(a.out, ob + k, x[k]);
+  if (a.fused) {
+    __shared__ int32_t last_list[kMfmaRows];
+    __shared__ int32_t n_last[1];
+    fused_merge_tail<uint16_t, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, n_last);
   }
 }
 
@@ -902,6 +976,7 @@ static DevPlan make_dev_plan(const deft_plan* p) {
   d.query_slots = b + L.query_slots;
   d.mfma_items = reinterpret_cast<const int4*>(b + L.mfma_items);
   d.valu_items = reinterpret_cast<const int4*>(b + L.valu_items);
+  d.tickets = const_cast<int32_t*>(b) + L.tickets;
   d.n_mfma = L.n_mfma;
   d.n_valu = L.n_valu;
   d.mask_words = p->mask_words;
@@ -953,7 +1028,7 @@ static int launch_partials(const PartialArgs& pa, hipStream_t st) {
 
 static int run_partials(const void* q, const void* k, const void* v, const int32_t* bt,
                         const deft_plan* p, const deft_attn_desc* d, float* po, float* pm,
-                        float* pl, bool po_bf16, hipStream_t st) {
+                        float* pl, bool po_bf16, hipStream_t st, void* fused_out = nullptr) {
   if (!q || !k || !v || !bt || !po || !pm || !pl)
     return fail(DEFT_ERR_INVALID_ARGUMENT, "device pointers must not be NULL");
   PartialArgs pa;
@@ -970,6 +1045,16 @@ static int run_partials(const void* q, const void* k, const void* v, const int32
   pa.grp = d->num_q_heads / d->num_kv_heads;
   pa.po_bf16 = po_bf16 ? 1 : 0;
   pa.scale_log2 = kLog2e / std::sqrt(static_cast<float>(d->head_dim));
+  pa.fused = fused_out != nullptr;
+  pa.merge.po = po;
+  pa.merge.pm = pm;
+  pa.merge.pl = pl;
+  pa.merge.out = fused_out;
+  pa.merge.query_slot_offsets = pa.plan.query_slot_offsets;
+  pa.merge.query_slots = pa.plan.query_slots;
+  pa.merge.nq = p->num_queries;
+  pa.merge.hq = d->num_q_heads;
+  pa.merge.po_bf16 = pa.po_bf16;
   if (d->dtype == DEFT_DTYPE_BF16)
     return d->head_dim == 128 ? launch_partials<uint16_t, 128>(pa, st) : launch_partials<uint16_t, 64>(pa, st);
   return d->head_dim == 128 ? launch_partials<float, 128>(pa, st) : launch_partials<float, 64>(pa, st);
@@ -1079,6 +1164,29 @@ int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
   rc = deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, po, pm, pl, po_bf16, st);
   if (rc) return rc;
   return deft::run_merge(plan, desc, po, pm, pl, out, po_bf16, st);
+}
+
+int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, deft_plan* plan, void* out,
+                              const deft_attn_desc* desc, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  int rc = deft::check_ready(plan, desc);
+  if (rc) return rc;
+  if (!workspace || !out) return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace and out must not be NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  const size_t need = deft::workspace_bytes_for(plan, desc);
+  if (workspace_bytes < need) return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace too small");
+  const bool po_bf16 = desc->dtype == DEFT_DTYPE_BF16;
+  const size_t sh = static_cast<size_t>(plan->num_slots) * desc->num_q_heads;
+  auto align = [](size_t n) { return (n + 63) & ~static_cast<size_t>(63); };
+  float* po = static_cast<float*>(workspace);
+  float* pm = po + align(deft::partial_o_words(plan, desc));
+  float* pl = pm + align(sh);
+  // One dispatch per partial kernel: the last work-group to finish a
+  // (query, head) row merges it (fused_merge_tail).
+  return deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, po, pm, pl, po_bf16,
+                            static_cast<hipStream_t>(stream), out);
 }
 
 }  // extern "C"

@@ -37,7 +37,7 @@ static_assert(sizeof(WorkItem) == 32, "work items are read as two int4");
 // Offsets (in 4-byte words) of each array inside the device image.
 struct ImageLayout {
   size_t chunk_start, group_offsets, chunk_full, slot_query, slot_mask, flat_to_logical,
-      query_slot_offsets, query_slots, mfma_items, valu_items, total_words;
+      query_slot_offsets, query_slots, mfma_items, valu_items, tickets, total_words;
   int32_t n_mfma, n_valu;
 };
 

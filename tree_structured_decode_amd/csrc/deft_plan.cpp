@@ -228,6 +228,9 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   L->query_slots = take(S);
   L->mfma_items = take(8 * mfma.size());
   L->valu_items = take(8 * valu.size());
+  // fused-merge tickets, one per (query, query head); zero in the uploaded
+  // image and reset to zero by the kernels after use
+  L->tickets = take(static_cast<size_t>(p->num_queries) * d->num_q_heads);
   L->total_words = w;
   L->n_mfma = static_cast<int32_t>(mfma.size());
   L->n_valu = static_cast<int32_t>(valu.size());

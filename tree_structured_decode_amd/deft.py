@@ -33,8 +33,8 @@ DEFT_PARTIAL_BF16_NORM = 1
 
 EXPORTED_SYMBOLS = (
     "deft_plan_create", "deft_plan_destroy", "deft_plan_export", "deft_plan_device_bytes",
-    "deft_plan_upload", "deft_tree_attention", "deft_partial_attention", "deft_lse_merge",
-    "deft_last_error",
+    "deft_plan_upload", "deft_tree_attention", "deft_tree_attention_fused", "deft_partial_attention",
+    "deft_lse_merge", "deft_last_error",
 )
 
 _P = ctypes.c_void_p
@@ -85,13 +85,15 @@ def lib() -> ctypes.CDLL:
     L.deft_plan_upload.argtypes = [_P, ctypes.POINTER(deft_attn_desc), _P, ctypes.c_size_t, _P]
     L.deft_tree_attention.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.POINTER(deft_attn_desc),
                                       _P, ctypes.c_size_t, _P]
+    L.deft_tree_attention_fused.argtypes = L.deft_tree_attention.argtypes
     L.deft_partial_attention.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(deft_attn_desc),
                                          _P, _P, _P, ctypes.c_int32, _P]
     L.deft_lse_merge.argtypes = [_P, ctypes.POINTER(deft_attn_desc), _P, _P, _P, ctypes.c_int32,
                                  _P, _P]
     L.deft_last_error.restype = ctypes.c_char_p
     for name in ("deft_plan_create", "deft_plan_export", "deft_plan_device_bytes", "deft_plan_upload",
-                 "deft_tree_attention", "deft_partial_attention", "deft_lse_merge"):
+                 "deft_tree_attention", "deft_tree_attention_fused", "deft_partial_attention",
+                 "deft_lse_merge"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -204,6 +206,13 @@ def deft_tree_attention(q, k_cache, v_cache, block_table, plan: Plan, out, desc,
     _check(lib().deft_tree_attention(_dev(q), _dev(k_cache), _dev(v_cache), _dev(block_table),
                                      plan.handle, _dev(out), ctypes.byref(desc), _dev(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def deft_tree_attention_fused(q, k_cache, v_cache, block_table, plan: Plan, out, desc, workspace,
+                              stream=None):
+    _check(lib().deft_tree_attention_fused(_dev(q), _dev(k_cache), _dev(v_cache), _dev(block_table),
+                                           plan.handle, _dev(out), ctypes.byref(desc), _dev(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def deft_partial_attention(q, k_cache, v_cache, block_table, plan: Plan, desc, part_o, part_m,
