@@ -95,7 +95,7 @@ struct PartialArgs {
   int32_t hq, hkv, grp;
   int32_t po_bf16;   // 1: store O / l rounded to bf16 (internal workspace format)
   float scale_log2;  // log2(e) / sqrt(d)
-  int32_t fused;     // 1: merge completed rows in this dispatch (fused_merge_tail)
+  int32_t fused;     // 1: launch the kernels' fused variants (fused_merge_tail)
   MergeArgs merge;   // used when fused
 };
 
@@ -374,7 +374,7 @@ __device__ void fused_merge_tail(const MergeArgs& m, const DevPlan& P, int32_t* 
 // Each lane group keeps its own online-softmax state; groups and waves are
 // merged at the end.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool FUSED>
 __global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
   constexpr int EPL = Elem<T>::kPerLoad;
   constexpr int LPT = D / EPL;
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
       a.pl[sh] = lsum;
     }
   }
-  if (a.fused) {
+  if constexpr (FUSED) {
     __shared__ int32_t last_list[kValuRows];
     __shared__ int32_t n_last[1];
     fused_merge_tail<T, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, n_last);
@@ -603,7 +603,7 @@ __device__ inline void pair_sync(int32_t* mine, int32_t* theirs, int32_t i, int 
   }
 }
 
-template <int D>
+template <int D, bool FUSED>
 __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   constexpr int NWAVE = 8;
   constexpr int NSPLIT = 4;
@@ -951,7 +951,7 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
       *reinterpret_cast<f32x4*>(a.po + at) = acc;
     }
   }
-  if (a.fused) {
+  if constexpr (FUSED) {
     __shared__ int32_t last_list[kMfmaRows];
     __shared__ int32_t n_last[1];
     fused_merge_tail<uint16_t, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, n_last);
@@ -1011,7 +1011,8 @@ static int launch_partials(const PartialArgs& pa, hipStream_t st) {
   const int hkv = pa.hkv;
   if (pa.plan.n_mfma > 0) {
     if constexpr (sizeof(T) == 2) {
-      hipLaunchKernelGGL(mfma_partial<D>, dim3(pa.plan.n_mfma * hkv), dim3(512), 0, st, pa);
+      if (pa.fused) hipLaunchKernelGGL((mfma_partial<D, true>), dim3(pa.plan.n_mfma * hkv), dim3(512), 0, st, pa);
+      else hipLaunchKernelGGL((mfma_partial<D, false>), dim3(pa.plan.n_mfma * hkv), dim3(512), 0, st, pa);
       int rc = hip_check(hipGetLastError(), "launch of mfma_partial");
       if (rc) return rc;
     } else {
@@ -1019,7 +1020,8 @@ static int launch_partials(const PartialArgs& pa, hipStream_t st) {
     }
   }
   if (pa.plan.n_valu > 0) {
-    hipLaunchKernelGGL((valu_partial<T, D>), dim3(pa.plan.n_valu * hkv), dim3(256), 0, st, pa);
+    if (pa.fused) hipLaunchKernelGGL((valu_partial<T, D, true>), dim3(pa.plan.n_valu * hkv), dim3(256), 0, st, pa);
+    else hipLaunchKernelGGL((valu_partial<T, D, false>), dim3(pa.plan.n_valu * hkv), dim3(256), 0, st, pa);
     int rc = hip_check(hipGetLastError(), "launch of valu_partial");
     if (rc) return rc;
   }
