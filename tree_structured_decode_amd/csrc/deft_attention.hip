@@ -96,10 +96,44 @@ struct PartialArgs {
   int32_t po_bf16;   // 1: store O / l rounded to bf16 (internal workspace format)
   float scale_log2;  // log2(e) / sqrt(d)
   int32_t fused;     // 1: launch the kernels' fused variants (fused_merge_tail)
+  int32_t max_valu_rows;   // host only: picks the VALU kernel's row capacity
   MergeArgs merge;   // used when fused
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum over aligned groups of N lanes (N = 4, 8, 16 or 32), every lane of a
+// group receiving the group's sum, with DPP lane moves on the VALU (no LDS
+// crossbar): swaps within quads, then mirrors within half-rows and rows of
+// 16 lanes (after the previous steps every lane of a subgroup holds the same
+// partial sum, so a mirror pairs each subgroup with its neighbour), then a
+// swap of adjacent 16-lane rows.
+template <int N>
+__device__ inline float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+  x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  if constexpr (N >= 16) x += dpp(x, std::integral_constant<int, 0x140>{});  // row_mirror
+  if constexpr (N >= 32) {
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  }
+  return x;
+}
+
+// s + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs, fp32 accumulate.
+// Written as inline asm: built from register words through the fdot2 builtin
+// and bit casts, the compiler fed one register to every call of an unrolled
+// sequence.  The compiler cannot see the asm's VGPR write, so the asm itself
+// provides the two wait states a following DPP read of the result needs.
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float s) {
+  asm("v_dot2c_f32_bf16 %0, %1, %2\n\ts_nop 1" : "+v"(s) : "v"(a), "v"(b));
+  return s;
+}
 
 __device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 
@@ -368,19 +402,26 @@ __device__ void fused_merge_tail(const MergeArgs& m, const DevPlan& P, int32_t* 
 }
 
 // ---------------------------------------------------------------------------
-// VALU partial kernel: up to 16 rows per work-group.  Lanes are grouped LPT
-// per token (each lane holds 16 bytes of the token's K and V row); a wave
-// covers TPW tokens per step and the 4 waves interleave over the chunk.
-// Each lane group keeps its own online-softmax state; groups and waves are
-// merged at the end.
+// VALU partial kernel: groups below one MFMA tile (and fp32 inputs), up to R
+// rows per work-group (R = 4, 8 or 16, the smallest that holds the plan's
+// largest such group).  The work is a stream over the chunk's KV rows with
+// little arithmetic per byte, so the kernel keeps many loads in flight: lanes
+// are grouped LPT per token (each lane holds EPL elements of the token's K
+// and V row), a wave covers TPW tokens per step, the 4 waves interleave over
+// the chunk, and each lane keeps PF steps of K and V loads outstanding in
+// registers.  Each lane group keeps its own online-softmax state (running
+// max raised lazily, as in the MFMA kernel); groups and waves are merged at
+// the end.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool FUSED>
+template <typename T, int D, int R, bool FUSED>
 __global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
   constexpr int EPL = Elem<T>::kPerLoad;
   constexpr int LPT = D / EPL;
   constexpr int TPW = 64 / LPT;
   constexpr int NW = 4;
-  constexpr int R = kValuRows;
+  constexpr int STRIDE = NW * TPW;                      // tokens per work-group step
+  constexpr int PF = R <= 4 ? 8 : (R <= 8 ? 4 : 2);     // steps of loads in flight per lane
+  static_assert(R <= kValuRows, "row capacity");
   __shared__ int32_t tok_row[kMaxChunkTokens];
   __shared__ uint32_t masks[R * (kMaxChunkTokens / 32)];
   __shared__ float red[NW][R][D + 2];
@@ -395,100 +436,120 @@ __global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
   const int W = P.mask_words;
   const int j0 = rb / a.grp;
   const int nslot = (rb + nr - 1) / a.grp - j0 + 1;
-
-  stage_token_rows<0, 256>(tok_row, P, a.block_table, cs, len);
-  if (!full)
-    for (int i = threadIdx.x; i < nslot * W; i += blockDim.x)
-      masks[i] = P.slot_mask[static_cast<size_t>(gofs + j0) * W + i];
-
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tg = lane / LPT, li = lane % LPT;
   constexpr int EB = sizeof(T);
 
-  float qv[R][EPL];
+  // queries of the rows, looked up before the token rows are staged
+  int32_t qrow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r < nr) {
-      const int row = rb + r;
-      const int32_t qi = P.slot_query[gofs + row / a.grp];
-      const int head = g * a.grp + row % a.grp;
-      float tmp[EPL];
-      Elem<T>::unpack(load16(a.q, (static_cast<int64_t>(qi) * a.hq + head) * D + li * EPL, EB), tmp);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qv[r][e] = tmp[e] * a.scale_log2;
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qv[r][e] = 0.f;
-    }
+    const int row = rb + min(r, nr - 1);
+    qrow[r] = P.slot_query[gofs + row / a.grp];
   }
+  // token rows are stored as rows of this KV head: pool row * Hkv + g
+  stage_token_rows<0, 256>(tok_row, P, a.block_table, cs, len, a.hkv, g);
+  if (!full)
+    for (int i = threadIdx.x; i < nslot * W; i += blockDim.x)
+      masks[i] = P.slot_mask[static_cast<size_t>(gofs + j0) * W + i];
+
+  // Q rows: bf16 kept packed (scores by bf16 dot2 with fp32 accumulation),
+  // fp32 as is; scores are scaled by scale * log2(e) into log2 units.
+  constexpr int QW = sizeof(T) == 2 ? EPL / 2 : EPL;   // 32-bit words of Q per lane and row
+  uint32_t qv[R][QW];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = rb + min(r, nr - 1);
+    const int head = g * a.grp + row % a.grp;
+    const u32x4 raw = load16(a.q, (static_cast<int64_t>(qrow[r]) * a.hq + head) * D + li * EPL, EB);
+#pragma unroll
+    for (int e = 0; e < QW; ++e) qv[r][e] = raw[e];
+  }
+  const float qscale = a.scale_log2;
   __syncthreads();
 
-  float m[R], l[R], o[R][EPL];
+  float m_run[R], m_true[R], l[R], o[R][EPL];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    m[r] = kNegInf;
+    m_run[r] = kNegInf;
+    m_true[r] = kNegInf;
     l[r] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[r][e] = 0.f;
   }
 
-  const int64_t head_off = static_cast<int64_t>(g) * D + li * EPL;
-  auto fetch = [&](int t, u32x4& kr, u32x4& vr) {
-    if (t < len) {
-      const int64_t off = static_cast<int64_t>(tok_row[t]) * a.hkv * D + head_off;
-      kr = load16(a.k, off, EB);
-      vr = load16(a.v, off, EB);
-    } else {
-      kr = u32x4{0, 0, 0, 0};
-      vr = u32x4{0, 0, 0, 0};
-    }
+  // K and V of one token for this lane (every load reads a valid row: tokens
+  // past the chunk end re-read its last token and are masked).
+  const char* kbase = static_cast<const char*>(a.k) + li * EPL * EB;
+  const char* vbase = static_cast<const char*>(a.v) + li * EPL * EB;
+  auto fetch = [&](int step, u32x4& kr, u32x4& vr) {
+    const int t = min(step * STRIDE + w * TPW + tg, len - 1);
+    const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(tok_row[t])) * (D * EB);
+    kr = *reinterpret_cast<const u32x4*>(kbase + off);
+    vr = *reinterpret_cast<const u32x4*>(vbase + off);
   };
-
-  constexpr int STRIDE = NW * TPW;
-  int t = w * TPW + tg;
-  u32x4 kr, vr, kn, vn;
-  fetch(t, kr, vr);
-  for (int base = 0; base < len; base += STRIDE, t += STRIDE) {
-    fetch(t + STRIDE, kn, vn);
+  auto process = [&](const u32x4& kr, const u32x4& vr, int step) {
+    const int t = step * STRIDE + w * TPW + tg;
     float kf[EPL], vf[EPL];
-    Elem<T>::unpack(kr, kf);
+    if constexpr (sizeof(T) != 2) Elem<T>::unpack(kr, kf);
     Elem<T>::unpack(vr, vf);
     const bool valid = t < len;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (r >= nr) continue;
       float s = 0.f;
+      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s = fmaf(qv[r][e], kf[e], s);
+        for (int e = 0; e < QW; ++e) s = dot2_bf16(kr[e], qv[r][e], s);
+      } else {
 #pragma unroll
-      for (int x = LPT / 2; x >= 1; x >>= 1) s += __shfl_xor(s, x);
+        for (int e = 0; e < EPL; ++e) s = fmaf(__uint_as_float(qv[r][e]), kf[e], s);
+      }
+      s = group_sum<LPT>(s) * qscale;
       bool vis = valid;
       if (!full && valid) {
         const int j = (rb + r) / a.grp - j0;
         vis = (masks[j * W + (t >> 5)] >> (t & 31)) & 1u;
       }
-      if (vis) {
-        const float mn = fmaxf(m[r], s);
-        const float alpha = exp2f(m[r] - mn);  // m = -inf gives 0
-        const float p = exp2f(s - mn);
-        l[r] = l[r] * alpha + p;
+      const float z = vis ? s : kNegInf;
+      m_true[r] = fmaxf(m_true[r], z);
+      // the running max rises only when a score exceeds it by the slack
+      const bool raise = z > m_run[r] + kRescaleSlack || (m_run[r] == kNegInf && z != kNegInf);
+      if (__any(raise)) {
+        const float mn = raise ? z : m_run[r];
+        const float alpha = raise ? exp2f(m_run[r] - mn) : 1.f;   // m = -inf gives 0
+        m_run[r] = mn;
+        l[r] *= alpha;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e] * alpha);
-        m[r] = mn;
+        for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
       }
+      const float p = m_run[r] == kNegInf ? 0.f : fast_exp2(z - m_run[r]);   // z = -inf gives 0
+      l[r] += p;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
     }
-    kr = kn;
-    vr = vn;
+  };
+
+  const int nsteps = (len + STRIDE - 1) / STRIDE;
+  u32x4 kb[PF], vb[PF];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) fetch(p, kb[p], vb[p]);
+  for (int s0 = 0; s0 < nsteps; s0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      if (s0 + p < nsteps) process(kb[p], vb[p], s0 + p);
+      fetch(s0 + p + PF, kb[p], vb[p]);   // loads are issued unconditionally, in a fixed order
+    }
   }
 
-  // Merge the lane groups of this wave, then the waves.
+  // Merge the lane groups of this wave, then the waves, at the true max.
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (r >= nr) continue;
-    float mx = m[r];
+    float mx = m_true[r];
 #pragma unroll
     for (int x = LPT; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
-    const float f = (m[r] == kNegInf) ? 0.f : exp2f(m[r] - mx);
+    const float f = (m_run[r] == kNegInf) ? 0.f : exp2f(m_run[r] - mx);
     float lsum = l[r] * f;
 #pragma unroll
     for (int x = LPT; x < 64; x <<= 1) lsum += __shfl_xor(lsum, x);
@@ -1020,8 +1081,17 @@ static int launch_partials(const PartialArgs& pa, hipStream_t st) {
     }
   }
   if (pa.plan.n_valu > 0) {
-    if (pa.fused) hipLaunchKernelGGL((valu_partial<T, D, true>), dim3(pa.plan.n_valu * hkv), dim3(256), 0, st, pa);
-    else hipLaunchKernelGGL((valu_partial<T, D, false>), dim3(pa.plan.n_valu * hkv), dim3(256), 0, st, pa);
+    const dim3 grid(pa.plan.n_valu * hkv), block(256);
+    const int rows = pa.max_valu_rows;
+    if (pa.fused) {
+      if (rows <= 4) hipLaunchKernelGGL((valu_partial<T, D, 4, true>), grid, block, 0, st, pa);
+      else if (rows <= 8) hipLaunchKernelGGL((valu_partial<T, D, 8, true>), grid, block, 0, st, pa);
+      else hipLaunchKernelGGL((valu_partial<T, D, kValuRows, true>), grid, block, 0, st, pa);
+    } else {
+      if (rows <= 4) hipLaunchKernelGGL((valu_partial<T, D, 4, false>), grid, block, 0, st, pa);
+      else if (rows <= 8) hipLaunchKernelGGL((valu_partial<T, D, 8, false>), grid, block, 0, st, pa);
+      else hipLaunchKernelGGL((valu_partial<T, D, kValuRows, false>), grid, block, 0, st, pa);
+    }
     int rc = hip_check(hipGetLastError(), "launch of valu_partial");
     if (rc) return rc;
   }
@@ -1048,6 +1118,7 @@ static int run_partials(const void* q, const void* k, const void* v, const int32
   pa.po_bf16 = po_bf16 ? 1 : 0;
   pa.scale_log2 = kLog2e / std::sqrt(static_cast<float>(d->head_dim));
   pa.fused = fused_out != nullptr;
+  pa.max_valu_rows = p->layout.max_valu_rows;
   pa.merge.po = po;
   pa.merge.pm = pm;
   pa.merge.pl = pl;

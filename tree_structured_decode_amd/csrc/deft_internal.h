@@ -39,6 +39,7 @@ struct ImageLayout {
   size_t chunk_start, group_offsets, chunk_full, slot_query, slot_mask, flat_to_logical,
       query_slot_offsets, query_slots, mfma_items, valu_items, tickets, total_words;
   int32_t n_mfma, n_valu;
+  int32_t max_valu_rows;   // largest row count of a VALU work item (picks the kernel's row capacity)
 };
 
 void set_error(const std::string& msg);

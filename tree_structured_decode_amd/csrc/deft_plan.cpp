@@ -234,6 +234,8 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   L->total_words = w;
   L->n_mfma = static_cast<int32_t>(mfma.size());
   L->n_valu = static_cast<int32_t>(valu.size());
+  L->max_valu_rows = 0;
+  for (const WorkItem& it : valu) L->max_valu_rows = std::max(L->max_valu_rows, it.row_count);
   if (!image) return DEFT_OK;
   try {
     image->assign(w, 0);
