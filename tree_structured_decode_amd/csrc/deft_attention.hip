@@ -125,13 +125,20 @@ __device__ inline float group_sum(float x) {
   return x;
 }
 
-// s + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs, fp32 accumulate.
-// Written as inline asm: built from register words through the fdot2 builtin
-// and bit casts, the compiler fed one register to every call of an unrolled
-// sequence.  The compiler cannot see the asm's VGPR write, so the asm itself
-// provides the two wait states a following DPP read of the result needs.
-__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float s) {
-  asm("v_dot2c_f32_bf16 %0, %1, %2\n\ts_nop 1" : "+v"(s) : "v"(a), "v"(b));
+// s + the dot product of 8 packed bf16 pairs (four words each), fp32
+// accumulate.  Written as inline asm: built from register words through the
+// fdot2 builtin and bit casts, the compiler fed one register to every call
+// of an unrolled sequence.  The compiler cannot see the asm's VGPR write, so
+// the asm itself provides the two wait states a following DPP read of the
+// result needs.
+__device__ inline float dot8_bf16(const u32x4& a, const uint32_t* b, float s) {
+  asm("v_dot2c_f32_bf16 %0, %1, %2\n\t"
+      "v_dot2c_f32_bf16 %0, %3, %4\n\t"
+      "v_dot2c_f32_bf16 %0, %5, %6\n\t"
+      "v_dot2c_f32_bf16 %0, %7, %8\n\t"
+      "s_nop 1"
+      : "+v"(s)
+      : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]), "v"(a[2]), "v"(b[2]), "v"(a[3]), "v"(b[3]));
   return s;
 }
 
@@ -402,220 +409,7 @@ __device__ void fused_merge_tail(const MergeArgs& m, const DevPlan& P, int32_t* 
 }
 
 // ---------------------------------------------------------------------------
-// VALU partial kernel: groups below one MFMA tile (and fp32 inputs), up to R
-// rows per work-group (R = 4, 8 or 16, the smallest that holds the plan's
-// largest such group).  The work is a stream over the chunk's KV rows with
-// little arithmetic per byte, so the kernel keeps many loads in flight: lanes
-// are grouped LPT per token (each lane holds EPL elements of the token's K
-// and V row), a wave covers TPW tokens per step, the 4 waves interleave over
-// the chunk, and each lane keeps PF steps of K and V loads outstanding in
-// registers.  Each lane group keeps its own online-softmax state (running
-// max raised lazily, as in the MFMA kernel); groups and waves are merged at
-// the end.
-// ---------------------------------------------------------------------------
-template <typename T, int D, int R, bool FUSED>
-__global__ __launch_bounds__(256) void valu_partial(PartialArgs a) {
-  constexpr int EPL = Elem<T>::kPerLoad;
-  constexpr int LPT = D / EPL;
-  constexpr int TPW = 64 / LPT;
-  constexpr int NW = 4;
-  constexpr int STRIDE = NW * TPW;                      // tokens per work-group step
-  constexpr int PF = R <= 4 ? 8 : (R <= 8 ? 4 : 2);     // steps of loads in flight per lane
-  static_assert(R <= kValuRows, "row capacity");
-  __shared__ int32_t tok_row[kMaxChunkTokens];
-  __shared__ uint32_t masks[R * (kMaxChunkTokens / 32)];
-  __shared__ float red[NW][R][D + 2];
-
-  const DevPlan& P = a.plan;
-  const int g = blockIdx.x % a.hkv;
-  const int4 it0 = P.valu_items[2 * (blockIdx.x / a.hkv)];
-  const int4 it1 = P.valu_items[2 * (blockIdx.x / a.hkv) + 1];
-  const int32_t rb = it0.y, nr = it0.z, cs = it0.w;
-  const int32_t len = it1.x, gofs = it1.y;
-  const bool full = it1.z != 0;
-  const int W = P.mask_words;
-  const int j0 = rb / a.grp;
-  const int nslot = (rb + nr - 1) / a.grp - j0 + 1;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int tg = lane / LPT, li = lane % LPT;
-  constexpr int EB = sizeof(T);
-
-  // queries of the rows, looked up before the token rows are staged
-  int32_t qrow[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int row = rb + min(r, nr - 1);
-    qrow[r] = P.slot_query[gofs + row / a.grp];
-  }
-  // token rows are stored as rows of this KV head: pool row * Hkv + g
-  stage_token_rows<0, 256>(tok_row, P, a.block_table, cs, len, a.hkv, g);
-  if (!full)
-    for (int i = threadIdx.x; i < nslot * W; i += blockDim.x)
-      masks[i] = P.slot_mask[static_cast<size_t>(gofs + j0) * W + i];
-
-  // Q rows: bf16 kept packed (scores by bf16 dot2 with fp32 accumulation),
-  // fp32 as is; scores are scaled by scale * log2(e) into log2 units.
-  constexpr int QW = sizeof(T) == 2 ? EPL / 2 : EPL;   // 32-bit words of Q per lane and row
-  uint32_t qv[R][QW];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int row = rb + min(r, nr - 1);
-    const int head = g * a.grp + row % a.grp;
-    const u32x4 raw = load16(a.q, (static_cast<int64_t>(qrow[r]) * a.hq + head) * D + li * EPL, EB);
-#pragma unroll
-    for (int e = 0; e < QW; ++e) qv[r][e] = raw[e];
-  }
-  const float qscale = a.scale_log2;
-  __syncthreads();
-
-  float m_run[R], m_true[R], l[R], o[R][EPL];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    m_run[r] = kNegInf;
-    m_true[r] = kNegInf;
-    l[r] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[r][e] = 0.f;
-  }
-
-  // K and V of one token for this lane (every load reads a valid row: tokens
-  // past the chunk end re-read its last token and are masked).
-  const char* kbase = static_cast<const char*>(a.k) + li * EPL * EB;
-  const char* vbase = static_cast<const char*>(a.v) + li * EPL * EB;
-  auto fetch = [&](int step, u32x4& kr, u32x4& vr) {
-    const int t = min(step * STRIDE + w * TPW + tg, len - 1);
-    const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(tok_row[t])) * (D * EB);
-    kr = *reinterpret_cast<const u32x4*>(kbase + off);
-    vr = *reinterpret_cast<const u32x4*>(vbase + off);
-  };
-  auto process = [&](const u32x4& kr, const u32x4& vr, int step) {
-    const int t = step * STRIDE + w * TPW + tg;
-    float kf[EPL], vf[EPL];
-    if constexpr (sizeof(T) != 2) Elem<T>::unpack(kr, kf);
-    Elem<T>::unpack(vr, vf);
-    const bool valid = t < len;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r >= nr) continue;
-      float s = 0.f;
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < QW; ++e) s = dot2_bf16(kr[e], qv[r][e], s);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) s = fmaf(__uint_as_float(qv[r][e]), kf[e], s);
-      }
-      s = group_sum<LPT>(s) * qscale;
-      bool vis = valid;
-      if (!full && valid) {
-        const int j = (rb + r) / a.grp - j0;
-        vis = (masks[j * W + (t >> 5)] >> (t & 31)) & 1u;
-      }
-      const float z = vis ? s : kNegInf;
-      m_true[r] = fmaxf(m_true[r], z);
-      // the running max rises only when a score exceeds it by the slack
-      const bool raise = z > m_run[r] + kRescaleSlack || (m_run[r] == kNegInf && z != kNegInf);
-      if (__any(raise)) {
-        const float mn = raise ? z : m_run[r];
-        const float alpha = raise ? exp2f(m_run[r] - mn) : 1.f;   // m = -inf gives 0
-        m_run[r] = mn;
-        l[r] *= alpha;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
-      }
-      const float p = m_run[r] == kNegInf ? 0.f : fast_exp2(z - m_run[r]);   // z = -inf gives 0
-      l[r] += p;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
-    }
-  };
-
-  const int nsteps = (len + STRIDE - 1) / STRIDE;
-  u32x4 kb[PF], vb[PF];
-#pragma unroll
-  for (int p = 0; p < PF; ++p) fetch(p, kb[p], vb[p]);
-  for (int s0 = 0; s0 < nsteps; s0 += PF) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      if (s0 + p < nsteps) process(kb[p], vb[p], s0 + p);
-      fetch(s0 + p + PF, kb[p], vb[p]);   // loads are issued unconditionally, in a fixed order
-    }
-  }
-
-  // Merge the lane groups of this wave, then the waves, at the true max.
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (r >= nr) continue;
-    float mx = m_true[r];
-#pragma unroll
-    for (int x = LPT; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
-    const float f = (m_run[r] == kNegInf) ? 0.f : exp2f(m_run[r] - mx);
-    float lsum = l[r] * f;
-#pragma unroll
-    for (int x = LPT; x < 64; x <<= 1) lsum += __shfl_xor(lsum, x);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float ov = o[r][e] * f;
-#pragma unroll
-      for (int x = LPT; x < 64; x <<= 1) ov += __shfl_xor(ov, x);
-      o[r][e] = ov;
-    }
-    if (tg == 0) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) red[w][r][li * EPL + e] = o[r][e];
-      if (li == 0) {
-        red[w][r][D] = mx;
-        red[w][r][D + 1] = lsum;
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
-    const int r = idx / D, e = idx % D;
-    float mx = kNegInf;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, red[ww][r][D]);
-    float ov = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float mw = red[ww][r][D];
-      const float f = (mw == kNegInf) ? 0.f : exp2f(mw - mx);
-      ov += f * red[ww][r][e];
-      lsum += f * red[ww][r][D + 1];
-    }
-    const int row = rb + r;
-    const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
-    if (a.po_bf16) reinterpret_cast<uint16_t*>(a.po)[sh * D + e] = f32_to_bf16(ov / lsum);
-    else a.po[sh * D + e] = ov;
-    if (e == 0) {
-      a.pm[sh] = mx == kNegInf ? kNegInf : mx * kLn2;
-      a.pl[sh] = lsum;
-    }
-  }
-  if constexpr (FUSED) {
-    __shared__ int32_t last_list[kValuRows];
-    __shared__ int32_t n_last[1];
-    fused_merge_tail<T, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, n_last);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// MFMA partial kernel (bf16).  Work-group = 8 waves (two per SIMD) on one
-// (chunk, KV head, block of up to 64 rows).  Wave w owns row half h = w & 1
-// (rows 32h .. 32h+31, two 16-row tiles) and token split sp = w >> 1: it takes
-// the chunk's 32-token steps sp, sp+4, ...  The two waves of a split share a
-// two-stage LDS ring; per step one of them loads the K rows and the 64 rows'
-// mask words, the other the V rows, by direct-to-LDS loads (no VGPRs), one
-// step ahead, with one work-group barrier per step.  Per step and wave:
-//   S^T = K Q^T   16x16x32 MFMA, A = K rows (LDS), B = Q^T (registers), for
-//                 2 token tiles x 2 row tiles;
-//   mask, online softmax on the S^T fragments in registers;
-//   O^T += V^T P^T  A = V^T from LDS transpose reads of the token-major V
-//                 rows, B = P^T taken straight from the S^T fragments.
-// K tile rows are permuted so every lane ends up holding 8 consecutive tokens
-// of one row, which is the B-operand layout of the PV product.  Rows in LDS
-// are stored with their 16-byte chunks XOR-swizzled by the row index.  The
-// four token splits of each row half are merged through LDS at the end.
+// Direct-to-LDS loads and wave helpers shared by the partial kernels.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lptr_t;
 // Direct-to-LDS loads, written as inline asm: lane i's bytes land at LDS
@@ -664,6 +458,316 @@ __device__ inline void pair_sync(int32_t* mine, int32_t* theirs, int32_t i, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// VALU partial kernel: groups below one MFMA tile, and fp32 inputs; up to R
+// rows per work-group (R = 4 or 8, the smaller that holds the plan's largest
+// VALU work item; larger groups are split into items of 8 rows that share
+// the chunk's KV through L2).  Scores and the PV update are wavefront arithmetic:
+// lanes are grouped LPT per token (each lane holds 16 bytes of the token's
+// K and V row), dot products are summed across the group with DPP moves.
+// The work is a stream over the chunk's KV rows with little arithmetic per
+// byte, so memory is fed like the MFMA kernel: each of the 4 waves takes the
+// chunk's steps (4 KB of K rows per step) w, w+4, ... and streams them with
+// direct-to-LDS loads into a private NSTG-stage ring, NSTG-1 steps ahead,
+// with explicit waits.  Each lane group keeps its own online-softmax state
+// (running max raised lazily); groups and waves are merged at the end.
+// ---------------------------------------------------------------------------
+template <int R> constexpr int valu_waves() { return R <= 8 ? 8 : 4; }
+
+template <typename T, int D, int R, bool FUSED>
+__global__ __launch_bounds__(64 * valu_waves<R>()) void valu_partial(PartialArgs a) {
+  constexpr int EB = sizeof(T);
+  constexpr int EPL = 16 / EB;                     // elements per lane (16 bytes)
+  constexpr int LPT = D / EPL;                     // lanes per token
+  constexpr int TPW = 64 / LPT;                    // tokens per wave pass
+  // two waves per SIMD (latency hiding) while the rows' registers allow it
+  constexpr int NW = valu_waves<R>();
+  constexpr int ROWB = D * EB;                     // bytes per token row
+  constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
+  constexpr int TILE_B = 4096;                     // K (or V) bytes per step
+  constexpr int STEP_T = TILE_B / ROWB;            // tokens per step (8, 16 or 32)
+  constexpr int NI = TILE_B / 1024;                // 1 KB direct loads per tile
+  constexpr int RPI = 1024 / ROWB;                 // rows per direct load
+  constexpr int NSTG = NW == 8 ? 2 : 4;            // ring stages per wave (same LDS either way)
+  constexpr int MASK_OFF = 2 * TILE_B;             // stage: K, V, mask words
+  constexpr int STAGE_B = 2 * TILE_B + 256;
+  constexpr int OPS = 2 * NI + 1;                  // vector-memory operations per step
+  constexpr int RING_B = NW * NSTG * STAGE_B;
+  constexpr int RED_B = NW * R * (D + 2) * 4;
+  static_assert(R <= kValuRows && R <= 64, "row capacity");
+  static_assert(STEP_T <= 32 && 32 % STEP_T == 0, "a step's mask bits lie in one word");
+  static_assert(RPI >= 2 && 32 % RPI == 0 && NI == 4, "staged-row permutation");
+  __shared__ __attribute__((aligned(1024))) char smem[RING_B > RED_B ? RING_B : RED_B];
+  __shared__ __attribute__((aligned(16))) int32_t tok_row[kMaxChunkTokens];
+
+  const DevPlan& P = a.plan;
+  const int g = blockIdx.x % a.hkv;
+  const int4 it0 = P.valu_items[2 * (blockIdx.x / a.hkv)];
+  const int4 it1 = P.valu_items[2 * (blockIdx.x / a.hkv) + 1];
+  const int32_t rb = it0.y, nr = it0.z, cs = it0.w;
+  const int32_t len = it1.x, gofs = it1.y;
+  const int W = P.mask_words;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tg = lane / LPT, li = lane % LPT;
+
+  // queries of the rows (rows past nr repeat the last row; never stored)
+  int32_t qrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) qrow[r] = P.slot_query[gofs + (rb + min(r, nr - 1)) / a.grp];
+  // token rows as rows of this KV head (pool row * Hkv + g), permuted so a
+  // lane's rows of one step are adjacent
+  stage_token_rows<RPI, 64 * NW>(tok_row, P, a.block_table, cs, len, a.hkv, g);
+  // lane i loads the mask word of row i (rows past nr: the last row's)
+  const int32_t mask_slot = gofs + (rb + min(lane, nr - 1)) / a.grp;
+  const uint32_t* mask_src = P.slot_mask + static_cast<size_t>(mask_slot) * W;
+  __syncthreads();
+
+  char* ring = smem + w * NSTG * STAGE_B;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  const int lrow = lane / CH, lch = lane % CH;     // this lane's row and 16-byte slot in each load
+  // Row R of a tile stores chunk p ^ (R % RPI) in its slot p (R % RPI is the
+  // loading lane's lrow for every load of the tile).
+  const char* kbase = static_cast<const char*>(a.k) + (lch ^ lrow) * 16;
+  const char* vbase = static_cast<const char*>(a.v) + (lch ^ lrow) * 16;
+  const int nsteps = (len + STEP_T - 1) / STEP_T;
+  const int my_steps = w < nsteps ? (nsteps - w + NW - 1) / NW : 0;
+
+  // Loads of one step into one stage: NI K rows, NI V rows, the mask words.
+  // Load n fetches rows n*RPI + lrow of the step (R = lrow + n*RPI, so
+  // R % CH = lrow % CH for every n: one swizzle per lane); tokens past the
+  // chunk end re-read its last token (finite values; masked).
+  auto issue = [&](int i, int stage) {
+    const int step = w + i * NW;
+    const int base = step * STEP_T;
+    const uint32_t sd = ring_lds + stage * STAGE_B;
+    int32_t rows[NI];
+    if (base + STEP_T <= len) {
+      const int32_t* tr = tok_row + (base & ~31) + lrow * (32 / RPI) + (base & 31) / RPI;
+      const int4 v4 = *reinterpret_cast<const int4*>(tr);
+      rows[0] = v4.x; rows[1] = v4.y; rows[2] = v4.z; rows[3] = v4.w;
+    } else {
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const int t = min(base + n * RPI + lrow, len - 1);
+        rows[n] = tok_row[(t & ~31) + (t % RPI) * (32 / RPI) + (t & 31) / RPI];
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+      lds_dma16(kbase + static_cast<uint64_t>(static_cast<uint32_t>(rows[n])) * ROWB, sd + n * 1024);
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+      lds_dma16(vbase + static_cast<uint64_t>(static_cast<uint32_t>(rows[n])) * ROWB, sd + TILE_B + n * 1024);
+    lds_dma4(mask_src + (base >> 5), sd + MASK_OFF);
+  };
+
+  float m_run[R], m_true[R], l[R], o[R][EPL];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m_run[r] = kNegInf;
+    m_true[r] = kNegInf;
+    l[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[r][e] = 0.f;
+  }
+  const float qscale = a.scale_log2;
+
+  // The R Q rows go through the last ring stage (first refilled in step 0),
+  // by direct-to-LDS loads like the KV rows, so no ordinary global load is
+  // pending in the loop; then NSTG-1 steps are put in flight.
+  constexpr int NQ = (R * ROWB + 1023) / 1024;     // Q loads of 1 KB
+  static_assert(R * ROWB <= 2 * TILE_B, "Q rows fit in one stage");
+  const uint32_t qstage = ring_lds + (NSTG - 1) * STAGE_B;
+  if (my_steps > 0) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const int byte = n * 1024 + lane * 16;
+      const int r = min(byte / ROWB, R - 1);       // lanes past R rows reload the last one
+      const int row = rb + min(r, nr - 1);
+      const int head = g * a.grp + row % a.grp;
+      lds_dma16(static_cast<const char*>(a.q) + ((static_cast<int64_t>(qrow[r]) * a.hq + head) * D) * EB +
+                    (byte % ROWB), qstage + n * 1024);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NSTG - 1; ++i)
+    if (i < my_steps) issue(i, i);
+  constexpr int QW = 4;   // 32-bit words of Q per lane and row
+  uint32_t qv[R][QW];
+  for (int i = 0; i < my_steps; ++i) {
+    const int stage = i % NSTG;
+    // this step's loads are done once at most the later issued steps remain
+    const int later = min(NSTG - 2, my_steps - 1 - i);
+    if (NSTG > 3 && later >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * OPS));
+    else if (NSTG > 2 && later >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(OPS));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if (i == 0) {
+      // Q rows (older than step 0's loads, so done too): bf16 stays packed
+      // (scores by bf16 dot2, fp32 accumulate), fp32 as is
+      const char* qs = ring + (NSTG - 1) * STAGE_B;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(qs + r * ROWB + li * 16);
+#pragma unroll
+        for (int e = 0; e < QW; ++e) qv[r][e] = raw[e];
+      }
+      // the Q reads complete before this stage is refilled below
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    }
+    // refill the stage read in step i-1 (its reads have all returned)
+    if (i + NSTG - 1 < my_steps) issue(i + NSTG - 1, (i + NSTG - 1) % NSTG);
+    const char* kb = ring + stage * STAGE_B;
+    const int base = (w + i * NW) * STEP_T;
+    const uint32_t* mw = reinterpret_cast<const uint32_t*>(kb + MASK_OFF);
+    uint32_t mbits[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) mbits[r] = mw[r] >> (base & 31);
+    // the step's K and V fragments for every pass, read before any is used
+    constexpr int NPASS = STEP_T / TPW;
+    u32x4 kfr[NPASS], vfr[NPASS];
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int tr = ps * TPW + tg;
+      const int sw = (li ^ (tr % RPI)) * 16;
+      kfr[ps] = *reinterpret_cast<const u32x4*>(kb + tr * ROWB + sw);
+      vfr[ps] = *reinterpret_cast<const u32x4*>(kb + TILE_B + tr * ROWB + sw);
+    }
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int tr = ps * TPW + tg;                 // token within the step
+      const bool valid = base + tr < len;
+      const u32x4& kr = kfr[ps];
+      const u32x4& vr = vfr[ps];
+      float vf[EPL];
+      Elem<T>::unpack(vr, vf);
+      // All rows side by side (independent chains): scores, group sums,
+      // mask, one branch for the rare rise of any running max, then the
+      // probability and the O and l updates.
+      float z[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float sc = 0.f;
+        if constexpr (EB == 2) {
+          sc = dot8_bf16(kr, qv[r], sc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < QW; ++e) sc = fmaf(__uint_as_float(qv[r][e]), __uint_as_float(kr[e]), sc);
+        }
+        z[r] = sc;
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) z[r] = group_sum<LPT>(z[r]) * qscale;
+      bool raise[R];
+      bool any_raise = false;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bool vis = valid && ((mbits[r] >> tr) & 1u);
+        z[r] = vis ? z[r] : kNegInf;
+        m_true[r] = fmaxf(m_true[r], z[r]);
+        // the running max rises only when a score exceeds it by the slack
+        // (a running max of -inf is exceeded by any finite score)
+        raise[r] = z[r] > m_run[r] + kRescaleSlack;
+        any_raise |= raise[r];
+      }
+      if (__any(any_raise)) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float mn = raise[r] ? z[r] : m_run[r];
+          const float alpha = raise[r] ? fast_exp2(m_run[r] - mn) : 1.f;   // m = -inf gives 0
+          m_run[r] = mn;
+          l[r] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float p = m_run[r] == kNegInf ? 0.f : fast_exp2(z[r] - m_run[r]);   // z = -inf gives 0
+        l[r] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
+      }
+    }
+  }
+
+  // Merge the lane groups of this wave, then the waves (through LDS, over
+  // the ring), at the true max.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);   // [NW][R][D + 2]
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float mx = m_true[r];
+#pragma unroll
+    for (int x = LPT; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+    const float f = (m_run[r] == kNegInf) ? 0.f : exp2f(m_run[r] - mx);
+    float lsum = l[r] * f;
+#pragma unroll
+    for (int x = LPT; x < 64; x <<= 1) lsum += __shfl_xor(lsum, x);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float ov = o[r][e] * f;
+#pragma unroll
+      for (int x = LPT; x < 64; x <<= 1) ov += __shfl_xor(ov, x);
+      o[r][e] = ov;
+    }
+    if (tg == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red[(w * R + r) * (D + 2) + li * EPL + e] = o[r][e];
+      if (li == 0) {
+        red[(w * R + r) * (D + 2) + D] = mx;
+        red[(w * R + r) * (D + 2) + D + 1] = lsum;
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
+    const int r = idx / D, e = idx % D;
+    float mx = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, red[(ww * R + r) * (D + 2) + D]);
+    float ov = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float mw = red[(ww * R + r) * (D + 2) + D];
+      const float f = (mw == kNegInf) ? 0.f : exp2f(mw - mx);
+      ov += f * red[(ww * R + r) * (D + 2) + e];
+      lsum += f * red[(ww * R + r) * (D + 2) + D + 1];
+    }
+    const int row = rb + r;
+    const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
+    if (a.po_bf16) reinterpret_cast<uint16_t*>(a.po)[sh * D + e] = f32_to_bf16(ov / lsum);
+    else a.po[sh * D + e] = ov;
+    if (e == 0) {
+      a.pm[sh] = mx == kNegInf ? kNegInf : mx * kLn2;
+      a.pl[sh] = lsum;
+    }
+  }
+  if constexpr (FUSED) {
+    __shared__ int32_t last_list[kValuRows];
+    __shared__ int32_t n_last[1];
+    fused_merge_tail<T, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, n_last);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA partial kernel (bf16).  Work-group = 8 waves (two per SIMD) on one
+// (chunk, KV head, block of up to 64 rows).  Wave w owns row half h = w & 1
+// (rows 32h .. 32h+31, two 16-row tiles) and token split sp = w >> 1: it takes
+// the chunk's 32-token steps sp, sp+4, ...  The two waves of a split share a
+// two-stage LDS ring; per step one of them loads the K rows and the 64 rows'
+// mask words, the other the V rows, by direct-to-LDS loads (no VGPRs), one
+// step ahead, with one work-group barrier per step.  Per step and wave:
+//   S^T = K Q^T   16x16x32 MFMA, A = K rows (LDS), B = Q^T (registers), for
+//                 2 token tiles x 2 row tiles;
+//   mask, online softmax on the S^T fragments in registers;
+//   O^T += V^T P^T  A = V^T from LDS transpose reads of the token-major V
+//                 rows, B = P^T taken straight from the S^T fragments.
+// K tile rows are permuted so every lane ends up holding 8 consecutive tokens
+// of one row, which is the B-operand layout of the PV product.  Rows in LDS
+// are stored with their 16-byte chunks XOR-swizzled by the row index.  The
+// four token splits of each row half are merged through LDS at the end.
+// ---------------------------------------------------------------------------
 template <int D, bool FUSED>
 __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   constexpr int NWAVE = 8;
@@ -886,10 +990,11 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
       m_true[rt] = fmaxf(m_true[rt], mx);
-      const bool high = mx > m_run[rt] + kRescaleSlack / cl2 || (m_run[rt] == kNegInf && mx != kNegInf);
+      // (a running max of -inf is exceeded by any finite score)
+      const bool high = mx > m_run[rt] + kRescaleSlack / cl2;
       if (__any(high)) {
         const float rmx = rowmax4(mx);
-        const bool raise = rmx > m_run[rt] + kRescaleSlack / cl2 || (m_run[rt] == kNegInf && rmx != kNegInf);
+        const bool raise = rmx > m_run[rt] + kRescaleSlack / cl2;
         const float mn = raise ? rmx : m_run[rt];
         const float alpha = raise ? fast_exp2((m_run[rt] - mn) * cl2) : 1.f;
         m_run[rt] = mn;
@@ -1081,16 +1186,16 @@ static int launch_partials(const PartialArgs& pa, hipStream_t st) {
     }
   }
   if (pa.plan.n_valu > 0) {
-    const dim3 grid(pa.plan.n_valu * hkv), block(256);
+    const dim3 grid(pa.plan.n_valu * hkv);
     const int rows = pa.max_valu_rows;
+    static_assert(kValuRows == 8, "VALU row capacities are 4 and 8");
+    const dim3 b4(64 * valu_waves<4>()), b8(64 * valu_waves<8>());
     if (pa.fused) {
-      if (rows <= 4) hipLaunchKernelGGL((valu_partial<T, D, 4, true>), grid, block, 0, st, pa);
-      else if (rows <= 8) hipLaunchKernelGGL((valu_partial<T, D, 8, true>), grid, block, 0, st, pa);
-      else hipLaunchKernelGGL((valu_partial<T, D, kValuRows, true>), grid, block, 0, st, pa);
+      if (rows <= 4) hipLaunchKernelGGL((valu_partial<T, D, 4, true>), grid, b4, 0, st, pa);
+      else hipLaunchKernelGGL((valu_partial<T, D, 8, true>), grid, b8, 0, st, pa);
     } else {
-      if (rows <= 4) hipLaunchKernelGGL((valu_partial<T, D, 4, false>), grid, block, 0, st, pa);
-      else if (rows <= 8) hipLaunchKernelGGL((valu_partial<T, D, 8, false>), grid, block, 0, st, pa);
-      else hipLaunchKernelGGL((valu_partial<T, D, kValuRows, false>), grid, block, 0, st, pa);
+      if (rows <= 4) hipLaunchKernelGGL((valu_partial<T, D, 4, false>), grid, b4, 0, st, pa);
+      else hipLaunchKernelGGL((valu_partial<T, D, 8, false>), grid, b8, 0, st, pa);
     }
     int rc = hip_check(hipGetLastError(), "launch of valu_partial");
     if (rc) return rc;

@@ -20,7 +20,7 @@ constexpr int kPageSize = 16;
 // the hh-th query head of the KV head being processed (G = Hq / Hkv).
 constexpr int kMfmaRows = 64;      // rows per MFMA work item (4 tiles of 16)
 constexpr int kMfmaMinRows = 16;   // a chunk needs this many rows to use MFMA
-constexpr int kValuRows = 16;      // rows per VALU work item
+constexpr int kValuRows = 8;       // rows per VALU work item
 
 struct WorkItem {                  // two int4 on the device
   int32_t chunk;
