@@ -148,6 +148,26 @@ int deft_plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t nu
                      const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
                      deft_plan** out_plan);
 
+/*
+ * Query-centric baseline plan, for measuring what KV-Guided Grouping saves
+ * on the same hardware (the pages contrast DeFT with per-query attention
+ * that reloads the shared prefix for every query: abstract; Guide, "The
+ * Memory Wall and Redundant IO").  Same arguments and errors as
+ * deft_plan_create (plus INVALID_TREE if the summed path lengths exceed
+ * 2^31 - 1).  Each query's root-to-node path tokens (root segment first, each
+ * segment in order) form their own run of the flat index space, queries in
+ * order; each run is cut into chunk_tokens windows from its start and every
+ * chunk has exactly one slot, its query, with all bits set, so the attention
+ * calls stream every query's whole path by itself.  In the view,
+ * total_tokens is the summed path length and flat_to_logical maps that
+ * space; node_start, flat_node_order and node_flat_start are those of
+ * deft_plan_create.  Results of the attention calls are those of the tree
+ * plan up to rounding.
+ */
+int deft_plan_create_query_centric(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                                   const int32_t* query_nodes, int32_t num_queries,
+                                   int32_t chunk_tokens, deft_plan** out_plan);
+
 /* Free a plan (NULL is ignored).  The caller must first let every stream that
  * consumes its device image get past that work. */
 void deft_plan_destroy(deft_plan* plan);

@@ -162,3 +162,64 @@ def ref_plan(parents, seg_lens, query_nodes, chunk_tokens: int) -> dict:
         "query_slot_offsets": i32(query_slot_offsets),
         "query_slots": i32(query_slots),
     }
+
+
+def ref_plan_query_centric(parents, seg_lens, query_nodes, chunk_tokens: int) -> dict:
+    """The query-centric baseline plan (no KV sharing), the per-query reading
+    of attention that DeFT's abstract and the Guide's "The Memory Wall and
+    Redundant IO" contrast it with: each query's root-to-node path tokens
+    (root segment first, every segment in order) form their own run of the
+    flat index space, queries one after another; each run is cut into
+    chunk_tokens windows from its own start; every chunk holds one slot (its
+    query) with every bit of the chunk set.  node_start, flat_node_order and
+    node_flat_start are those of the tree plan.
+    """
+    tree = ref_plan(parents, seg_lens, query_nodes, chunk_tokens)
+    parents = np.asarray(parents, dtype=np.int64)
+    seg_lens = np.asarray(seg_lens, dtype=np.int64)
+    query_nodes = np.asarray(query_nodes, dtype=np.int64)
+    node_start = tree["node_start"].astype(np.int64)
+    nq = query_nodes.shape[0]
+    c = int(chunk_tokens)
+    words = -(-c // 32)
+    flat, chunk_start, slot_query, qso = [], [], [], [0]
+    for qi in range(nq):
+        path = []
+        x = int(query_nodes[qi])
+        while x >= 0:
+            path.append(x)
+            x = int(parents[x])
+        q0 = len(flat)
+        for x in reversed(path):                 # root first
+            flat.extend(range(int(node_start[x]), int(node_start[x] + seg_lens[x])))
+        for a in range(q0, len(flat), c):
+            chunk_start.append(a)
+            slot_query.append(qi)
+        qso.append(len(slot_query))
+    total = len(flat)
+    if total > INT32_MAX:
+        raise PlanError("invalid_tree", "total path tokens exceed int32")
+    chunk_start.append(total)
+    nc = len(slot_query)
+    slot_mask = np.zeros((nc, words), dtype=np.uint32)
+    for k in range(nc):
+        bits = np.zeros(words * 32, dtype=np.uint8)
+        bits[:chunk_start[k + 1] - chunk_start[k]] = 1
+        slot_mask[k] = np.packbits(bits, bitorder="little").view("<u4")
+    i32 = lambda a: np.asarray(a, dtype=np.int64).astype(np.int32)
+    out = dict(tree)
+    out.update({
+        "total_tokens": total,
+        "num_chunks": nc,
+        "num_slots": nc,
+        "mask_words": words,
+        "flat_to_logical": i32(flat),
+        "chunk_start": i32(chunk_start),
+        "group_offsets": i32(np.arange(nc + 1)),
+        "slot_query": i32(slot_query),
+        "slot_mask": slot_mask,
+        "chunk_full": np.ones(nc, dtype=np.uint8),
+        "query_slot_offsets": i32(qso),
+        "query_slots": i32(np.arange(nc)),
+    })
+    return out

@@ -6,7 +6,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle.plan import PlanError, ref_plan
+from oracle.plan import PlanError, ref_plan, ref_plan_query_centric
 from tree_structured_decode_amd import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -139,3 +139,34 @@ def test_rejects_bad_input():
     with pytest.raises(PlanError) as e:
         ref_plan(ok[0], ok[1], [], 4)
     assert e.value.kind == "invalid_argument"
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_query_centric_plan_covers_each_path_once(seed):
+    """Each query's run of the query-centric plan holds exactly the logical
+    tokens it may see (ancestor sets by closure, not by walking paths), once
+    each; every chunk is one full single-query slot within one run."""
+    rng = np.random.default_rng(9100 + seed)
+    n = int(rng.integers(1, 30))
+    p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([1, 4, 40])), int(rng.integers(1, 9)),
+                             forest_prob=float(rng.choice([0.0, 0.4])))
+    c = int(rng.choice([1, 5, 32, 64]))
+    plan = ref_plan_query_centric(p, s, qn, c)
+    anc = _ancestor_sets(p)
+    starts = np.concatenate([[0], np.cumsum(s)])
+    f2l = plan["flat_to_logical"]
+    cs = plan["chunk_start"]
+    qso = plan["query_slot_offsets"]
+    assert plan["num_slots"] == plan["num_chunks"] == len(cs) - 1
+    assert (plan["chunk_full"] == 1).all()
+    assert (plan["group_offsets"] == np.arange(plan["num_chunks"] + 1)).all()
+    for qi, node in enumerate(qn):
+        want = sorted(t for x in anc[int(node)] for t in range(starts[x], starts[x + 1]))
+        ks = range(qso[qi], qso[qi + 1])
+        assert all(plan["slot_query"][k] == qi for k in ks)
+        got = [int(t) for k in ks for t in f2l[cs[k]:cs[k + 1]]]
+        assert sorted(got) == want and len(got) == len(set(got))
+        for k in ks:
+            assert 1 <= cs[k + 1] - cs[k] <= c
+            nbits = sum(bin(int(w)).count("1") for w in plan["slot_mask"][k])
+            assert nbits == cs[k + 1] - cs[k]

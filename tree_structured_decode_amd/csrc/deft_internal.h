@@ -55,6 +55,8 @@ struct deft_plan {
   std::vector<uint32_t> slot_mask;
   std::vector<uint8_t> chunk_full;
 
+  bool query_centric = false;   // built by deft_plan_create_query_centric
+
   // Device image for the last uploaded desc.
   bool uploaded = false;
   deft_attn_desc desc{};

@@ -170,6 +170,64 @@ static int build_plan(deft_plan* p, const int32_t* parents, const int32_t* seg_l
   return DEFT_OK;
 }
 
+// Query-centric baseline plan: no KV sharing.  Each query's root-to-node
+// path tokens (root segment first, each segment in order) form its own run of
+// the flat index space, queries one after another; each run is cut into
+// chunk_tokens windows from its start, every chunk has one slot (its query)
+// with every bit set.  The same kernels then stream every query's whole path
+// by itself, which is the per-query reading the pages compare DeFT against.
+// node_start / flat_node_order / node_flat_start keep the tree plan's values.
+static int build_query_centric(deft_plan* p, const int32_t* parents, const int32_t* seg_lens,
+                               int32_t n, const int32_t* query_nodes, int32_t nq, int32_t c) {
+  int rc = build_plan(p, parents, seg_lens, n, query_nodes, nq, c);   // tree fields
+  if (rc) return rc;
+  std::vector<int32_t> path;
+  int64_t total = 0;
+  for (int32_t q = 0; q < nq; ++q)
+    for (int32_t x = query_nodes[q]; x >= 0; x = parents[x]) total += seg_lens[x];
+  if (total > INT32_MAX) return fail(DEFT_ERR_INVALID_TREE, "total path tokens exceed 2^31 - 1");
+  p->flat_to_logical.assign(static_cast<size_t>(total), 0);
+  p->chunk_start.clear();
+  p->slot_query.clear();
+  p->query_slot_offsets.assign(nq + 1, 0);
+  int64_t f = 0;
+  for (int32_t q = 0; q < nq; ++q) {
+    path.clear();
+    for (int32_t x = query_nodes[q]; x >= 0; x = parents[x]) path.push_back(x);
+    const int64_t q0 = f;
+    for (auto it = path.rbegin(); it != path.rend(); ++it)
+      for (int32_t i = 0; i < seg_lens[*it]; ++i) p->flat_to_logical[f++] = p->node_start[*it] + i;
+    for (int64_t a = q0; a < f; a += c) {
+      p->chunk_start.push_back(static_cast<int32_t>(a));
+      p->slot_query.push_back(q);
+    }
+    p->query_slot_offsets[q + 1] = static_cast<int32_t>(p->slot_query.size());
+  }
+  const int32_t nc = static_cast<int32_t>(p->slot_query.size());
+  p->chunk_start.push_back(static_cast<int32_t>(total));
+  const int32_t words = (c + 31) / 32;
+  p->group_offsets.resize(nc + 1);
+  p->query_slots.resize(nc);
+  for (int32_t k = 0; k <= nc; ++k) p->group_offsets[k] = k;
+  for (int32_t k = 0; k < nc; ++k) p->query_slots[k] = k;
+  p->slot_mask.assign(static_cast<size_t>(nc) * words, 0u);
+  for (int32_t k = 0; k < nc; ++k) {
+    const int32_t len = p->chunk_start[k + 1] - p->chunk_start[k];
+    uint32_t* row = &p->slot_mask[static_cast<size_t>(k) * words];
+    for (int32_t w = 0; w < words; ++w) {
+      const int32_t bits = std::min(32, std::max(0, len - 32 * w));
+      row[w] = bits == 32 ? 0xffffffffu : ((1u << bits) - 1u);
+    }
+  }
+  p->chunk_full.assign(nc, 1);
+  p->total_tokens = static_cast<int32_t>(total);
+  p->num_chunks = nc;
+  p->num_slots = nc;
+  p->mask_words = words;
+  p->query_centric = true;
+  return DEFT_OK;
+}
+
 int check_desc(const deft_plan* p, const deft_attn_desc* d) {
   if (!d) return fail(DEFT_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->page_size < 1 ||
@@ -208,7 +266,9 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   for (int32_t k = 0; k < p->num_chunks; ++k) {
     const int32_t rows = (p->group_offsets[k + 1] - p->group_offsets[k]) * G;
     if (rows == 0) continue;
-    const bool use_mfma = d->dtype == DEFT_DTYPE_BF16 && rows >= kMfmaMinRows;
+    // MFMA when the group fills a tile; the query-centric baseline (groups of
+    // one query) takes MFMA for every bf16 group, its faster kernel
+    const bool use_mfma = d->dtype == DEFT_DTYPE_BF16 && (rows >= kMfmaMinRows || p->query_centric);
     const int32_t blk = use_mfma ? kMfmaRows : kValuRows;
     const int32_t cs = p->chunk_start[k], len = p->chunk_start[k + 1] - cs;
     for (int32_t r = 0; r < rows; r += blk)
@@ -262,9 +322,9 @@ using deft::fail;
 
 extern "C" {
 
-int deft_plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
-                     const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
-                     deft_plan** out_plan) {
+static int plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                       const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
+                       bool query_centric, deft_plan** out_plan) {
   deft::set_error("");
   if (!out_plan) return fail(DEFT_ERR_INVALID_ARGUMENT, "out_plan is NULL");
   *out_plan = nullptr;
@@ -290,7 +350,9 @@ int deft_plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t nu
   if (!p) return fail(DEFT_ERR_NO_MEMORY, "host allocation failed");
   int rc;
   try {
-    rc = deft::build_plan(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens);
+    rc = query_centric
+             ? deft::build_query_centric(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens)
+             : deft::build_plan(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens);
   } catch (const std::bad_alloc&) {
     rc = fail(DEFT_ERR_NO_MEMORY, "host allocation failed while planning");
   }
@@ -300,6 +362,18 @@ int deft_plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t nu
   }
   *out_plan = p;
   return DEFT_OK;
+}
+
+int deft_plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                     const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
+                     deft_plan** out_plan) {
+  return plan_create(parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens, false, out_plan);
+}
+
+int deft_plan_create_query_centric(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                                   const int32_t* query_nodes, int32_t num_queries,
+                                   int32_t chunk_tokens, deft_plan** out_plan) {
+  return plan_create(parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens, true, out_plan);
 }
 
 void deft_plan_destroy(deft_plan* plan) { delete plan; }

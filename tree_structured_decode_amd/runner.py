@@ -15,9 +15,10 @@ class TreeAttention:
     """
 
     def __init__(self, parents, seg_lens, query_nodes, chunk_tokens: int, desc, device="cuda",
-                 stream=None):
+                 stream=None, query_centric: bool = False):
         self.desc = desc
-        self.plan = D.deft_plan_create(parents, seg_lens, query_nodes, chunk_tokens)
+        create = D.deft_plan_create_query_centric if query_centric else D.deft_plan_create
+        self.plan = create(parents, seg_lens, query_nodes, chunk_tokens)
         plan_bytes, ws_bytes = D.deft_plan_device_bytes(self.plan, desc)
         self.plan_bytes, self.workspace_bytes = plan_bytes, ws_bytes
         self.dev_plan = torch.empty(max(plan_bytes, 256), dtype=torch.uint8, device=device)
