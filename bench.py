@@ -280,32 +280,39 @@ def main():
     for i in range(copies):
         step(i)
     torch.cuda.synchronize()
-    # Query-centric baseline on the same kernels: every query streams its own
-    # root-to-node path (no KV-Guided Grouping), same copies, same timing.
-    qc_plan = D.deft_plan_create_query_centric(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens)
-    qc_pb, qc_wb = D.deft_plan_device_bytes(qc_plan, desc)
-    qc_dev = torch.empty(max(qc_pb, 256), dtype=torch.uint8, device=dev)
-    qc_ws = torch.empty(max(qc_wb, 256), dtype=torch.uint8, device=dev)
-    D.deft_plan_upload(qc_plan, desc, qc_dev)
-    qc_outs = [torch.empty_like(o) for o in outs]
+    def alt_plan_leg(create):
+        """Another plan of the same tree on the same kernels, inputs and
+        copies, timed the same way; returns (step us, max |diff| vs DeFT)."""
+        plan2 = create(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens)
+        pb2, wb2 = D.deft_plan_device_bytes(plan2, desc)
+        dev2 = torch.empty(max(pb2, 256), dtype=torch.uint8, device=dev)
+        ws2 = torch.empty(max(wb2, 256), dtype=torch.uint8, device=dev)
+        D.deft_plan_upload(plan2, desc, dev2)
+        outs2 = [torch.empty_like(o) for o in outs]
 
-    def qc_step(i):
-        r = i % copies
-        D.deft_tree_attention(qs[r], kc, vc, bts[r], qc_plan, qc_outs[r], desc, qc_ws)
+        def step2(i):
+            r = i % copies
+            D.deft_tree_attention(qs[r], kc, vc, bts[r], plan2, outs2[r], desc, ws2)
 
-    for i in range(copies):
-        qc_step(i)
-    torch.cuda.synchronize()
-    qc_err = max(float((qc_outs[r].float() - eager[r].float()).abs().max()) for r in range(copies))
-    g_qc = torch.cuda.CUDAGraph()
-    s_qc = torch.cuda.Stream()
-    s_qc.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.graph(g_qc, stream=s_qc):
-        for i in range(args.steps):
-            qc_step(i)
-    torch.cuda.synchronize()
-    _, qc_ms = timed(g_qc)
-    del g_qc
+        for i in range(copies):
+            step2(i)
+        torch.cuda.synchronize()
+        err = max(float((outs2[r].float() - eager[r].float()).abs().max()) for r in range(copies))
+        g2 = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g2, stream=s2):
+            for i in range(args.steps):
+                step2(i)
+        torch.cuda.synchronize()
+        _, ms2 = timed(g2)
+        del g2
+        return ms2 * 1e3 / args.steps, err, D.deft_plan_export(plan2)
+
+    # Query-centric baseline: every query streams its own root-to-node path
+    # (no KV-Guided Grouping).  Node granularity: chunks never cross a node.
+    qc_us, qc_err, _ = alt_plan_leg(D.deft_plan_create_query_centric)
+    nc_us, nc_err, nc_info = alt_plan_leg(D.deft_plan_create_node_chunks)
     copies_saved = copies
     copies = 1                        # warm: the same copy every step, labelled as such
     g_warm = capture("both", 0, args.steps)
@@ -378,10 +385,16 @@ def main():
         "merge_kernel_us_mean": mean_merge,
         "fused_single_dispatch_step_us": fused_ms * 1e3 / args.steps,
         "query_centric_baseline": {
-            "step_us": qc_ms * 1e3 / args.steps,
+            "step_us": qc_us,
             "kv_bytes_read_ideal": naive_kv,
-            "deft_speedup": (qc_ms * 1e3 / args.steps) / (ev_ms * 1e3 / args.steps),
+            "deft_speedup": qc_us / (ev_ms * 1e3 / args.steps),
             "max_abs_diff_vs_deft": qc_err,
+        },
+        "node_granularity": {
+            "step_us": nc_us,
+            "num_chunks": nc_info["num_chunks"],
+            "deft_speedup": nc_us / (ev_ms * 1e3 / args.steps),
+            "max_abs_diff_vs_deft": nc_err,
         },
         "warm_step_us": warm_ms * 1e3 / args.steps,
         "planner_host_us_median": float(np.median(plan_times) * 1e6),

@@ -168,6 +168,22 @@ int deft_plan_create_query_centric(const int32_t* parents, const int32_t* seg_le
                                    const int32_t* query_nodes, int32_t num_queries,
                                    int32_t chunk_tokens, deft_plan** out_plan);
 
+/*
+ * Node-granularity plan, the ablation of Flattened Tree KV Splitting (the
+ * Guide's "2. Flattened Tree KV Splitting" sets its equal flat chunks against
+ * node-sized work units): the same depth-first flat layout as
+ * deft_plan_create, but every node's segment is cut into chunk_tokens
+ * windows from its own start, so no chunk crosses a node boundary and only
+ * nodes longer than chunk_tokens are split.  A chunk's group is every query
+ * whose root-to-node path holds the chunk's node (ascending), each slot with
+ * all of the chunk's bits set; chunk_full is 1 for every chunk with a group.
+ * Same arguments and errors as deft_plan_create; results of the attention
+ * calls are those of the tree plan up to rounding.
+ */
+int deft_plan_create_node_chunks(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                                 const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
+                                 deft_plan** out_plan);
+
 /* Free a plan (NULL is ignored).  The caller must first let every stream that
  * consumes its device image get past that work. */
 void deft_plan_destroy(deft_plan* plan);

@@ -223,3 +223,60 @@ def ref_plan_query_centric(parents, seg_lens, query_nodes, chunk_tokens: int) ->
         "query_slots": i32(np.arange(nc)),
     })
     return out
+
+
+def ref_plan_node_chunks(parents, seg_lens, query_nodes, chunk_tokens: int) -> dict:
+    """Node-granularity grouping (the ablation of Flattened Tree KV
+    Splitting; the Guide's "2. Flattened Tree KV Splitting" contrasts it with
+    node-sized work units): the tree plan's depth-first flat layout, but
+    every node's segment is cut into chunk_tokens windows from its own start,
+    so no chunk crosses a node boundary.  A chunk's group is every query whose
+    root-to-node path holds the chunk's node, ascending, each slot with all of
+    the chunk's bits set; the merge lists follow.
+    """
+    tree = ref_plan(parents, seg_lens, query_nodes, chunk_tokens)
+    parents = np.asarray(parents, dtype=np.int64)
+    seg_lens = np.asarray(seg_lens, dtype=np.int64)
+    query_nodes = np.asarray(query_nodes, dtype=np.int64)
+    n, nq, c = parents.shape[0], query_nodes.shape[0], int(chunk_tokens)
+    words = -(-c // 32)
+    sees = [set() for _ in range(n)]          # queries whose path holds node x
+    for qi in range(nq):
+        x = int(query_nodes[qi])
+        while x >= 0:
+            sees[x].add(qi)
+            x = int(parents[x])
+    chunk_start, group_offsets, slot_query, rows, full = [], [0], [], [], []
+    for x in tree["flat_node_order"]:
+        x = int(x)
+        a0 = int(tree["node_flat_start"][x])
+        for a in range(0, int(seg_lens[x]), c):
+            length = min(c, int(seg_lens[x]) - a)
+            chunk_start.append(a0 + a)
+            members = sorted(sees[x])
+            for qi in members:
+                bits = np.zeros(words * 32, dtype=np.uint8)
+                bits[:length] = 1
+                rows.append(np.packbits(bits, bitorder="little").view("<u4"))
+                slot_query.append(qi)
+            group_offsets.append(group_offsets[-1] + len(members))
+            full.append(1 if members else 0)
+    chunk_start.append(int(tree["total_tokens"]))
+    s_tot = len(slot_query)
+    query_slots = [s for qi in range(nq) for s in range(s_tot) if slot_query[s] == qi]
+    qso = np.concatenate([[0], np.cumsum(np.bincount(np.asarray(slot_query, dtype=np.int64), minlength=nq))])
+    i32 = lambda v: np.asarray(v, dtype=np.int64).astype(np.int32)
+    out = dict(tree)
+    out.update({
+        "num_chunks": len(chunk_start) - 1,
+        "num_slots": s_tot,
+        "mask_words": words,
+        "chunk_start": i32(chunk_start),
+        "group_offsets": i32(group_offsets),
+        "slot_query": i32(slot_query),
+        "slot_mask": (np.stack(rows) if s_tot else np.zeros((0, words), "<u4")).astype(np.uint32),
+        "chunk_full": np.asarray(full, dtype=np.uint8),
+        "query_slot_offsets": i32(qso),
+        "query_slots": i32(query_slots),
+    })
+    return out

@@ -244,6 +244,28 @@ def test_query_centric_baseline_matches_oracle(cfg):
         _rms_check(got, want, "query-centric")
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_node_granularity_plan_matches_oracle(cfg):
+    """Node-granularity chunks (no chunk crosses a node) on the same kernels
+    give the same attention as the oracle."""
+    wl = W.standard_workload(cfg)
+    say("node granularity", cfg)
+    q, kc, vc, bt = gpu_inputs(wl)
+    desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    from tree_structured_decode_amd.runner import TreeAttention
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens, desc, device=DEV,
+                       node_chunks=True)
+    ta.workspace.view(torch.float32).fill_(float("nan"))
+    out = torch.full_like(q, float("nan"))
+    ta(q, kc, vc, bt, out)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    want = oracle_out(wl)
+    check_close(got, want, TOL[wl.dtype], "node granularity")
+    if wl.dtype == torch.bfloat16:
+        _rms_check(got, want, "node granularity")
+
+
 def test_single_node_single_query_and_duplicates():
     for parents, seg, qn in [([-1], [1], [0]), ([-1], [17], [0, 0, 0]), ([-1, 0, 0], [5, 1, 1], [0, 1, 2, 1])]:
         for dtype in (torch.float32, torch.bfloat16):

@@ -8,7 +8,7 @@ import pytest
 import torch
 from hypothesis import given, settings, strategies as st
 
-from oracle.plan import PlanError, ref_plan, ref_plan_query_centric
+from oracle.plan import PlanError, ref_plan, ref_plan_node_chunks, ref_plan_query_centric
 from tree_structured_decode_amd import deft as D
 from tree_structured_decode_amd import workloads as W
 
@@ -71,6 +71,26 @@ def test_query_centric_random_trees_bit_exact(seed):
     c = int(rng.choice([1, 16, 33, 128]))
     native = D.deft_plan_export(D.deft_plan_create_query_centric(p, s, qn, c))
     assert_same_plan(native, ref_plan_query_centric(p, s, qn, c))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_node_chunks_bit_exact(cfg):
+    wl = W.standard_workload(cfg)
+    for c in sorted({wl.chunk_tokens, 100, 256}):
+        native = D.deft_plan_export(D.deft_plan_create_node_chunks(wl.parents, wl.seg_lens,
+                                                                   wl.query_nodes, c))
+        assert_same_plan(native, ref_plan_node_chunks(wl.parents, wl.seg_lens, wl.query_nodes, c))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_node_chunks_random_trees_bit_exact(seed):
+    rng = np.random.default_rng(8000 + seed)
+    n = int(rng.integers(1, 40))
+    p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([1, 5, 70])), int(rng.integers(1, 12)),
+                             forest_prob=float(rng.choice([0.0, 0.3])))
+    c = int(rng.choice([1, 16, 33, 128]))
+    native = D.deft_plan_export(D.deft_plan_create_node_chunks(p, s, qn, c))
+    assert_same_plan(native, ref_plan_node_chunks(p, s, qn, c))
 
 
 @pytest.mark.parametrize("c", [1, 7, 16, 64, 100, 128, 256, 512])

@@ -6,7 +6,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle.plan import PlanError, ref_plan, ref_plan_query_centric
+from oracle.plan import PlanError, ref_plan, ref_plan_node_chunks, ref_plan_query_centric
 from tree_structured_decode_amd import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -170,3 +170,37 @@ def test_query_centric_plan_covers_each_path_once(seed):
             assert 1 <= cs[k + 1] - cs[k] <= c
             nbits = sum(bin(int(w)).count("1") for w in plan["slot_mask"][k])
             assert nbits == cs[k + 1] - cs[k]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_node_chunk_plan_invariants(seed):
+    """Node-granularity chunks: the tree plan's flat layout; no chunk crosses
+    a node (each chunk lies in one node's flat interval, at most C long);
+    every query's slots cover exactly its visible tokens (closure ancestor
+    sets), once each; every slot row is all ones."""
+    rng = np.random.default_rng(9300 + seed)
+    n = int(rng.integers(1, 30))
+    p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([1, 4, 40])), int(rng.integers(1, 9)),
+                             forest_prob=float(rng.choice([0.0, 0.4])))
+    c = int(rng.choice([1, 5, 32, 64]))
+    plan = ref_plan_node_chunks(p, s, qn, c)
+    tree = ref_plan(p, s, qn, c)
+    assert (plan["flat_to_logical"] == tree["flat_to_logical"]).all()
+    anc = _ancestor_sets(p)
+    starts = np.concatenate([[0], np.cumsum(s)])
+    cs, go, f2l = plan["chunk_start"], plan["group_offsets"], plan["flat_to_logical"]
+    nfs = tree["node_flat_start"]
+    for k in range(plan["num_chunks"]):
+        a, b = int(cs[k]), int(cs[k + 1])
+        assert 1 <= b - a <= c
+        owners = [x for x in range(len(p)) if nfs[x] <= a and b <= nfs[x] + s[x]]
+        assert len(owners) == 1
+    for qi, node in enumerate(qn):
+        want = sorted(t for x in anc[int(node)] for t in range(starts[x], starts[x + 1]))
+        got = []
+        for si in plan["query_slots"][plan["query_slot_offsets"][qi]:plan["query_slot_offsets"][qi + 1]]:
+            k = int(np.searchsorted(go, si, side="right") - 1)
+            assert plan["slot_query"][si] == qi
+            got += [int(t) for t in f2l[cs[k]:cs[k + 1]]]
+            assert sum(bin(int(w)).count("1") for w in plan["slot_mask"][si]) == cs[k + 1] - cs[k]
+        assert sorted(got) == want and len(got) == len(set(got))

@@ -228,6 +228,71 @@ static int build_query_centric(deft_plan* p, const int32_t* parents, const int32
   return DEFT_OK;
 }
 
+// Node-granularity plan (ablation of Flattened Tree KV Splitting): the same
+// depth-first flat layout, but chunks never cross a node boundary; each
+// node's segment is cut into chunk_tokens windows from its own start (only
+// nodes longer than chunk_tokens are split).  A chunk's group is every query
+// whose path holds the chunk's node, in ascending query index, each with all
+// bits of the chunk set.
+static int build_node_chunks(deft_plan* p, const int32_t* parents, const int32_t* seg_lens,
+                             int32_t n, const int32_t* query_nodes, int32_t nq, int32_t c) {
+  int rc = build_plan(p, parents, seg_lens, n, query_nodes, nq, c);   // flat layout
+  if (rc) return rc;
+  // chunk list in flat order, and the first chunk of every node
+  std::vector<int32_t> node_first_chunk(n, 0);
+  p->chunk_start.clear();
+  for (int32_t x : p->flat_node_order) {
+    node_first_chunk[x] = static_cast<int32_t>(p->chunk_start.size());
+    for (int32_t a = 0; a < seg_lens[x]; a += c) p->chunk_start.push_back(p->node_flat_start[x] + a);
+  }
+  const int32_t nc = static_cast<int32_t>(p->chunk_start.size());
+  p->chunk_start.push_back(p->total_tokens);
+  auto n_chunks_of = [&](int32_t x) { return (seg_lens[x] + c - 1) / c; };
+  // slots: chunk by chunk, its node's queries ascending
+  std::vector<std::vector<int32_t>> node_queries(n);
+  std::vector<int32_t> path;
+  for (int32_t q = 0; q < nq; ++q)
+    for (int32_t x = query_nodes[q]; x >= 0; x = parents[x]) node_queries[x].push_back(q);
+  const int32_t words = (c + 31) / 32;
+  p->group_offsets.assign(nc + 1, 0);
+  for (int32_t x : p->flat_node_order)
+    for (int32_t k = 0; k < n_chunks_of(x); ++k)
+      p->group_offsets[node_first_chunk[x] + k + 1] = static_cast<int32_t>(node_queries[x].size());
+  for (int32_t k = 0; k < nc; ++k) p->group_offsets[k + 1] += p->group_offsets[k];
+  const int32_t S = p->group_offsets[nc];
+  p->slot_query.assign(S, 0);
+  p->slot_mask.assign(static_cast<size_t>(S) * words, 0u);
+  p->chunk_full.assign(nc, 0);
+  for (int32_t x : p->flat_node_order)
+    for (int32_t k = 0; k < n_chunks_of(x); ++k) {
+      const int32_t ch = node_first_chunk[x] + k;
+      const int32_t len = p->chunk_start[ch + 1] - p->chunk_start[ch];
+      for (size_t j = 0; j < node_queries[x].size(); ++j) {
+        const int32_t s = p->group_offsets[ch] + static_cast<int32_t>(j);
+        p->slot_query[s] = node_queries[x][j];
+        uint32_t* row = &p->slot_mask[static_cast<size_t>(s) * words];
+        for (int32_t w = 0; w < words; ++w) {
+          const int32_t bits = std::min(32, std::max(0, len - 32 * w));
+          row[w] = bits == 32 ? 0xffffffffu : ((1u << bits) - 1u);
+        }
+      }
+      p->chunk_full[ch] = node_queries[x].empty() ? 0 : 1;
+    }
+  // merge lists: each query's slots in ascending chunk (= slot) order
+  p->query_slot_offsets.assign(nq + 1, 0);
+  for (int32_t s = 0; s < S; ++s) p->query_slot_offsets[p->slot_query[s] + 1]++;
+  for (int32_t q = 0; q < nq; ++q) p->query_slot_offsets[q + 1] += p->query_slot_offsets[q];
+  p->query_slots.assign(S, 0);
+  {
+    std::vector<int32_t> fill(p->query_slot_offsets.begin(), p->query_slot_offsets.end() - 1);
+    for (int32_t s = 0; s < S; ++s) p->query_slots[fill[p->slot_query[s]]++] = s;
+  }
+  p->num_chunks = nc;
+  p->num_slots = S;
+  p->mask_words = words;
+  return DEFT_OK;
+}
+
 int check_desc(const deft_plan* p, const deft_attn_desc* d) {
   if (!d) return fail(DEFT_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->page_size < 1 ||
@@ -322,9 +387,11 @@ using deft::fail;
 
 extern "C" {
 
+enum class PlanKind { kFlat, kQueryCentric, kNodeChunks };
+
 static int plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
                        const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
-                       bool query_centric, deft_plan** out_plan) {
+                       PlanKind kind, deft_plan** out_plan) {
   deft::set_error("");
   if (!out_plan) return fail(DEFT_ERR_INVALID_ARGUMENT, "out_plan is NULL");
   *out_plan = nullptr;
@@ -350,9 +417,12 @@ static int plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t 
   if (!p) return fail(DEFT_ERR_NO_MEMORY, "host allocation failed");
   int rc;
   try {
-    rc = query_centric
-             ? deft::build_query_centric(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens)
-             : deft::build_plan(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens);
+    if (kind == PlanKind::kQueryCentric)
+      rc = deft::build_query_centric(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens);
+    else if (kind == PlanKind::kNodeChunks)
+      rc = deft::build_node_chunks(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens);
+    else
+      rc = deft::build_plan(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens);
   } catch (const std::bad_alloc&) {
     rc = fail(DEFT_ERR_NO_MEMORY, "host allocation failed while planning");
   }
@@ -367,13 +437,22 @@ static int plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t 
 int deft_plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
                      const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
                      deft_plan** out_plan) {
-  return plan_create(parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens, false, out_plan);
+  return plan_create(parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens, PlanKind::kFlat,
+                     out_plan);
 }
 
 int deft_plan_create_query_centric(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
                                    const int32_t* query_nodes, int32_t num_queries,
                                    int32_t chunk_tokens, deft_plan** out_plan) {
-  return plan_create(parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens, true, out_plan);
+  return plan_create(parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens,
+                     PlanKind::kQueryCentric, out_plan);
+}
+
+int deft_plan_create_node_chunks(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                                 const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
+                                 deft_plan** out_plan) {
+  return plan_create(parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens,
+                     PlanKind::kNodeChunks, out_plan);
 }
 
 void deft_plan_destroy(deft_plan* plan) { delete plan; }

@@ -32,7 +32,8 @@ DEFT_PARTIAL_F32 = 0
 DEFT_PARTIAL_BF16_NORM = 1
 
 EXPORTED_SYMBOLS = (
-    "deft_plan_create", "deft_plan_create_query_centric", "deft_plan_destroy", "deft_plan_export", "deft_plan_device_bytes",
+    "deft_plan_create", "deft_plan_create_query_centric", "deft_plan_create_node_chunks",
+    "deft_plan_destroy", "deft_plan_export", "deft_plan_device_bytes",
     "deft_plan_upload", "deft_tree_attention", "deft_tree_attention_fused", "deft_partial_attention",
     "deft_lse_merge", "deft_last_error",
 )
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
     L.deft_plan_create.argtypes = [_I32P, _I32P, ctypes.c_int32, _I32P, ctypes.c_int32,
                                    ctypes.c_int32, ctypes.POINTER(_P)]
     L.deft_plan_create_query_centric.argtypes = L.deft_plan_create.argtypes
+    L.deft_plan_create_node_chunks.argtypes = L.deft_plan_create.argtypes
     L.deft_plan_destroy.argtypes = [_P]
     L.deft_plan_destroy.restype = None
     L.deft_plan_export.argtypes = [_P, ctypes.POINTER(deft_plan_view)]
@@ -92,7 +94,8 @@ def lib() -> ctypes.CDLL:
     L.deft_lse_merge.argtypes = [_P, ctypes.POINTER(deft_attn_desc), _P, _P, _P, ctypes.c_int32,
                                  _P, _P]
     L.deft_last_error.restype = ctypes.c_char_p
-    for name in ("deft_plan_create", "deft_plan_create_query_centric", "deft_plan_export",
+    for name in ("deft_plan_create", "deft_plan_create_query_centric", "deft_plan_create_node_chunks",
+                 "deft_plan_export",
                  "deft_plan_device_bytes", "deft_plan_upload",
                  "deft_tree_attention", "deft_tree_attention_fused", "deft_partial_attention",
                  "deft_lse_merge"):
@@ -157,6 +160,14 @@ def deft_plan_create_query_centric(parents, seg_lens, query_nodes, chunk_tokens:
     h = _P()
     _check(lib().deft_plan_create_query_centric(_ptr_i32(p), _ptr_i32(s), int(p.shape[0]), _ptr_i32(q),
                                                 int(q.shape[0]), int(chunk_tokens), ctypes.byref(h)))
+    return Plan(h)
+
+
+def deft_plan_create_node_chunks(parents, seg_lens, query_nodes, chunk_tokens: int) -> Plan:
+    p, s, q = _i32(parents), _i32(seg_lens), _i32(query_nodes)
+    h = _P()
+    _check(lib().deft_plan_create_node_chunks(_ptr_i32(p), _ptr_i32(s), int(p.shape[0]), _ptr_i32(q),
+                                              int(q.shape[0]), int(chunk_tokens), ctypes.byref(h)))
     return Plan(h)
 
 

@@ -15,9 +15,10 @@ class TreeAttention:
     """
 
     def __init__(self, parents, seg_lens, query_nodes, chunk_tokens: int, desc, device="cuda",
-                 stream=None, query_centric: bool = False):
+                 stream=None, query_centric: bool = False, node_chunks: bool = False):
         self.desc = desc
-        create = D.deft_plan_create_query_centric if query_centric else D.deft_plan_create
+        create = (D.deft_plan_create_query_centric if query_centric else
+                  D.deft_plan_create_node_chunks if node_chunks else D.deft_plan_create)
         self.plan = create(parents, seg_lens, query_nodes, chunk_tokens)
         plan_bytes, ws_bytes = D.deft_plan_device_bytes(self.plan, desc)
         self.plan_bytes, self.workspace_bytes = plan_bytes, ws_bytes
