@@ -44,10 +44,11 @@ def source_hash() -> str:
     return h.hexdigest()[:12]
 
 
-def path_lengths(parents, seg_lens, query_nodes):
+def path_lengths(parents, seg_lens, query_nodes, query_lens=None):
+    """Tokens each query attends to (its own node cut to query_lens if given)."""
     out = []
-    for x in query_nodes:
-        t = 0
+    for i, x in enumerate(query_nodes):
+        t = 0 if query_lens is None else int(query_lens[i]) - int(seg_lens[x])
         while x >= 0:
             t += int(seg_lens[x])
             x = int(parents[x])
@@ -83,7 +84,7 @@ def cpu_baseline(wl, budget_s: float):
     nq = wl.num_queries
     t0 = time.perf_counter()
     OA.tree_attention(wl.q, kp, vp, wl.block_table, wl.parents, wl.seg_lens, wl.query_nodes,
-                      page_ids=ids, queries=[0])
+                      page_ids=ids, queries=[0], query_lens=wl.query_lens)
     one = time.perf_counter() - t0
     nsamp = int(max(1, min(nq, budget_s / max(one, 1e-6))))
     sample = list(np.linspace(0, nq - 1, nsamp).round().astype(int))
@@ -91,7 +92,7 @@ def cpu_baseline(wl, budget_s: float):
     t0 = time.perf_counter()
     while True:
         OA.tree_attention(wl.q, kp, vp, wl.block_table, wl.parents, wl.seg_lens, wl.query_nodes,
-                          page_ids=ids, queries=sample)
+                          page_ids=ids, queries=sample, query_lens=wl.query_lens)
         reps += 1
         elapsed = time.perf_counter() - t0
         if elapsed >= budget_s or (nsamp < nq and reps >= 1):
@@ -178,7 +179,11 @@ def main():
     plan_times = []
     for _ in range(20):
         t0 = time.perf_counter()
-        plan = D.deft_plan_create(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens)
+        if wl.query_lens is None:
+            plan = D.deft_plan_create(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens)
+        else:
+            plan = D.deft_plan_create_multi_token(wl.parents, wl.seg_lens, wl.query_nodes, wl.query_lens,
+                                                  wl.chunk_tokens)
         plan_times.append(time.perf_counter() - t0)
     plan_bytes, ws_bytes = D.deft_plan_device_bytes(plan, desc)
     dev_plan = torch.empty(plan_bytes, dtype=torch.uint8, device=dev)
@@ -311,8 +316,10 @@ def main():
 
     # Query-centric baseline: every query streams its own root-to-node path
     # (no KV-Guided Grouping).  Node granularity: chunks never cross a node.
-    qc_us, qc_err, _ = alt_plan_leg(D.deft_plan_create_query_centric)
-    nc_us, nc_err, nc_info = alt_plan_leg(D.deft_plan_create_node_chunks)
+    # (Both take whole nodes only, so multi-token query nodes skip them.)
+    alt = wl.query_lens is None
+    qc_us, qc_err, _ = alt_plan_leg(D.deft_plan_create_query_centric) if alt else (None, None, None)
+    nc_us, nc_err, nc_info = alt_plan_leg(D.deft_plan_create_node_chunks) if alt else (None, None, None)
     copies_saved = copies
     copies = 1                        # warm: the same copy every step, labelled as such
     g_warm = capture("both", 0, args.steps)
@@ -323,7 +330,7 @@ def main():
 
     ms_per_step = wall / args.steps * 1e3
     latency_us = ms_per_step * 1e3
-    paths = path_lengths(wl.parents, wl.seg_lens, wl.query_nodes)
+    paths = path_lengths(wl.parents, wl.seg_lens, wl.query_nodes, wl.query_lens)
     flops = 4.0 * d * hq * float(sum(paths))
     naive_kv = float(sum(paths)) * 2 * hkv * d * eb
     part_bytes = S * hq * (d * (2 if wl.dtype == torch.bfloat16 else 4) + 8)
@@ -331,7 +338,8 @@ def main():
     mean_part = part_ms * 1e3 / args.steps
     mean_merge = merge_ms * 1e3 / args.steps
     dominant = "partial" if mean_part >= mean_merge else "merge"
-    mfma_bound = args.workload == 5
+    # the bound whose time floor is larger: matrix-core flops or HBM bytes
+    mfma_bound = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > (kv_bytes + q_bytes) / (HBM_PEAK_GBS * 1e9)
     if dominant == "partial":
         if mfma_bound:
             achieved = flops / (mean_part * 1e-6) / 1e12
@@ -384,13 +392,13 @@ def main():
         "partial_kernel_us_mean": mean_part,
         "merge_kernel_us_mean": mean_merge,
         "fused_single_dispatch_step_us": fused_ms * 1e3 / args.steps,
-        "query_centric_baseline": {
+        "query_centric_baseline": None if qc_us is None else {
             "step_us": qc_us,
             "kv_bytes_read_ideal": naive_kv,
             "deft_speedup": qc_us / (ev_ms * 1e3 / args.steps),
             "max_abs_diff_vs_deft": qc_err,
         },
-        "node_granularity": {
+        "node_granularity": None if nc_us is None else {
             "step_us": nc_us,
             "num_chunks": nc_info["num_chunks"],
             "deft_speedup": nc_us / (ev_ms * 1e3 / args.steps),

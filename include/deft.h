@@ -184,6 +184,25 @@ int deft_plan_create_node_chunks(const int32_t* parents, const int32_t* seg_lens
                                  const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
                                  deft_plan** out_plan);
 
+/*
+ * Tree plan with multi-token query nodes (tree prefill, speculative nodes
+ * holding several draft tokens).  The pages' mask (DeFT Guide, "Deep Dive:
+ * Mathematical Formulation", "Tree-Constrained Attention Formulation") is
+ * defined by ancestry alone; the causal rule inside one node is a reading
+ * that keeps ordinary causal attention along a chain: query q sits at a
+ * position inside its node and sees its ancestors' segments plus the first
+ * query_lens[q] tokens of its own node (it sees its own token).  Grouping,
+ * flattening and chunking are those of deft_plan_create; a chunk's group
+ * holds only the queries that see at least one of its tokens.
+ *   query_lens  host int32 [num_queries], each in [1, seg_lens[query_nodes[q]]];
+ *               NULL means the whole segment (exactly deft_plan_create).
+ * Errors: those of deft_plan_create; DEFT_ERR_INVALID_TREE for a query_lens
+ * entry outside its range.
+ */
+int deft_plan_create_multi_token(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                                 const int32_t* query_nodes, const int32_t* query_lens,
+                                 int32_t num_queries, int32_t chunk_tokens, deft_plan** out_plan);
+
 /* Free a plan (NULL is ignored).  The caller must first let every stream that
  * consumes its device image get past that work. */
 void deft_plan_destroy(deft_plan* plan);

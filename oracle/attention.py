@@ -17,6 +17,14 @@ Readings where the pages leave a point open:
   * no epsilon in the normalisation (the simulator adds 1e-8; the formula
     does not, and the denominator is at least 1 after max subtraction).
 
+Multi-token query nodes (tree prefill, speculative nodes that hold several
+draft tokens): the pages define M_i only by ancestry, so the plainest reading
+that keeps ordinary causal attention inside one node is taken: a query may sit
+at a position inside its node and then sees the ancestors' segments and its
+own node's tokens up to and including its position (query_lens[i] leading
+tokens of the node).  With query_lens[i] = seg_lens[node] this is the decode
+case above.
+
 Paged KV ("Production Engineering ... Integration with Paged KV Caches"):
 logical token t lives in pool page block_table[t // page_size], row
 t % page_size.  Logical order is node segments concatenated in node-id order.
@@ -51,14 +59,22 @@ def path_nodes(parents, node: int) -> list:
     return out
 
 
-def path_tokens(parents, seg_lens, node: int) -> np.ndarray:
-    """Logical token ids visible to a query on `node` (root segment first)."""
+def path_tokens(parents, seg_lens, node: int, own_len=None) -> np.ndarray:
+    """Logical token ids visible to a query on `node` (root segment first).
+
+    own_len: how many leading tokens of `node` itself the query sees (None:
+    the whole segment)."""
     starts = node_starts(seg_lens)
     nodes = path_nodes(parents, node)[::-1]
     if not nodes:
         return np.zeros(0, dtype=np.int64)
-    return np.concatenate([np.arange(starts[n], starts[n] + int(seg_lens[n]), dtype=np.int64)
-                           for n in nodes])
+    lens = [int(seg_lens[n]) for n in nodes]
+    if own_len is not None:
+        if not 1 <= int(own_len) <= lens[-1]:
+            raise ValueError("own_len must lie in [1, seg_lens[node]]")
+        lens[-1] = int(own_len)
+    return np.concatenate([np.arange(starts[n], starts[n] + ln, dtype=np.int64)
+                           for n, ln in zip(nodes, lens)])
 
 
 def gather_tokens(pool, tokens, block_table, page_size=16, page_ids=None) -> np.ndarray:
@@ -91,11 +107,12 @@ def attend(qh: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.nda
 
 
 def tree_attention(q, k_pool, v_pool, block_table, parents, seg_lens, query_nodes,
-                   page_size: int = 16, page_ids=None, queries=None) -> np.ndarray:
+                   page_size: int = 16, page_ids=None, queries=None, query_lens=None) -> np.ndarray:
     """Reference output [len(queries), Hq, d] in fp64.
 
     q: [Nq, Hq, d]; k_pool, v_pool: [P', page_size, Hkv, d]; queries: indices
-    into query_nodes to evaluate (default all of them).
+    into query_nodes to evaluate (default all of them); query_lens: per query,
+    the leading tokens of its own node it sees (None: every token).
     """
     q = _as_f64(q)
     kp, vp = _as_f64(k_pool), _as_f64(v_pool)
@@ -108,7 +125,8 @@ def tree_attention(q, k_pool, v_pool, block_table, parents, seg_lens, query_node
     sel = range(nq) if queries is None else queries
     out = []
     for i in sel:
-        toks = path_tokens(parents, seg_lens, int(query_nodes[i]))
+        own = None if query_lens is None else int(query_lens[i])
+        toks = path_tokens(parents, seg_lens, int(query_nodes[i]), own)
         k = gather_tokens(kp, toks, block_table, page_size, page_ids)
         v = gather_tokens(vp, toks, block_table, page_size, page_ids)
         o = np.empty((hq, d))
@@ -151,12 +169,13 @@ def lse_merge(os_, ms, ls) -> np.ndarray:
 
 
 def chunk_partials(q, k_pool, v_pool, block_table, parents, seg_lens, query_nodes, plan,
-                   page_size: int = 16, page_ids=None):
+                   page_size: int = 16, page_ids=None, query_lens=None):
     """Per-slot partials over the chunks of a reference plan.
 
-    For slot s (chunk c, query qi): the chunk's flat tokens whose node lies
-    on qi's path, mapped to logical ids by the plan's flattening.  Visibility
-    comes from the path walk, not from the plan's bitmasks.
+    For slot s (chunk c, query qi): the chunk's flat tokens that qi sees (the
+    path tokens of path_tokens), mapped to logical ids by the plan's
+    flattening.  Visibility comes from the path walk, not from the plan's
+    bitmasks.
     Returns O [S, Hq, d], m [S, Hq], l [S, Hq] in fp64.
     """
     q = _as_f64(q)
@@ -165,11 +184,6 @@ def chunk_partials(q, k_pool, v_pool, block_table, parents, seg_lens, query_node
     hkv = kp.shape[2]
     grp = hq // hkv
     scale = 1.0 / np.sqrt(d)
-    n = len(parents)
-    flat_node = np.empty(int(np.sum(seg_lens, dtype=np.int64)), dtype=np.int64)
-    for node in range(n):
-        a = int(plan["node_flat_start"][node])
-        flat_node[a:a + int(seg_lens[node])] = node
     f2l = plan["flat_to_logical"].astype(np.int64)
     cs = plan["chunk_start"]
     go = plan["group_offsets"]
@@ -182,9 +196,9 @@ def chunk_partials(q, k_pool, v_pool, block_table, parents, seg_lens, query_node
         f = np.arange(int(cs[c]), int(cs[c + 1]), dtype=np.int64)
         for s in range(int(go[c]), int(go[c + 1])):
             qi = int(sq[s])
-            on_path = np.zeros(n, dtype=bool)
-            on_path[path_nodes(parents, int(query_nodes[qi]))] = True
-            toks = f2l[f[on_path[flat_node[f]]]]
+            own = None if query_lens is None else int(query_lens[qi])
+            seen = np.isin(f2l[f], path_tokens(parents, seg_lens, int(query_nodes[qi]), own))
+            toks = f2l[f[seen]]
             k = gather_tokens(kp, toks, block_table, page_size, page_ids)
             v = gather_tokens(vp, toks, block_table, page_size, page_ids)
             for g in range(hkv):

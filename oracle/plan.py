@@ -19,6 +19,11 @@ so that the native planner can be compared with it array for array:
   the chunk's t-th flat token belongs to a node on the query's root-to-node
   path (the node itself included).  Bits are packed LSB first into uint32
   words, ceil(C/32) words per row; bits past the chunk's end are zero.
+* Multi-token query nodes (a reading; the pages define the mask by ancestry
+  only): query_lens[i], when given, is how many leading tokens of its own
+  node query i sees (1 .. seg_lens[node]), the causal mask inside a node that
+  tree prefill needs; its node's later tokens are masked like another
+  branch's.  Without query_lens every query sees its whole node.
 * Merge lists: each query's (chunk, query) slots in ascending chunk order,
   the operands of its log-sum-exp merge ("3. Fused In-SRAM Online Softmax
   Merging" and "The Online Softmax Tile Accumulation").
@@ -38,7 +43,7 @@ class PlanError(ValueError):
         self.kind = kind          # "invalid_tree" or "invalid_argument"
 
 
-def ref_plan(parents, seg_lens, query_nodes, chunk_tokens: int) -> dict:
+def ref_plan(parents, seg_lens, query_nodes, chunk_tokens: int, query_lens=None) -> dict:
     parents = np.asarray(parents, dtype=np.int64)
     seg_lens = np.asarray(seg_lens, dtype=np.int64)
     query_nodes = np.asarray(query_nodes, dtype=np.int64)
@@ -56,6 +61,13 @@ def ref_plan(parents, seg_lens, query_nodes, chunk_tokens: int) -> dict:
     for qi in range(nq):
         if not (0 <= query_nodes[qi] < n):
             raise PlanError("invalid_tree", f"query_nodes[{qi}] out of range")
+    if query_lens is not None:
+        query_lens = np.asarray(query_lens, dtype=np.int64)
+        if query_lens.shape[0] != nq:
+            raise PlanError("invalid_argument", "query_lens needs one entry per query")
+        for qi in range(nq):
+            if not (1 <= query_lens[qi] <= seg_lens[query_nodes[qi]]):
+                raise PlanError("invalid_tree", f"query_lens[{qi}] must be in [1, seg_lens[node]]")
     total = int(seg_lens.sum())
     if total > INT32_MAX:
         raise PlanError("invalid_tree", "total tokens exceed int32")
@@ -88,10 +100,12 @@ def ref_plan(parents, seg_lens, query_nodes, chunk_tokens: int) -> dict:
 
     flat_to_logical = np.empty(total, dtype=np.int64)
     flat_node = np.empty(total, dtype=np.int64)
+    flat_offset = np.empty(total, dtype=np.int64)     # position inside its node
     for x in range(n):
         a = node_flat_start[x]
         flat_to_logical[a:a + seg_lens[x]] = np.arange(node_start[x], node_start[x] + seg_lens[x])
         flat_node[a:a + seg_lens[x]] = x
+        flat_offset[a:a + seg_lens[x]] = np.arange(seg_lens[x])
 
     c = int(chunk_tokens)
     n_chunks = -(-total // c)
@@ -117,6 +131,8 @@ def ref_plan(parents, seg_lens, query_nodes, chunk_tokens: int) -> dict:
         members = 0
         for qi in range(nq):
             vis = on_path[qi, nodes]
+            if query_lens is not None:
+                vis = vis & ~((nodes == query_nodes[qi]) & (flat_offset[a:b] >= query_lens[qi]))
             if not vis.any():
                 continue
             members += 1

@@ -30,7 +30,8 @@ def run_gpu(wl, chunk_tokens=None, poison_workspace=True, inputs=None):
     c = chunk_tokens or wl.chunk_tokens
     desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
     q, kc, vc, bt = inputs if inputs is not None else gpu_inputs(wl)
-    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, c, desc, device=DEV)
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, c, desc, device=DEV,
+                       query_lens=wl.query_lens)
     if poison_workspace:
         ta.workspace.view(torch.float32).fill_(float("nan"))
     out = torch.full_like(q, float("nan"))
@@ -42,7 +43,7 @@ def run_gpu(wl, chunk_tokens=None, poison_workspace=True, inputs=None):
 def oracle_out(wl, queries=None):
     ids, kp, vp = W.compact_pool(wl)
     return OA.tree_attention(wl.q, kp, vp, wl.block_table, wl.parents, wl.seg_lens, wl.query_nodes,
-                             page_ids=ids, queries=queries)
+                             page_ids=ids, queries=queries, query_lens=wl.query_lens)
 
 
 def check_close(got, want, tol, what=""):

@@ -266,6 +266,49 @@ def test_node_granularity_plan_matches_oracle(cfg):
         _rms_check(got, want, "node granularity")
 
 
+def test_multi_token_workload_matches_oracle():
+    """Multi-token query nodes (a query per draft token, causal inside its
+    node): whole output, partials of the internal format, and the
+    single-dispatch variant."""
+    wl = W.standard_workload(6)
+    say("multi-token workload")
+    q, kc, vc, bt = inputs = gpu_inputs(wl)
+    got, ta = run_gpu(wl, inputs=inputs)
+    want = oracle_out(wl)
+    check_close(got, want, TOL[wl.dtype], "multi-token")
+    _rms_check(got, want, "multi-token")
+    out = torch.full_like(q, float("nan"))
+    for _ in range(2):
+        D.deft_tree_attention_fused(q, kc, vc, bt, ta.plan, out, ta.desc, ta.workspace)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.double().cpu().numpy(), got)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("seed", range(6))
+def test_multi_token_random_trees(seed, dtype):
+    """Random trees with random positions inside the query nodes; groups big
+    enough for the matrix-core path at some chunks, single rows at others."""
+    rng = np.random.default_rng(4200 + seed)
+    n = int(rng.integers(2, 12))
+    p, s, qn = W.random_tree(rng, n, 1, 60, int(rng.integers(1, 6)), forest_prob=0.2)
+    # add a multi-token prefill of one node: a query on each of its tokens
+    x = int(rng.integers(0, n))
+    qn = np.concatenate([qn, np.full(int(s[x]), x)]).astype(np.int32)
+    ql = np.array([int(rng.integers(1, s[v] + 1)) for v in qn[:-int(s[x])]] +
+                  list(range(1, int(s[x]) + 1)), dtype=np.int32)
+    c = int(rng.choice([16, 48, 128]))
+    wl = W.make_workload("mt", p, s, qn, chunk_tokens=c, hq=8, hkv=2, d=128, dtype=dtype,
+                         seed=seed, placement="permuted", value_scale=1.0 / np.sqrt(128),
+                         query_lens=ql)
+    say("multi-token random", seed, str(dtype), "queries", len(qn), "C", c)
+    got, _ = run_gpu(wl)
+    want = oracle_out(wl)
+    check_close(got, want, TOL[dtype], "multi-token random")
+    if dtype == torch.bfloat16:
+        _rms_check(got, want, "multi-token random")
+
+
 def test_single_node_single_query_and_duplicates():
     for parents, seg, qn in [([-1], [1], [0]), ([-1], [17], [0, 0, 0]), ([-1, 0, 0], [5, 1, 1], [0, 1, 2, 1])]:
         for dtype in (torch.float32, torch.bfloat16):

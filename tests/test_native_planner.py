@@ -93,6 +93,40 @@ def test_node_chunks_random_trees_bit_exact(seed):
     assert_same_plan(native, ref_plan_node_chunks(p, s, qn, c))
 
 
+@pytest.mark.parametrize("seed", range(30))
+def test_multi_token_random_trees_bit_exact(seed):
+    rng = np.random.default_rng(8800 + seed)
+    n = int(rng.integers(1, 40))
+    p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([2, 9, 70])), int(rng.integers(1, 14)),
+                             forest_prob=float(rng.choice([0.0, 0.3])))
+    ql = np.array([int(rng.integers(1, s[x] + 1)) for x in qn], dtype=np.int32)
+    c = int(rng.choice([1, 16, 33, 128]))
+    native = D.deft_plan_export(D.deft_plan_create_multi_token(p, s, qn, ql, c))
+    assert_same_plan(native, ref_plan(p, s, qn, c, query_lens=ql))
+
+
+def test_multi_token_workload_bit_exact():
+    wl = W.standard_workload(6)
+    for c in (wl.chunk_tokens, 64, 520):
+        native = D.deft_plan_export(D.deft_plan_create_multi_token(wl.parents, wl.seg_lens, wl.query_nodes,
+                                                                   wl.query_lens, c))
+        assert_same_plan(native, ref_plan(wl.parents, wl.seg_lens, wl.query_nodes, c,
+                                          query_lens=wl.query_lens))
+
+
+def test_multi_token_null_lengths_and_errors():
+    wl = W.standard_workload(1)
+    a = D.deft_plan_export(D.deft_plan_create_multi_token(wl.parents, wl.seg_lens, wl.query_nodes, None, 64))
+    b = D.deft_plan_export(D.deft_plan_create(wl.parents, wl.seg_lens, wl.query_nodes, 64))
+    assert_same_plan(a, b)
+    for ql in ([0], [5]):
+        with pytest.raises(D.DeftError) as e:
+            D.deft_plan_create_multi_token([-1, 0], [3, 4], [1], ql, 4)
+        assert e.value.code == D.DEFT_ERR_INVALID_TREE
+    with pytest.raises(ValueError):
+        D.deft_plan_create_multi_token([-1, 0], [3, 4], [1], [1, 1], 4)
+
+
 @pytest.mark.parametrize("c", [1, 7, 16, 64, 100, 128, 256, 512])
 @pytest.mark.parametrize("seed", range(25))
 def test_random_trees_bit_exact(seed, c):

@@ -8,7 +8,10 @@
   * relabelling sibling nodes (which changes the flattening and the plan)
     leaves every query's output unchanged;
   * a brute-force scalar loop over every pool row with ancestor sets built
-    by closure (not by walking parents) agrees on tiny trees;
+    by closure (not by walking parents) agrees on tiny trees, also with
+    multi-token query nodes;
+  * one multi-token node with a query per token is causal self-attention,
+    and multi-token branches under a prefix are causal over their own path;
   * closed forms: zero keys make the softmax uniform, so the output is the
     token-count-weighted mean of per-node value patterns; constant values
     give that constant back;
@@ -97,6 +100,28 @@ def test_split_then_merge_equals_unsplit(seed):
             np.testing.assert_allclose(merged, full[i, 2 * g:2 * g + 2], rtol=1e-13, atol=1e-13)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_chunk_partials_merge_to_tree_attention(seed):
+    """Per-slot partials over a plan's chunks, merged along each query's
+    slot list, give the unsplit attention (with and without multi-token
+    query nodes); every slot holds at least one token (finite m, l > 0)."""
+    rng = np.random.default_rng(700 + seed)
+    p, s, qn = W.random_tree(rng, int(rng.integers(2, 15)), 1, 40, int(rng.integers(1, 8)), forest_prob=0.2)
+    ql = None if seed % 2 == 0 else np.array([int(rng.integers(1, s[x] + 1)) for x in qn], np.int32)
+    wl = W.make_workload("cp", p, s, qn, chunk_tokens=16, hq=4, hkv=2, d=8, dtype=torch.float32,
+                         seed=seed, placement="permuted", query_lens=ql)
+    c = int(rng.choice([3, 16, 50]))
+    plan = ref_plan(p, s, qn, c, query_lens=ql)
+    ids, kp, vp = W.compact_pool(wl)
+    o, m, l = OA.chunk_partials(wl.q, kp, vp, wl.block_table, p, s, qn, plan, page_ids=ids, query_lens=ql)
+    assert np.isfinite(m).all() and (l > 0).all()
+    full = OA.tree_attention(wl.q, kp, vp, wl.block_table, p, s, qn, page_ids=ids, query_lens=ql)
+    qso, qs = plan["query_slot_offsets"], plan["query_slots"]
+    for i in range(len(qn)):
+        sl = qs[qso[i]:qso[i + 1]]
+        np.testing.assert_allclose(OA.lse_merge(o[sl], m[sl], l[sl]), full[i], rtol=1e-12, atol=1e-12)
+
+
 def _relabel_siblings(parents, seg, queries, rng):
     """Renumber nodes breadth-first with each node's children shuffled."""
     n = len(parents)
@@ -177,6 +202,9 @@ def _brute(wl):
                     node = next(j for j, (a, b) in enumerate(bounds) if a <= t < b)
                     if node not in anc[int(wl.query_nodes[qi])]:
                         continue
+                    if (wl.query_lens is not None and node == int(wl.query_nodes[qi])
+                            and t - bounds[node][0] >= int(wl.query_lens[qi])):
+                        continue
                     dot = 0.0
                     for x in range(d):
                         dot += q[qi, h, x] * kp[row, r, g, x]
@@ -201,6 +229,55 @@ def test_brute_force_tiny_trees(seed):
     wl = W.make_workload("b", p, s, qn, chunk_tokens=4, hq=hq, hkv=hkv, d=d, dtype=torch.float32,
                          seed=seed, placement="scattered", pool_pages=int(rng.integers(2, 9)) + (-(-int(s.sum()) // 16)))
     np.testing.assert_allclose(_oracle(wl), _brute(wl), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_brute_force_tiny_trees_multi_token(seed):
+    """Multi-token query nodes: the query at position j of its node sees the
+    node's first j + 1 tokens (brute force, closure ancestor sets)."""
+    rng = np.random.default_rng(350 + seed)
+    n = int(rng.integers(1, 8))
+    p, s, qn = W.random_tree(rng, n, 1, 6, int(rng.integers(1, 6)), forest_prob=0.2)
+    ql = np.array([int(rng.integers(1, s[x] + 1)) for x in qn], dtype=np.int32)
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2]))
+    wl = W.make_workload("bm", p, s, qn, chunk_tokens=4, hq=hq, hkv=hkv, d=int(rng.choice([2, 5])),
+                         dtype=torch.float32, seed=seed, placement="permuted", query_lens=ql)
+    np.testing.assert_allclose(_oracle(wl, query_lens=ql), _brute(wl), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_one_multi_token_node_is_causal_attention(seed):
+    """A single node of L tokens with a query on each token (tree prefill of
+    one segment) is ordinary causal self-attention."""
+    L = 45
+    p, s, qn = np.array([-1]), np.array([L]), np.zeros(L, dtype=np.int32)
+    ql = np.arange(1, L + 1, dtype=np.int32)
+    wl = _wl(p, s, qn, hq=4, hkv=2, d=16, seed=seed)
+    got = _oracle(wl, query_lens=ql)
+    want = _sdpa(wl.q, wl.k_tokens, wl.v_tokens, causal=True)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_multi_token_branches_are_causal_over_their_path(seed):
+    """Prefix plus two multi-token branches: each branch's queries give the
+    last rows of causal attention over prefix ++ that branch, untouched by
+    the sibling branch."""
+    rng = np.random.default_rng(600 + seed)
+    lp, la, lb = int(rng.integers(3, 30)), int(rng.integers(2, 20)), int(rng.integers(2, 20))
+    p = np.array([-1, 0, 0], dtype=np.int32)
+    s = np.array([lp, la, lb], dtype=np.int32)
+    qn = np.array([1] * la + [2] * lb, dtype=np.int32)
+    ql = np.concatenate([np.arange(1, la + 1), np.arange(1, lb + 1)]).astype(np.int32)
+    wl = _wl(p, s, qn, hq=6, hkv=3, d=8, seed=seed, placement="scattered")
+    got = _oracle(wl, query_lens=ql)
+    for node, rows, (a, b) in ((1, slice(0, la), (lp, lp + la)), (2, slice(la, la + lb), (lp + la, lp + la + lb))):
+        kk = torch.cat([wl.k_tokens[:lp], wl.k_tokens[a:b]])
+        vv = torch.cat([wl.v_tokens[:lp], wl.v_tokens[a:b]])
+        qq = torch.cat([torch.zeros_like(wl.q[:lp]), wl.q[rows]])
+        want = _sdpa(qq, kk, vv, causal=True)[lp:]
+        np.testing.assert_allclose(got[rows], want, rtol=1e-12, atol=1e-12)
 
 
 @pytest.mark.parametrize("seed", range(5))

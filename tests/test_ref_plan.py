@@ -43,7 +43,7 @@ def _ancestor_sets(parents):
     return anc
 
 
-def check_plan_invariants(pl, parents, seg, queries, c):
+def check_plan_invariants(pl, parents, seg, queries, c, query_lens=None):
     n, nq = len(parents), len(queries)
     total = int(np.sum(seg))
     assert pl["total_tokens"] == total
@@ -75,10 +75,16 @@ def check_plan_invariants(pl, parents, seg, queries, c):
     go, sq, sm = pl["group_offsets"], pl["slot_query"], pl["slot_mask"]
     words = -(-c // 32)
     assert sm.shape == (pl["num_slots"], words)
+    own_len = list(seg[queries]) if query_lens is None else list(query_lens)
+
+    def sees(qi, f):
+        x = flat_node[f]
+        return x in anc[queries[qi]] and (x != queries[qi] or f - nfs[x] < own_len[qi])
+
     for k in range(len(cs) - 1):
         members = []
         for qi in range(nq):
-            vis = [flat_node[f] in anc[queries[qi]] for f in range(cs[k], cs[k + 1])]
+            vis = [sees(qi, f) for f in range(cs[k], cs[k + 1])]
             if any(vis):
                 members.append((qi, vis))
         assert go[k + 1] - go[k] == len(members)
@@ -96,7 +102,7 @@ def check_plan_invariants(pl, parents, seg, queries, c):
         mine = qs[qso[qi]:qso[qi + 1]].tolist()
         assert mine == sorted(mine) and all(sq[s] == qi for s in mine)
         pop = sum(bin(int(w)).count("1") for s in mine for w in sm[s])
-        assert pop == sum(seg[x] for x in anc[queries[qi]])
+        assert pop == sum(seg[x] for x in anc[queries[qi]]) - seg[queries[qi]] + own_len[qi]
     assert qso[-1] == pl["num_slots"]
 
 
@@ -108,6 +114,41 @@ def test_random_trees_against_closure(seed, c):
     p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([1, 3, 60])), int(rng.integers(1, 12)),
                              forest_prob=0.15)
     check_plan_invariants(ref_plan(p, s, qn, c), p, s, qn, c)
+
+
+@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("c", [1, 7, 32, 100])
+def test_multi_token_plans_against_closure(seed, c):
+    """Multi-token query nodes: the query sees its node's first query_lens
+    tokens; groups hold only queries that see a token of the chunk."""
+    rng = np.random.default_rng(7100 + seed * 13 + c)
+    n = int(rng.integers(1, 30))
+    p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([2, 9, 70])), int(rng.integers(1, 12)),
+                             forest_prob=0.15)
+    ql = np.array([int(rng.integers(1, s[x] + 1)) for x in qn], dtype=np.int32)
+    check_plan_invariants(ref_plan(p, s, qn, c, query_lens=ql), p, s, qn, c, query_lens=ql)
+
+
+def test_multi_token_full_lengths_are_the_tree_plan():
+    rng = np.random.default_rng(77)
+    p, s, qn = W.random_tree(rng, 25, 1, 40, 9, forest_prob=0.1)
+    a = ref_plan(p, s, qn, 16, query_lens=s[qn])
+    b = ref_plan(p, s, qn, 16)
+    for k in b:
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+
+
+def test_multi_token_workload_plan():
+    wl = W.standard_workload(6)
+    pl = ref_plan(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens, query_lens=wl.query_lens)
+    check_plan_invariants(pl, wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens,
+                          query_lens=wl.query_lens)
+
+
+def test_multi_token_rejects_bad_lengths():
+    for ql in ([0], [5], [1, 1]):
+        with pytest.raises(PlanError):
+            ref_plan([-1, 0], [3, 4], [1], 4, query_lens=ql)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])

@@ -39,8 +39,10 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
+// query_lens (may be null): leading tokens of its own node each query sees.
 static int build_plan(deft_plan* p, const int32_t* parents, const int32_t* seg_lens,
-                      int32_t n, const int32_t* query_nodes, int32_t nq, int32_t c) {
+                      int32_t n, const int32_t* query_nodes, int32_t nq, int32_t c,
+                      const int32_t* query_lens = nullptr) {
   // Logical layout: segments in node-id order.
   p->node_start.resize(n);
   int64_t run = 0;
@@ -101,7 +103,7 @@ static int build_plan(deft_plan* p, const int32_t* parents, const int32_t* seg_l
     int32_t last = -1;
     for (auto it = path.rbegin(); it != path.rend(); ++it) {
       const int64_t a = p->node_flat_start[*it];
-      const int64_t b = a + seg_lens[*it];
+      const int64_t b = a + (query_lens && *it == query_nodes[q] ? query_lens[q] : seg_lens[*it]);
       for (int64_t k = a / c; k <= (b - 1) / c; ++k) {
         if (static_cast<int32_t>(k) == last) continue;
         last = static_cast<int32_t>(k);
@@ -132,7 +134,7 @@ static int build_plan(deft_plan* p, const int32_t* parents, const int32_t* seg_l
     int32_t t = touch_off[q];
     for (auto it = path.rbegin(); it != path.rend(); ++it) {
       const int64_t a = p->node_flat_start[*it];
-      const int64_t b = a + seg_lens[*it];
+      const int64_t b = a + (query_lens && *it == query_nodes[q] ? query_lens[q] : seg_lens[*it]);
       while (t < touch_off[q + 1] && static_cast<int64_t>(touch_chunk[t] + 1) * c <= a) ++t;
       for (int32_t u = t; u < touch_off[q + 1]; ++u) {
         const int64_t cs = static_cast<int64_t>(touch_chunk[u]) * c;
@@ -391,7 +393,7 @@ enum class PlanKind { kFlat, kQueryCentric, kNodeChunks };
 
 static int plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
                        const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
-                       PlanKind kind, deft_plan** out_plan) {
+                       PlanKind kind, deft_plan** out_plan, const int32_t* query_lens = nullptr) {
   deft::set_error("");
   if (!out_plan) return fail(DEFT_ERR_INVALID_ARGUMENT, "out_plan is NULL");
   *out_plan = nullptr;
@@ -410,6 +412,10 @@ static int plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t 
   for (int32_t q = 0; q < num_queries; ++q)
     if (query_nodes[q] < 0 || query_nodes[q] >= num_nodes)
       return fail(DEFT_ERR_INVALID_TREE, "query_nodes[" + std::to_string(q) + "] out of range");
+  if (query_lens)
+    for (int32_t q = 0; q < num_queries; ++q)
+      if (query_lens[q] < 1 || query_lens[q] > seg_lens[query_nodes[q]])
+        return fail(DEFT_ERR_INVALID_TREE, "query_lens[" + std::to_string(q) + "] must be in [1, seg_lens[node]]");
   int64_t total = 0;
   for (int32_t i = 0; i < num_nodes; ++i) total += seg_lens[i];
   if (total > INT32_MAX) return fail(DEFT_ERR_INVALID_TREE, "total tokens exceed 2^31 - 1");
@@ -422,7 +428,8 @@ static int plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t 
     else if (kind == PlanKind::kNodeChunks)
       rc = deft::build_node_chunks(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens);
     else
-      rc = deft::build_plan(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens);
+      rc = deft::build_plan(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens,
+                            query_lens);
   } catch (const std::bad_alloc&) {
     rc = fail(DEFT_ERR_NO_MEMORY, "host allocation failed while planning");
   }
@@ -453,6 +460,13 @@ int deft_plan_create_node_chunks(const int32_t* parents, const int32_t* seg_lens
                                  deft_plan** out_plan) {
   return plan_create(parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens,
                      PlanKind::kNodeChunks, out_plan);
+}
+
+int deft_plan_create_multi_token(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                                 const int32_t* query_nodes, const int32_t* query_lens,
+                                 int32_t num_queries, int32_t chunk_tokens, deft_plan** out_plan) {
+  return plan_create(parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens, PlanKind::kFlat,
+                     out_plan, query_lens);
 }
 
 void deft_plan_destroy(deft_plan* plan) { delete plan; }

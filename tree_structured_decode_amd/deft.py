@@ -33,7 +33,7 @@ DEFT_PARTIAL_BF16_NORM = 1
 
 EXPORTED_SYMBOLS = (
     "deft_plan_create", "deft_plan_create_query_centric", "deft_plan_create_node_chunks",
-    "deft_plan_destroy", "deft_plan_export", "deft_plan_device_bytes",
+    "deft_plan_create_multi_token", "deft_plan_destroy", "deft_plan_export", "deft_plan_device_bytes",
     "deft_plan_upload", "deft_tree_attention", "deft_tree_attention_fused", "deft_partial_attention",
     "deft_lse_merge", "deft_last_error",
 )
@@ -80,6 +80,10 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_int32, ctypes.POINTER(_P)]
     L.deft_plan_create_query_centric.argtypes = L.deft_plan_create.argtypes
     L.deft_plan_create_node_chunks.argtypes = L.deft_plan_create.argtypes
+    L.deft_plan_create_multi_token.argtypes = [
+        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32,
+        ctypes.POINTER(_P)]
     L.deft_plan_destroy.argtypes = [_P]
     L.deft_plan_destroy.restype = None
     L.deft_plan_export.argtypes = [_P, ctypes.POINTER(deft_plan_view)]
@@ -95,7 +99,7 @@ def lib() -> ctypes.CDLL:
                                  _P, _P]
     L.deft_last_error.restype = ctypes.c_char_p
     for name in ("deft_plan_create", "deft_plan_create_query_centric", "deft_plan_create_node_chunks",
-                 "deft_plan_export",
+                 "deft_plan_create_multi_token", "deft_plan_export",
                  "deft_plan_device_bytes", "deft_plan_upload",
                  "deft_tree_attention", "deft_tree_attention_fused", "deft_partial_attention",
                  "deft_lse_merge"):
@@ -168,6 +172,19 @@ def deft_plan_create_node_chunks(parents, seg_lens, query_nodes, chunk_tokens: i
     h = _P()
     _check(lib().deft_plan_create_node_chunks(_ptr_i32(p), _ptr_i32(s), int(p.shape[0]), _ptr_i32(q),
                                               int(q.shape[0]), int(chunk_tokens), ctypes.byref(h)))
+    return Plan(h)
+
+
+def deft_plan_create_multi_token(parents, seg_lens, query_nodes, query_lens, chunk_tokens: int) -> Plan:
+    """query_lens None passes NULL (every query sees its whole node)."""
+    p, s, q = _i32(parents), _i32(seg_lens), _i32(query_nodes)
+    ql = None if query_lens is None else _i32(query_lens)
+    if ql is not None and ql.shape[0] != q.shape[0]:
+        raise ValueError("query_lens needs one entry per query")
+    h = _P()
+    _check(lib().deft_plan_create_multi_token(_ptr_i32(p), _ptr_i32(s), int(p.shape[0]), _ptr_i32(q),
+                                              None if ql is None else _ptr_i32(ql), int(q.shape[0]),
+                                              int(chunk_tokens), ctypes.byref(h)))
     return Plan(h)
 
 

@@ -10,16 +10,26 @@ from . import deft as D
 class TreeAttention:
     """Plan a tree once, then run tree attention over paged KV.
 
+    query_lens (optional): multi-token query nodes, the leading tokens of its
+    own node each query sees.
+
     desc: a deft_attn_desc (see deft.make_desc).  Device buffers are torch
     tensors on `device`; the plan image is uploaded on `stream`.
     """
 
     def __init__(self, parents, seg_lens, query_nodes, chunk_tokens: int, desc, device="cuda",
-                 stream=None, query_centric: bool = False, node_chunks: bool = False):
+                 stream=None, query_centric: bool = False, node_chunks: bool = False,
+                 query_lens=None):
         self.desc = desc
-        create = (D.deft_plan_create_query_centric if query_centric else
-                  D.deft_plan_create_node_chunks if node_chunks else D.deft_plan_create)
-        self.plan = create(parents, seg_lens, query_nodes, chunk_tokens)
+        if query_lens is not None:
+            if query_centric or node_chunks:
+                raise ValueError("query_lens is supported by the tree plan only")
+            self.plan = D.deft_plan_create_multi_token(parents, seg_lens, query_nodes, query_lens,
+                                                       chunk_tokens)
+        else:
+            create = (D.deft_plan_create_query_centric if query_centric else
+                      D.deft_plan_create_node_chunks if node_chunks else D.deft_plan_create)
+            self.plan = create(parents, seg_lens, query_nodes, chunk_tokens)
         plan_bytes, ws_bytes = D.deft_plan_device_bytes(self.plan, desc)
         self.plan_bytes, self.workspace_bytes = plan_bytes, ws_bytes
         self.dev_plan = torch.empty(max(plan_bytes, 256), dtype=torch.uint8, device=device)

@@ -16,6 +16,9 @@ Tree encoding used throughout:
   seg_lens[i]  number of KV tokens owned by node i (>= 1)
   query_nodes  node id each decode query sits on (it sees that node and
                all of its ancestors)
+  query_lens   optional, multi-token query nodes: how many leading tokens
+               of its own node each query sees (its position in the node
+               plus one); absent means the whole node
 Logical KV token order is the node segments concatenated in node-id order, so
 node i owns logical tokens [node_start[i], node_start[i] + seg_lens[i]) with
 node_start the exclusive prefix sum of seg_lens.  Logical token t lives in
@@ -39,6 +42,7 @@ WORKLOADS = {
     3: "parallel-sampling-2k-prompt-32x512-bf16",
     4: "reasoning-tree-1k-root-depth6-100-leaves-bf16",
     5: "spec-tree-32k-prefix-256-nodes-llama3-70b-bf16",
+    6: "multi-token-tree-2k-prompt-32-nodes-x8-bf16",
 }
 
 
@@ -60,6 +64,7 @@ class Workload:
     v_tokens: torch.Tensor       # [T, Hkv, d] in `dtype`, CPU, logical order
     page_size: int = PAGE_SIZE
     meta: dict = field(default_factory=dict)
+    query_lens: Optional[np.ndarray] = None   # int32 [Nq] or None
 
     @property
     def total_tokens(self) -> int:
@@ -136,6 +141,20 @@ def prefix_plus_token_tree(prefix_len: int, tree_parents: np.ndarray):
     seg[0] = prefix_len
     queries = np.arange(1, k + 1, dtype=np.int32)
     return parents, seg, queries
+
+
+def multi_token_nodes(parents: np.ndarray, seg_lens: np.ndarray, node_tokens: int):
+    """Give every non-root node `node_tokens` tokens and put a query on each
+    of them (tree prefill of multi-token speculative nodes): the query on a
+    node's j-th token sees the ancestors and the node's first j + 1 tokens.
+    Queries are ordered by node, then position.  Returns
+    (parents, seg_lens, query_nodes, query_lens)."""
+    seg = np.asarray(seg_lens, dtype=np.int32).copy()
+    inner = np.nonzero(np.asarray(parents) >= 0)[0]
+    seg[inner] = node_tokens
+    qn = np.repeat(inner, node_tokens).astype(np.int32)
+    ql = np.tile(np.arange(1, node_tokens + 1), inner.shape[0]).astype(np.int32)
+    return np.asarray(parents, dtype=np.int32), seg, qn, ql
 
 
 def shared_prompt_branches(prompt_len: int, n_branches: int, suffix_len: int):
@@ -217,7 +236,7 @@ def draw_qkv(seed: int, nq: int, hq: int, hkv: int, d: int, total_tokens: int,
 
 def make_workload(name, parents, seg_lens, query_nodes, *, chunk_tokens, hq, hkv, d,
                   dtype, seed=0, placement="identity", pool_pages=None,
-                  value_scale=1.0, meta=None) -> Workload:
+                  value_scale=1.0, meta=None, query_lens=None) -> Workload:
     """Assemble a workload: draw values, choose page placement.
 
     placement: "identity"  block_table[j] = j, pool = exactly the used pages
@@ -249,7 +268,8 @@ def make_workload(name, parents, seg_lens, query_nodes, *, chunk_tokens, hq, hkv
     return Workload(name=name, parents=parents, seg_lens=seg_lens, query_nodes=query_nodes,
                     chunk_tokens=int(chunk_tokens), num_q_heads=hq, num_kv_heads=hkv,
                     head_dim=d, dtype=dtype, num_pages=n_pages, block_table=bt,
-                    q=q, k_tokens=k, v_tokens=v, meta=dict(meta or {}))
+                    q=q, k_tokens=k, v_tokens=v, meta=dict(meta or {}),
+                    query_lens=None if query_lens is None else np.asarray(query_lens, dtype=np.int32))
 
 
 def hbm_pool_pages(total_bytes: int, hkv: int = 8, d: int = 128, elem_bytes: int = 2,
@@ -262,7 +282,7 @@ def hbm_pool_pages(total_bytes: int, hkv: int = 8, d: int = 128, elem_bytes: int
 def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = None,
                       pool_pages: Optional[int] = None, unscaled: bool = False,
                       placement: Optional[str] = None) -> Workload:
-    """The five standard workloads (see WORKLOADS for their names).
+    """The standard workloads (see WORKLOADS for their names).
 
     1: fp32, 4 q heads / 1 KV head, d 64; binary tree 256 + 2x32 + 4x32,
        one query per leaf; chunks of 64 tokens.
@@ -276,6 +296,10 @@ def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = 
     5: bf16, 64 q / 8 KV heads, d 128; 32768-token prefix plus a 256-node
        Medusa tree (branching 8/4/2/2/1), every tree node a query; pages at
        random positions of a `pool_pages` pool (default: just the used pages).
+    6: bf16, 32/8, d 128; multi-token query nodes: a 2048-token prompt and a
+       32-node Medusa tree (branching 4/3/2) whose nodes hold 8 draft tokens
+       each, every draft token a query (256 queries, causal inside a node);
+       chunks of 256 tokens; values scaled by 1/sqrt(d).
     """
     rng = np.random.default_rng(seed)
     if cfg == 1:
@@ -310,6 +334,14 @@ def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = 
                              hq=64, hkv=8, d=128, dtype=torch.bfloat16, seed=seed,
                              placement=placement or "scattered", pool_pages=pages,
                              meta={"depths": depths})
+    if cfg == 6:
+        tp, depths = medusa_token_tree(rng, (4, 3, 2), 32)
+        p, s, _ = prefix_plus_token_tree(2048, tp)
+        p, s, qn, ql = multi_token_nodes(p, s, 8)
+        return make_workload(WORKLOADS[6], p, s, qn, chunk_tokens=chunk_tokens or 256,
+                             hq=32, hkv=8, d=128, dtype=torch.bfloat16, seed=seed,
+                             placement=placement or "permuted", value_scale=1.0 / math.sqrt(128),
+                             meta={"depths": depths}, query_lens=ql)
     raise ValueError(f"unknown workload {cfg}")
 
 
