@@ -179,15 +179,20 @@ __device__ inline u32x4 load16(const void* base, int64_t elem_off, int elem_byte
 // Pool row (page * 16 + slot) of every flat token of the chunk, into LDS,
 // stored as row * mul + add.  All flat-to-logical loads are issued before any
 // block-table load so the two dependent lookups cost two memory latencies,
-// not two per token.  With RPI > 0 the rows of each 32-token step are stored
+// not two per token; mid() runs right after the block-table loads are issued
+// (callers issue their own independent loads there, so those overlap the
+// second lookup).  With RPI > 0 the rows of each 32-token step are stored
 // permuted, entry (t % RPI) * (32 / RPI) + (t % 32) / RPI, which puts the rows
 // one lane of a direct-to-LDS load sequence needs next to each other.  NT is
 // the work-group size.
-template <int RPI, int NT, int N>
+template <int RPI, int NT, int N, typename Mid>
 __device__ inline void stage_token_rows_n(int32_t* tok_row, const DevPlan& P, const int32_t* bt,
-                                          int32_t cs, int32_t len, int32_t mul, int32_t add) {
-  // N fixed loads per thread, no branches between them; indices past the
-  // chunk end re-read its last token and are not stored.
+                                          int32_t cs, int32_t len, int32_t mul, int32_t add, Mid mid) {
+  // N fixed loads per thread and no branches: indices past the chunk end
+  // re-read its last token, and their entries (t < N * NT <= kMaxChunkTokens,
+  // beyond the chunk's steps or masked in its last step) are stored but never
+  // used.  A conditional store would let the compiler sink the loads into it
+  // and serialise them.
   int32_t lt[N];
 #pragma unroll
   for (int k = 0; k < N; ++k)
@@ -195,26 +200,28 @@ __device__ inline void stage_token_rows_n(int32_t* tok_row, const DevPlan& P, co
   int32_t pg[N];
 #pragma unroll
   for (int k = 0; k < N; ++k) pg[k] = bt[lt[k] >> 4];
+  mid();
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const int t = threadIdx.x + k * NT;
-    if (t < len) {
-      int at = t;
-      if constexpr (RPI > 0) at = (t & ~31) + (t % RPI) * (32 / RPI) + (t & 31) / RPI;
-      tok_row[at] = (pg[k] * kPageSize + (lt[k] & (kPageSize - 1))) * mul + add;
-    }
+    int at = t;
+    if constexpr (RPI > 0) at = (t & ~31) + (t % RPI) * (32 / RPI) + (t & 31) / RPI;
+    tok_row[at] = (pg[k] * kPageSize + (lt[k] & (kPageSize - 1))) * mul + add;
   }
 }
-template <int RPI, int NT>
+template <int RPI, int NT, typename Mid>
 __device__ inline void stage_token_rows(int32_t* tok_row, const DevPlan& P, const int32_t* bt,
-                                        int32_t cs, int32_t len, int32_t mul = 1, int32_t add = 0) {
+                                        int32_t cs, int32_t len, int32_t mul, int32_t add, Mid mid) {
   static_assert(kMaxChunkTokens <= 16 * NT, "at most 16 staging batches");
+  // N * NT stays within kMaxChunkTokens: N is the power of two at or above
+  // ceil(len / NT) and NT divides kMaxChunkTokens.
+  static_assert(kMaxChunkTokens % NT == 0, "whole staging batches");
   const int nk = (len + NT - 1) / NT;
-  if (nk <= 1) stage_token_rows_n<RPI, NT, 1>(tok_row, P, bt, cs, len, mul, add);
-  else if (nk <= 2) stage_token_rows_n<RPI, NT, 2>(tok_row, P, bt, cs, len, mul, add);
-  else if (nk <= 4) stage_token_rows_n<RPI, NT, 4>(tok_row, P, bt, cs, len, mul, add);
-  else if (nk <= 8) stage_token_rows_n<RPI, NT, 8>(tok_row, P, bt, cs, len, mul, add);
-  else stage_token_rows_n<RPI, NT, 16>(tok_row, P, bt, cs, len, mul, add);
+  if (nk <= 1) stage_token_rows_n<RPI, NT, 1>(tok_row, P, bt, cs, len, mul, add, mid);
+  else if (nk <= 2) stage_token_rows_n<RPI, NT, 2>(tok_row, P, bt, cs, len, mul, add, mid);
+  else if (nk <= 4) stage_token_rows_n<RPI, NT, 4>(tok_row, P, bt, cs, len, mul, add, mid);
+  else if (nk <= 8) stage_token_rows_n<RPI, NT, 8>(tok_row, P, bt, cs, len, mul, add, mid);
+  else stage_token_rows_n<RPI, NT, 16>(tok_row, P, bt, cs, len, mul, add, mid);
 }
 
 // ---------------------------------------------------------------------------
@@ -416,16 +423,24 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // address lds + size * i (M0 holds the wave-uniform LDS base).  The compiler
 // sees no LDS write here, so it adds no waits of its own for them; callers
 // order them with explicit s_waitcnt vmcnt (they count as vector-memory loads).
+// Work-group barrier for LDS data only: the wave's LDS operations complete,
+// then s_barrier.  Unlike __syncthreads() it does not wait for the wave's
+// outstanding global loads and stores, so loads issued before it (Q rows,
+// the first step's K/V) stay in flight across it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ inline uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lptr_t)p));
 }
+// `lds` is wave-uniform; readfirstlane only tells the compiler so (it keeps
+// it in an SGPR at no cost where it can already prove it).
 __device__ inline void lds_dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds) : "memory", "m0");
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 __device__ inline void lds_dma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(lds) : "memory", "m0");
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 // s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
 // operations are outstanding / until all LDS operations are done.
@@ -517,11 +532,11 @@ __global__ __launch_bounds__(64 * valu_waves<R>()) void valu_partial(PartialArgs
   for (int r = 0; r < R; ++r) qrow[r] = P.slot_query[gofs + (rb + min(r, nr - 1)) / a.grp];
   // token rows as rows of this KV head (pool row * Hkv + g), permuted so a
   // lane's rows of one step are adjacent
-  stage_token_rows<RPI, 64 * NW>(tok_row, P, a.block_table, cs, len, a.hkv, g);
+  stage_token_rows<RPI, 64 * NW>(tok_row, P, a.block_table, cs, len, a.hkv, g, [] {});
   // lane i loads the mask word of row i (rows past nr: the last row's)
   const int32_t mask_slot = gofs + (rb + min(lane, nr - 1)) / a.grp;
   const uint32_t* mask_src = P.slot_mask + static_cast<size_t>(mask_slot) * W;
-  __syncthreads();
+  lds_barrier();
 
   char* ring = smem + w * NSTG * STAGE_B;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
@@ -693,7 +708,7 @@ __global__ __launch_bounds__(64 * valu_waves<R>()) void valu_partial(PartialArgs
 
   // Merge the lane groups of this wave, then the waves (through LDS, over
   // the ring), at the true max.
-  __syncthreads();
+  lds_barrier();
   float* red = reinterpret_cast<float*>(smem);   // [NW][R][D + 2]
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -720,7 +735,7 @@ __global__ __launch_bounds__(64 * valu_waves<R>()) void valu_partial(PartialArgs
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
     const int r = idx / D, e = idx % D;
     float mx = kNegInf;
@@ -783,13 +798,13 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   constexpr int RPI = 64 / CH;          // token rows per direct load
   constexpr int STAGE_B = 2 * TILE_B + 256;   // K, V, 64 mask words
   constexpr int RING_B = NSPLIT * 2 * STAGE_B;
-  constexpr int RED_B = NWAVE * DT * NRT * 64 * 16;   // every wave's O^T fragments
+  constexpr int RED_W = DT * NRT * 64 * 16;   // one wave's O^T fragments (epilogue)
+  static_assert(2 * RED_W <= 2 * STAGE_B, "a split's two waves reduce through their own ring");
   static_assert(NI == 8 || NI == 4, "token rows per lane come in groups of 4 or 8");
   static_assert(kMfmaRows == 2 * WROWS, "a work item is two row halves");
-  __shared__ __attribute__((aligned(1024))) char smem[RING_B > RED_B ? RING_B : RED_B];
+  __shared__ __attribute__((aligned(1024))) char smem[RING_B];
   __shared__ __attribute__((aligned(16))) int32_t tok_row[kMaxChunkTokens];
   __shared__ float stats[NWAVE][WROWS][3];
-  __shared__ float row_ml[kMfmaRows][2];
   __shared__ int32_t pair_ready[NSPLIT][2];
 
   const DevPlan& P = a.plan;
@@ -809,30 +824,41 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   const uint16_t* kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* vp = static_cast<const uint16_t*>(a.v);
 
-  // The queries of this wave's rows are looked up before the token rows are
-  // staged, so both dependent lookups overlap; rows past nr read a valid row
-  // and are masked later.
-  int32_t sq[NRT];
+  // The block's 64 Q rows (64 * 2D bytes) are copied once into LDS, into
+  // stage 1 of split 0's ring (first refilled in the loop, after every wave
+  // has read its fragments).  Copy n (1 KB, NQW per wave) holds rows RPQ*n
+  // .. RPQ*n + RPQ-1; its lane i takes 16-byte chunk (i % CH) ^ (R % CH) of
+  // row R = RPQ*n + i / CH, so the fragment reads below avoid bank
+  // conflicts.  The rows' queries are looked up alongside the flat-to-logical
+  // lookups of the staging, the copies are issued alongside its block-table
+  // lookups.  Rows past nr copy a valid row; they are masked later.
+  constexpr int RPQ = 1024 / ROWB;
+  constexpr int NQW = kMfmaRows * ROWB / 1024 / NWAVE;
+  static_assert(kMfmaRows * ROWB <= STAGE_B, "the block's Q rows fit in one ring stage");
+  static_assert(NQW >= 1 && NQW * NWAVE * 1024 == kMfmaRows * ROWB, "whole 1 KB Q copies per wave");
+  const uint32_t q_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + STAGE_B));
+  int32_t qsq[NQW];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
-    sq[rt] = P.slot_query[gofs + (rb + min(WROWS * h + rt * 16 + lr, nr - 1)) / a.grp];
-  // token rows are stored as rows of this KV head: pool row * Hkv + g
-  stage_token_rows<RPI, 512>(tok_row, P, a.block_table, cs, len, a.hkv, g);
-  // Q^T fragments (B operand of S^T = K Q^T) of this wave's 32 rows.
-  bf16x8 qf[NRT][KS];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int row = rb + min(WROWS * h + rt * 16 + lr, nr - 1);
-    const int head = g * a.grp + row % a.grp;
-    const uint16_t* src = qp + (static_cast<int64_t>(sq[rt]) * a.hq + head) * D + lj * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[rt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 32));
+  for (int j = 0; j < NQW; ++j) {
+    const int R = RPQ * (NQW * w + j) + lane / CH;
+    qsq[j] = P.slot_query[gofs + (rb + min(R, nr - 1)) / a.grp];
   }
+  // token rows are stored as rows of this KV head: pool row * Hkv + g
+  stage_token_rows<RPI, 512>(tok_row, P, a.block_table, cs, len, a.hkv, g, [&] {
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) {
+      const int R = RPQ * (NQW * w + j) + lane / CH;
+      const int row = rb + min(R, nr - 1);
+      const int head = g * a.grp + row % a.grp;
+      const int c = (lane % CH) ^ (R % CH);
+      lds_dma16(qp + (static_cast<int64_t>(qsq[j]) * a.hq + head) * D + c * 8, q_lds + (NQW * w + j) * 1024);
+    }
+  });
   // Row of the mask word this lane loads (lane i <-> row i of the block).
   const int32_t mask_slot = gofs + (rb + (lane < nr ? lane : 0)) / a.grp;
   if (threadIdx.x < 2 * NSPLIT) pair_ready[threadIdx.x >> 1][threadIdx.x & 1] = -1;
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // this wave's Q copies are in LDS
+  lds_barrier();
 
   char* ring = smem + sp * 2 * STAGE_B;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
@@ -916,6 +942,20 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
     for (int n = 0; n < NI; ++n) lds_dma16(ptr[n], ring_lds + h * TILE_B + n * 1024);
     if (h == 0) lds_dma4(mask_src + sp, ring_lds + 2 * TILE_B);
   }
+  // Q^T fragments (B operand of S^T = K Q^T) of this wave's 32 rows: lane
+  // (lr, lj) takes d = 32 ks + 8 lj .. +7 of row R = 32h + 16rt + lr, i.e.
+  // chunk 4 ks + lj, stored in slot (4 ks + lj) ^ (R % CH).  Every wave reads
+  // them before any wave refills stage 1 of split 0 (the barrier below; this
+  // step's loads above go to stage 0).
+  bf16x8 qf[NRT][KS];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int R = WROWS * h + rt * 16 + lr;
+      qf[rt][ks] = *reinterpret_cast<const bf16x8*>(smem + STAGE_B + R * ROWB + (((4 * ks + lj) ^ (R % CH)) * 16));
+    }
+  lds_barrier();
   static_assert(2 * KS == NI && DT == NI, "the next step's loads are spread one per two MFMA groups");
 
   // One step on ring stage STG (a compile-time constant, so every LDS address
@@ -928,8 +968,6 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
     // work-group: each publishes "my half of iteration i is in LDS and I have
     // finished iteration i-1", then waits for the partner to say the same,
     // after which the other stage can be refilled with step i+1.
-    // (The wait for all loads also covers the Q loads, so the compiler
-    // places none in the loop.)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     pair_sync(&pair_ready[sp][h], &pair_ready[sp][h ^ 1], i, lane);
     if (step >= nsteps) return;
@@ -1049,8 +1087,13 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
     if (i + 1 < iters) step_body(std::integral_constant<int, 1>{}, i + 1);
   }
 
-  // Combine the four token splits of each row half: true max, per-split
-  // weights, summed l and O.
+  // Combine the four token splits of each row half.  Each wave publishes its
+  // rows' (running max, true max, l) and its unscaled O^T fragments as f32x4
+  // at red[dt][rt][lane] in its half of its own split's ring, as soon as its
+  // partner is done with that ring too, so waves that finish early write
+  // while others still compute.  After one barrier every thread takes DT/2
+  // d-tiles of one row: M = the splits' largest true max, weights
+  // f_q = exp2(m_run_q - M), l = sum f_q l_q, O = sum f_q O_q.
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const float ls = rowsum4(l_part[rt]);
@@ -1061,60 +1104,54 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
       stats[w][rt * 16 + lr][2] = ls;
     }
   }
-  __syncthreads();   // every wave is past its loop: the ring is free
-  // Per row of the block: true max M over the splits and the total l.
-  for (int r = threadIdx.x; r < kMfmaRows; r += blockDim.x) {
-    const int hh = r / WROWS, rw = r % WROWS;
+  pair_sync(&pair_ready[sp][h], &pair_ready[sp][h ^ 1], iters, lane);   // both past their last step
+  {
+    f32x4* mine = reinterpret_cast<f32x4*>(smem + sp * 2 * STAGE_B + h * RED_W);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) mine[(dt * NRT + rt) * 64 + lane] = o[dt][rt];
+  }
+  lds_barrier();
+  {
+    static_assert(2 * NRT * 64 * 2 == 512, "thread -> (d half, row half, row tile, lane)");
+    const int ln = threadIdx.x & 63, rt = (threadIdx.x >> 6) % NRT;
+    const int hh = (threadIdx.x >> 6) / NRT % 2, dq = threadIdx.x >> 8;
+    const int rw = rt * 16 + (ln & 15), r = WROWS * hh + rw;
     float mx = kNegInf;
 #pragma unroll
     for (int q = 0; q < NSPLIT; ++q) mx = fmaxf(mx, stats[2 * q + hh][rw][1]);
-    float ls = 0.f;
+    float f[NSPLIT], ls = 0.f;
 #pragma unroll
     for (int q = 0; q < NSPLIT; ++q) {
       const float mr = stats[2 * q + hh][rw][0];
-      ls += (mr == kNegInf) ? 0.f : fast_exp2((mr - mx) * cl2) * stats[2 * q + hh][rw][2];
+      f[q] = (mr == kNegInf) ? 0.f : fast_exp2((mr - mx) * cl2);
+      ls += f[q] * stats[2 * q + hh][rw][2];
     }
-    row_ml[r][0] = mx;
-    row_ml[r][1] = ls;
     if (r < nr) {
       const int row = rb + r;
       const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
-      a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
-      a.pl[sh] = ls;
-    }
-  }
-  // Each wave stores its O^T fragments scaled by exp2(m_run - M) as f32x4 at
-  // red[w][dt][rt][lane].
-  f32x4* red = reinterpret_cast<f32x4*>(smem);
+      if (ln < 16 && dq == 0) {
+        a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
+        a.pl[sh] = ls;
+      }
+      const float inv = 1.f / ls;
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int r = rt * 16 + lr;
-    float mx = kNegInf;
+      for (int k = 0; k < DT / 2; ++k) {
+        const int dt = dq * (DT / 2) + k;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < NSPLIT; ++q) mx = fmaxf(mx, stats[2 * q + h][r][1]);
-    const float f = (m_run[rt] == kNegInf) ? 0.f : fast_exp2((m_run[rt] - mx) * cl2);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) red[((w * DT + dt) * NRT + rt) * 64 + lane] = o[dt][rt] * f;
-  }
-  __syncthreads();
-  // Sum over the splits; thread -> (half, dt, rt, lane) f32x4 = 4 consecutive d of one row.
-  for (int idx = threadIdx.x; idx < 2 * DT * NRT * 64; idx += blockDim.x) {
-    const int ln = idx & 63, rt = (idx >> 6) % NRT, dt = ((idx >> 6) / NRT) % DT, hh = (idx >> 6) / (NRT * DT);
-    const int r = WROWS * hh + rt * 16 + (ln & 15);
-    if (r >= nr) continue;
-    f32x4 acc = red[((hh * DT + dt) * NRT + rt) * 64 + ln];
-#pragma unroll
-    for (int q = 1; q < NSPLIT; ++q) acc += red[(((2 * q + hh) * DT + dt) * NRT + rt) * 64 + ln];
-    const int row = rb + r;
-    const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
-    const int64_t at = sh * D + dt * 16 + (ln >> 4) * 4;
-    if (a.po_bf16) {
-      const float inv = 1.f / row_ml[r][1];
-      const uint32_t lo = f32_to_bf16(acc[0] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[1] * inv)) << 16);
-      const uint32_t hi = f32_to_bf16(acc[2] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[3] * inv)) << 16);
-      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + at) = u32x2{lo, hi};
-    } else {
-      *reinterpret_cast<f32x4*>(a.po + at) = acc;
+        for (int q = 0; q < NSPLIT; ++q)
+          acc += f[q] * reinterpret_cast<const f32x4*>(smem + q * 2 * STAGE_B + hh * RED_W)[(dt * NRT + rt) * 64 + ln];
+        const int64_t at = sh * D + dt * 16 + (ln >> 4) * 4;
+        if (a.po_bf16) {
+          const uint32_t lo = f32_to_bf16(acc[0] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[1] * inv)) << 16);
+          const uint32_t hi = f32_to_bf16(acc[2] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[3] * inv)) << 16);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + at) = u32x2{lo, hi};
+        } else {
+          *reinterpret_cast<f32x4*>(a.po + at) = acc;
+        }
+      }
     }
   }
   if constexpr (FUSED) {
