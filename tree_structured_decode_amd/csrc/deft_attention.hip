@@ -68,7 +68,8 @@ struct DevPlan {
   const int4* mfma_items;
   const int4* valu_items;
   int32_t* tickets;          // [Nq * Hq], zero between calls (fused merge)
-  int32_t n_mfma, n_valu, mask_words, num_queries;
+  const int32_t* merge_slots;   // [Nq][merge_stride] slot ids padded with -1, or unused
+  int32_t n_mfma, n_valu, mask_words, num_queries, merge_stride;
 };
 
 // Operands of the per-(query, head) merge (the merge kernel and the fused
@@ -80,7 +81,8 @@ struct MergeArgs {
   void* out;
   const int32_t* query_slot_offsets;
   const int32_t* query_slots;
-  int32_t nq, hq, po_bf16;
+  const int32_t* merge_slots;   // fixed-stride lists (merge_stride > 0) or unused
+  int32_t nq, hq, po_bf16, merge_stride;
 };
 
 struct PartialArgs {
@@ -235,16 +237,30 @@ __device__ inline void stage_token_rows(int32_t* tok_row, const DevPlan& P, cons
 // Queries with more than 64 slots take several rounds, rescaled online.
 // ---------------------------------------------------------------------------
 
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) x = fmaxf(x, __shfl_xor(x, k));
-  return x;
+// Whole-wave reductions without the LDS crossbar: DPP within each row of 16
+// lanes, then the lane^16 and lane^32 exchanges by permlane swaps.
+template <typename Op>
+__device__ inline float wave_reduce(float x, Op op) {
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  x = op(x, dpp(x, std::integral_constant<int, 0xB1>{}));    // quad_perm [1,0,3,2]
+  x = op(x, dpp(x, std::integral_constant<int, 0x4E>{}));    // quad_perm [2,3,0,1]
+  x = op(x, dpp(x, std::integral_constant<int, 0x141>{}));   // row_half_mirror
+  x = op(x, dpp(x, std::integral_constant<int, 0x140>{}));   // row_mirror
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
-
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) x += __shfl_xor(x, k);
-  return x;
+__device__ inline float wave_max(float x) { return wave_reduce(x, [](float a, float b) { return fmaxf(a, b); }); }
+__device__ inline float wave_sum(float x) { return wave_reduce(x, [](float a, float b) { return a + b; }); }
+// Sum of lanes l, l^16, l^32, l^48 (the four 16-lane groups), in every lane.
+__device__ inline float groups4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // EPL consecutive elements of one partial O row (slot-head sh), as fp32.
@@ -281,15 +297,31 @@ __device__ void merge_query_head(const MergeArgs& a, int qi, int h) {
   constexpr int PER_G = EPL / 4;   // output elements each lane stores
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, sub = lane & 15;
-  const int s0 = a.query_slot_offsets[qi], s1 = a.query_slot_offsets[qi + 1];
+  // The query's slot list: fixed stride (padded with -1, read without a
+  // dependent offset lookup) or CSR.
+  const int32_t* list;
+  int cnt;
+  if (a.merge_stride > 0) {
+    list = a.merge_slots + static_cast<size_t>(qi) * a.merge_stride;
+    cnt = a.merge_stride;
+  } else {
+    const int s0 = a.query_slot_offsets[qi];
+    list = a.query_slots + s0;
+    cnt = a.query_slot_offsets[qi + 1] - s0;
+  }
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
   float mrun = kNegInf, wsum = 0.f;
-  for (int i0 = s0; i0 < s1; i0 += 64) {
-    const int n = min(64, s1 - i0);
-    // lanes past the list re-read its first slot and get weight 0
-    const int slot = a.query_slots[i0 + (lane < n ? lane : 0)];
+  for (int i0 = 0; i0 < cnt; i0 += 64) {
+    const int nmax = min(64, cnt - i0);
+    const int raw = list[i0 + (lane < nmax ? lane : 0)];
+    // valid entries form a prefix of the round (padding is at the end)
+    const bool ok = lane < nmax && raw >= 0;
+    const int n = __popcll(__ballot(ok));
+    if (n == 0) break;
+    // lanes past the list take its first slot and get weight 0
+    const int slot = ok ? raw : __shfl(raw, 0);
     const int64_t sh = static_cast<int64_t>(slot) * a.hq + h;
     const float mv = lane < n ? a.pm[sh] : kNegInf;
     const float lv = lane < n ? a.pl[sh] : 0.f;
@@ -331,10 +363,7 @@ __device__ void merge_query_head(const MergeArgs& a, int qi, int h) {
   }
   // sum the four groups; every group then holds the full row
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    acc[e] += __shfl_xor(acc[e], 16);
-    acc[e] += __shfl_xor(acc[e], 32);
-  }
+  for (int e = 0; e < EPL; ++e) acc[e] = groups4_sum(acc[e]);
   const float inv = 1.f / wsum;
   // group g stores elements [g * PER_G, (g + 1) * PER_G) of each lane's EPL
   float x[PER_G];
@@ -1180,6 +1209,8 @@ static DevPlan make_dev_plan(const deft_plan* p) {
   d.mfma_items = reinterpret_cast<const int4*>(b + L.mfma_items);
   d.valu_items = reinterpret_cast<const int4*>(b + L.valu_items);
   d.tickets = const_cast<int32_t*>(b) + L.tickets;
+  d.merge_slots = b + L.merge_slots;
+  d.merge_stride = L.merge_stride;
   d.n_mfma = L.n_mfma;
   d.n_valu = L.n_valu;
   d.mask_words = p->mask_words;
@@ -1267,6 +1298,8 @@ static int run_partials(const void* q, const void* k, const void* v, const int32
   pa.merge.out = fused_out;
   pa.merge.query_slot_offsets = pa.plan.query_slot_offsets;
   pa.merge.query_slots = pa.plan.query_slots;
+  pa.merge.merge_slots = pa.plan.merge_slots;
+  pa.merge.merge_stride = pa.plan.merge_stride;
   pa.merge.nq = p->num_queries;
   pa.merge.hq = d->num_q_heads;
   pa.merge.po_bf16 = pa.po_bf16;
@@ -1286,6 +1319,8 @@ static int run_merge(const deft_plan* p, const deft_attn_desc* d, const float* p
   const DevPlan dp = make_dev_plan(p);
   ma.query_slot_offsets = dp.query_slot_offsets;
   ma.query_slots = dp.query_slots;
+  ma.merge_slots = dp.merge_slots;
+  ma.merge_stride = dp.merge_stride;
   ma.nq = p->num_queries;
   ma.hq = d->num_q_heads;
   ma.po_bf16 = po_bf16 ? 1 : 0;

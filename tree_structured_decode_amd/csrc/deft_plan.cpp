@@ -358,6 +358,13 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   // fused-merge tickets, one per (query, query head); zero in the uploaded
   // image and reset to zero by the kernels after use
   L->tickets = take(static_cast<size_t>(p->num_queries) * d->num_q_heads);
+  // fixed-stride merge lists when padding costs at most about 4x the slots
+  int32_t max_slots = 0;
+  for (int32_t q = 0; q < p->num_queries; ++q)
+    max_slots = std::max(max_slots, p->query_slot_offsets[q + 1] - p->query_slot_offsets[q]);
+  const int64_t padded = static_cast<int64_t>(p->num_queries) * max_slots;
+  L->merge_stride = (max_slots > 0 && padded <= 4 * static_cast<int64_t>(S) + 4096) ? max_slots : 0;
+  L->merge_slots = take(L->merge_stride ? static_cast<size_t>(padded) : 0);
   L->total_words = w;
   L->n_mfma = static_cast<int32_t>(mfma.size());
   L->n_valu = static_cast<int32_t>(valu.size());
@@ -380,6 +387,15 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   std::copy(p->query_slots.begin(), p->query_slots.end(), im + L->query_slots);
   std::memcpy(im + L->mfma_items, mfma.data(), sizeof(WorkItem) * mfma.size());
   std::memcpy(im + L->valu_items, valu.data(), sizeof(WorkItem) * valu.size());
+  if (L->merge_stride) {
+    int32_t* ms = im + L->merge_slots;
+    for (int32_t q = 0; q < p->num_queries; ++q) {
+      const int32_t a = p->query_slot_offsets[q], b = p->query_slot_offsets[q + 1];
+      int32_t* row = ms + static_cast<size_t>(q) * L->merge_stride;
+      std::copy(p->query_slots.begin() + a, p->query_slots.begin() + b, row);
+      std::fill(row + (b - a), row + L->merge_stride, -1);
+    }
+  }
   return DEFT_OK;
 }
 
