@@ -347,7 +347,7 @@ def main():
         else:
             achieved = (kv_bytes + q_bytes) / (mean_part * 1e-6) / 1e9
             roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-        roof["kernel"] = "mfma_partial" if (wl.dtype == torch.bfloat16) else "valu_partial"
+        roof["kernel"] = "partial_attention"
         roof["algorithmic_bytes_per_launch"] = kv_bytes + q_bytes
     else:
         achieved = (part_bytes + q_bytes) / (mean_merge * 1e-6) / 1e9

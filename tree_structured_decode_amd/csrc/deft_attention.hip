@@ -22,12 +22,12 @@
 // Row convention: for KV head g and chunk c with group slots j = 0..n-1, row
 // r = j * G + hh is slot j's query on query head g * G + hh (G = Hq / Hkv).
 //
-// Two partial kernels share the work description:
-//   mfma_partial  bf16 groups with >= 16 rows: 16x16x32 bf16 MFMA for S = K Q^T
-//                 and O^T = V^T P^T, 64 rows per work-group, the chunk's
-//                 tokens split across 4 waves and the waves merged in LDS;
-//   valu_partial  fp32 inputs and bf16 groups below one MFMA tile: per-token
-//                 dot products with wavefront reductions.
+// One partial kernel (partial_attention) runs two bodies on one work description:
+//   mfma_body  bf16 groups with >= 16 rows: 16x16x32 bf16 MFMA for S = K Q^T
+//              and O^T = V^T P^T, 64 rows per work-group, the chunk's
+//              tokens split across 4 wave pairs and the splits merged in LDS;
+//   valu_body  fp32 inputs and bf16 groups below one MFMA tile: per-token
+//              dot products with wavefront reductions.
 // Scores are kept in log2 units (scale * log2(e) folded in) so exp2 is used;
 // the stored m is converted back to natural-log units.
 
@@ -518,8 +518,24 @@ __device__ inline void pair_sync(int32_t* mine, int32_t* theirs, int32_t i, int 
 // ---------------------------------------------------------------------------
 template <int R> constexpr int valu_waves() { return R <= 8 ? 8 : 4; }
 
+template <typename T, int D, int R>
+struct ValuShape {
+  static constexpr int EB = sizeof(T);
+  static constexpr int NW = valu_waves<R>();
+  static constexpr int TILE_B = 4096;
+  static constexpr int NSTG = NW == 8 ? 2 : 4;
+  static constexpr int STAGE_B = 2 * TILE_B + 256;
+  static constexpr int RING_B = NW * NSTG * STAGE_B;
+  static constexpr int RED_B = NW * R * (D + 2) * 4;
+  static constexpr int SMEM_B = RING_B > RED_B ? RING_B : RED_B;
+  // LDS carve-out: ring / reduction buffer, staged token rows, fused-merge lists
+  static constexpr int TOK_OFF = SMEM_B;
+  static constexpr int LIST_OFF = TOK_OFF + 4 * kMaxChunkTokens;
+  static constexpr int LDS_B = LIST_OFF + 4 * (kValuRows + 4);
+};
+
 template <typename T, int D, int R, bool FUSED>
-__global__ __launch_bounds__(64 * valu_waves<R>()) void valu_partial(PartialArgs a) {
+__device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int bid) {
   constexpr int EB = sizeof(T);
   constexpr int EPL = 16 / EB;                     // elements per lane (16 bytes)
   constexpr int LPT = D / EPL;                     // lanes per token
@@ -541,13 +557,15 @@ __global__ __launch_bounds__(64 * valu_waves<R>()) void valu_partial(PartialArgs
   static_assert(R <= kValuRows && R <= 64, "row capacity");
   static_assert(STEP_T <= 32 && 32 % STEP_T == 0, "a step's mask bits lie in one word");
   static_assert(RPI >= 2 && 32 % RPI == 0 && NI == 4, "staged-row permutation");
-  __shared__ __attribute__((aligned(1024))) char smem[RING_B > RED_B ? RING_B : RED_B];
-  __shared__ __attribute__((aligned(16))) int32_t tok_row[kMaxChunkTokens];
+  using Shape = ValuShape<T, D, R>;
+  static_assert(Shape::RING_B == RING_B && Shape::RED_B == RED_B, "shape constants agree");
+  char* smem = lds;
+  int32_t* tok_row = reinterpret_cast<int32_t*>(lds + Shape::TOK_OFF);
 
   const DevPlan& P = a.plan;
-  const int g = blockIdx.x % a.hkv;
-  const int4 it0 = P.valu_items[2 * (blockIdx.x / a.hkv)];
-  const int4 it1 = P.valu_items[2 * (blockIdx.x / a.hkv) + 1];
+  const int g = bid % a.hkv;
+  const int4 it0 = P.valu_items[2 * (bid / a.hkv)];
+  const int4 it1 = P.valu_items[2 * (bid / a.hkv) + 1];
   const int32_t rb = it0.y, nr = it0.z, cs = it0.w;
   const int32_t len = it1.x, gofs = it1.y;
   const int W = P.mask_words;
@@ -788,9 +806,8 @@ __global__ __launch_bounds__(64 * valu_waves<R>()) void valu_partial(PartialArgs
     }
   }
   if constexpr (FUSED) {
-    __shared__ int32_t last_list[kValuRows];
-    __shared__ int32_t n_last[1];
-    fused_merge_tail<T, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, n_last);
+    int32_t* last_list = reinterpret_cast<int32_t*>(lds + Shape::LIST_OFF);
+    fused_merge_tail<T, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, last_list + kValuRows);
   }
 }
 
@@ -812,8 +829,23 @@ __global__ __launch_bounds__(64 * valu_waves<R>()) void valu_partial(PartialArgs
 // are stored with their 16-byte chunks XOR-swizzled by the row index.  The
 // four token splits of each row half are merged through LDS at the end.
 // ---------------------------------------------------------------------------
+template <int D>
+struct MfmaShape {
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILE_B = 32 * ROWB;
+  static constexpr int STAGE_B = 2 * TILE_B + 256;
+  static constexpr int RING_B = 4 * 2 * STAGE_B;
+  // LDS carve-out: rings (and the epilogue's reduction), staged token rows,
+  // split statistics, pair flags, fused-merge lists
+  static constexpr int TOK_OFF = RING_B;
+  static constexpr int STATS_OFF = TOK_OFF + 4 * kMaxChunkTokens;
+  static constexpr int FLAGS_OFF = STATS_OFF + 8 * 32 * 3 * 4;
+  static constexpr int LIST_OFF = FLAGS_OFF + 4 * 2 * 4;
+  static constexpr int LDS_B = LIST_OFF + 4 * (kMfmaRows + 4);
+};
+
 template <int D, bool FUSED>
-__global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
+__device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int bid) {
   constexpr int NWAVE = 8;
   constexpr int NSPLIT = 4;
   constexpr int NRT = 2;                // row tiles per wave
@@ -831,15 +863,18 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
   static_assert(2 * RED_W <= 2 * STAGE_B, "a split's two waves reduce through their own ring");
   static_assert(NI == 8 || NI == 4, "token rows per lane come in groups of 4 or 8");
   static_assert(kMfmaRows == 2 * WROWS, "a work item is two row halves");
-  __shared__ __attribute__((aligned(1024))) char smem[RING_B];
-  __shared__ __attribute__((aligned(16))) int32_t tok_row[kMaxChunkTokens];
-  __shared__ float stats[NWAVE][WROWS][3];
-  __shared__ int32_t pair_ready[NSPLIT][2];
+  using Shape = MfmaShape<D>;
+  static_assert(Shape::RING_B == RING_B && Shape::STAGE_B == STAGE_B, "shape constants agree");
+  static_assert(NWAVE == 8 && WROWS == 32 && NSPLIT == 4, "carve-out sizes");
+  char* smem = lds;
+  int32_t* tok_row = reinterpret_cast<int32_t*>(lds + Shape::TOK_OFF);
+  float (*stats)[WROWS][3] = reinterpret_cast<float (*)[WROWS][3]>(lds + Shape::STATS_OFF);
+  int32_t (*pair_ready)[2] = reinterpret_cast<int32_t (*)[2]>(lds + Shape::FLAGS_OFF);
 
   const DevPlan& P = a.plan;
-  const int g = blockIdx.x % a.hkv;
-  const int4 it0 = P.mfma_items[2 * (blockIdx.x / a.hkv)];
-  const int4 it1 = P.mfma_items[2 * (blockIdx.x / a.hkv) + 1];
+  const int g = bid % a.hkv;
+  const int4 it0 = P.mfma_items[2 * (bid / a.hkv)];
+  const int4 it1 = P.mfma_items[2 * (bid / a.hkv) + 1];
   const int32_t rb = it0.y, nr = it0.z, cs = it0.w;
   const int32_t len = it1.x, gofs = it1.y;
   const bool full = it1.z != 0;
@@ -1184,10 +1219,33 @@ __global__ __launch_bounds__(512) void mfma_partial(PartialArgs a) {
     }
   }
   if constexpr (FUSED) {
-    __shared__ int32_t last_list[kMfmaRows];
-    __shared__ int32_t n_last[1];
-    fused_merge_tail<uint16_t, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, n_last);
+    int32_t* last_list = reinterpret_cast<int32_t*>(lds + Shape::LIST_OFF);
+    fused_merge_tail<uint16_t, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, last_list + kMfmaRows);
   }
+}
+
+// ---------------------------------------------------------------------------
+// One launch for all partial work: the plan's MFMA items take the first
+// n_mfma * Hkv work-groups (dispatched first: the longest), the VALU items
+// the rest, so both kinds share the chip instead of running one after the
+// other.  Block b of either kind takes KV head b % Hkv (n_mfma * Hkv is a
+// multiple of Hkv, so a head keeps its XCD).  One LDS block serves whichever
+// body the work-group runs.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int R, bool FUSED>
+__global__ __launch_bounds__(512) void partial_attention(PartialArgs a) {
+  static_assert(64 * valu_waves<R>() == 512, "both bodies run 8 waves");
+  constexpr int VB = ValuShape<T, D, R>::LDS_B;
+  constexpr int MB = sizeof(T) == 2 ? MfmaShape<D>::LDS_B : 0;
+  __shared__ __attribute__((aligned(1024))) char lds[VB > MB ? VB : MB];
+  const int nm = a.plan.n_mfma * a.hkv;
+  if constexpr (sizeof(T) == 2) {
+    if (static_cast<int>(blockIdx.x) < nm) {
+      mfma_body<D, FUSED>(a, lds, blockIdx.x);
+      return;
+    }
+  }
+  valu_body<T, D, R, FUSED>(a, lds, static_cast<int>(blockIdx.x) - nm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1243,32 +1301,20 @@ static int check_ready(const deft_plan* p, const deft_attn_desc* d) {
 template <typename T, int D>
 static int launch_partials(const PartialArgs& pa, hipStream_t st) {
   const int hkv = pa.hkv;
-  if (pa.plan.n_mfma > 0) {
-    if constexpr (sizeof(T) == 2) {
-      if (pa.fused) hipLaunchKernelGGL((mfma_partial<D, true>), dim3(pa.plan.n_mfma * hkv), dim3(512), 0, st, pa);
-      else hipLaunchKernelGGL((mfma_partial<D, false>), dim3(pa.plan.n_mfma * hkv), dim3(512), 0, st, pa);
-      int rc = hip_check(hipGetLastError(), "launch of mfma_partial");
-      if (rc) return rc;
-    } else {
-      return fail(DEFT_ERR_UNSUPPORTED, "MFMA work for fp32 inputs");
-    }
+  if (sizeof(T) != 2 && pa.plan.n_mfma > 0) return fail(DEFT_ERR_UNSUPPORTED, "MFMA work for fp32 inputs");
+  const dim3 grid((pa.plan.n_mfma + pa.plan.n_valu) * hkv), block(512);
+  if (grid.x == 0) return DEFT_OK;
+  // the VALU body's row capacity: 4 when every VALU item fits, else 8
+  static_assert(kValuRows == 8, "VALU row capacities are 4 and 8");
+  const bool r4 = pa.max_valu_rows <= 4;
+  if (pa.fused) {
+    if (r4) hipLaunchKernelGGL((partial_attention<T, D, 4, true>), grid, block, 0, st, pa);
+    else hipLaunchKernelGGL((partial_attention<T, D, 8, true>), grid, block, 0, st, pa);
+  } else {
+    if (r4) hipLaunchKernelGGL((partial_attention<T, D, 4, false>), grid, block, 0, st, pa);
+    else hipLaunchKernelGGL((partial_attention<T, D, 8, false>), grid, block, 0, st, pa);
   }
-  if (pa.plan.n_valu > 0) {
-    const dim3 grid(pa.plan.n_valu * hkv);
-    const int rows = pa.max_valu_rows;
-    static_assert(kValuRows == 8, "VALU row capacities are 4 and 8");
-    const dim3 b4(64 * valu_waves<4>()), b8(64 * valu_waves<8>());
-    if (pa.fused) {
-      if (rows <= 4) hipLaunchKernelGGL((valu_partial<T, D, 4, true>), grid, b4, 0, st, pa);
-      else hipLaunchKernelGGL((valu_partial<T, D, 8, true>), grid, b8, 0, st, pa);
-    } else {
-      if (rows <= 4) hipLaunchKernelGGL((valu_partial<T, D, 4, false>), grid, b4, 0, st, pa);
-      else hipLaunchKernelGGL((valu_partial<T, D, 8, false>), grid, b8, 0, st, pa);
-    }
-    int rc = hip_check(hipGetLastError(), "launch of valu_partial");
-    if (rc) return rc;
-  }
-  return DEFT_OK;
+  return hip_check(hipGetLastError(), "launch of partial_attention");
 }
 
 static int run_partials(const void* q, const void* k, const void* v, const int32_t* bt,
