@@ -982,21 +982,24 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-  // LDS byte offsets (within a stage) of this lane's operand fragments: K
-  // fragment n = (ks, tt) for S, and the two halves of V^T d-tile dt for PV.
+  // LDS byte offsets (from the block's LDS base: stage 0 of this split's
+  // ring; stage 1 adds STAGE_B as an immediate) of this lane's operand
+  // fragments: K fragment n = (ks, tt) for S, and the two halves of V^T
+  // d-tile dt for PV.
   const int rk0 = 8 * (lr >> 2) + (lr & 3);   // K rows of this lane, per token tile
   int koff[2 * KS], voff[DT][2];
 #pragma unroll
   for (int n = 0; n < 2 * KS; ++n) {
     const int ks = n >> 1, R = rk0 + 4 * (n & 1);
-    koff[n] = R * ROWB + (((ks * 4 + lj) ^ (R % CH)) * 16);
+    koff[n] = sp * 2 * STAGE_B + R * ROWB + (((ks * 4 + lj) ^ (R % CH)) * 16);
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int R = 8 * lj + 4 * hh + (lr >> 2);
-      voff[dt][hh] = TILE_B + R * ROWB + (((2 * dt + ((lr & 3) >> 1)) ^ (R % CH)) * 16) + 8 * (lr & 1);
+      voff[dt][hh] = sp * 2 * STAGE_B + TILE_B + R * ROWB + (((2 * dt + ((lr & 3) >> 1)) ^ (R % CH)) * 16) +
+                     8 * (lr & 1);
     }
 
   if (sp < nsteps) {
@@ -1046,23 +1049,41 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     const char* ptr[NI];
     if (next) load_ptrs(step + NSPLIT, ptr);
 
-    // S^T = K Q^T; fragment n = (ks, tt) is read one group ahead of its MFMAs.
+    // S^T = K Q^T.  All of the step's K fragments (n = (ks, tt)) are read up
+    // front, so the MFMAs wait for the LDS latency once, not once per group.
     // Waves raise their issue priority around MFMA runs so that the SIMD's
     // other wave fills the gaps with its softmax arithmetic.
+    bf16x8 kfr[2 * KS];
+#pragma unroll
+    for (int n = 0; n < 2 * KS; ++n) kfr[n] = *reinterpret_cast<const bf16x8*>(smem + STG * STAGE_B + koff[n]);
     __builtin_amdgcn_s_setprio(1);
     f32x4 sacc[2][NRT];
-    bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + koff[0]);
 #pragma unroll
     for (int n = 0; n < 2 * KS; ++n) {
-      const bf16x8 kn = *reinterpret_cast<const bf16x8*>(kb + koff[n + 1 < 2 * KS ? n + 1 : n]);
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
         sacc[n & 1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            kf, qf[rt][n >> 1], n < 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[n & 1][rt], 0, 0, 0);
+            kfr[n], qf[rt][n >> 1], n < 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[n & 1][rt], 0, 0, 0);
       if (next && (n & 1)) lds_dma16(ptr[n >> 1], nd + (n >> 1) * 1024);
-      kf = kn;
     }
     __builtin_amdgcn_s_setprio(0);
+
+    // V^T fragments for the PV product, read now so their LDS latency is
+    // hidden behind the softmax.  They come from transpose reads of the
+    // token-major rows: within each 16-lane group, ds_read_b64_tr_b16 hands
+    // lane i element (i % 4) of the 8 bytes that lane 4k + i/4 addresses, as
+    // its k-th element.  Lane (lr, lj) addresses row 8lj + 4h' + lr/4 at d
+    // 16dt + 4(lr % 4), so it receives V[8lj + 4h' + k][16dt + lr], k = 0..3.
+    bf16x8 vfr[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      u32x2 half[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        half[hh] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                       (lds_s16x4_t)(smem + STG * STAGE_B + voff[dt][hh])));
+      vfr[dt] = __builtin_bit_cast(bf16x8, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
+    }
 
     // Mask and online softmax.  Lane holds tokens base + 8*lj + e of row
     // 32h + rt*16 + lr; scores stay in raw units, exp2 folds in scale*log2(e).
@@ -1118,30 +1139,14 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
       l_part[rt] = ls;
     }
 
-    // O^T += V^T P^T.  V^T fragments come from LDS transpose reads of the
-    // token-major rows: within each 16-lane group, ds_read_b64_tr_b16 hands
-    // lane i element (i % 4) of the 8 bytes that lane 4k + i/4 addresses, as
-    // its k-th element.  Lane (lr, lj) addresses row 8lj + 4h' + lr/4 at d
-    // 16dt + 4(lr % 4), so it receives V[8lj + 4h' + k][16dt + lr], k = 0..3.
-    // Fragments are read one d-tile ahead of their MFMAs.
-    auto vfrag = [&](int dt) {
-      u32x2 half[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        half[hh] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                       (lds_s16x4_t)(kb + voff[dt][hh])));
-      return __builtin_bit_cast(bf16x8, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
-    };
+    // O^T += V^T P^T with the fragments read before the softmax.
     __builtin_amdgcn_s_setprio(1);
-    bf16x8 vf = vfrag(0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 vn = vfrag(dt + 1 < DT ? dt + 1 : dt);
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
-        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rt], o[dt][rt], 0, 0, 0);
+        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[dt], pb[rt], o[dt][rt], 0, 0, 0);
       if (next && (dt & 1)) lds_dma16(ptr[NI / 2 + (dt >> 1)], nd + (NI / 2 + (dt >> 1)) * 1024);
-      vf = vn;
     }
     if (next && h == 0) lds_dma4(mask_src + step + NSPLIT, ring_lds + (STG ^ 1) * STAGE_B + 2 * TILE_B);
     __builtin_amdgcn_s_setprio(0);
