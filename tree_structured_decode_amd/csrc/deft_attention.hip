@@ -227,14 +227,8 @@ __device__ inline void stage_token_rows(int32_t* tok_row, const DevPlan& P, cons
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel: one wave per (query, query head).  Lane i of the wave reads
-// the metadata (slot id, m, l) of the query's i-th slot, so a query's whole
-// slot list costs one round of dependent loads; the partial O rows are then
-// read by four 16-lane groups, group g taking slots g, g + 4, ..., each lane
-// D/16 consecutive elements.  With M = max_s m_s and w_s = exp(m_s - M):
-//   fp32 unnormalised partials   out = sum_s w_s O_s / sum_s w_s l_s
-//   bf16 partials holding O_s/l_s out = sum_s w_s l_s (O_s/l_s) / sum_s w_s l_s
-// Queries with more than 64 slots take several rounds, rescaled online.
+// Merge kernel: four (query, query head) rows per wave, one per 16-lane row
+// of lanes (merge_rows4 below).
 // ---------------------------------------------------------------------------
 
 // Whole-wave reductions without the LDS crossbar: DPP within each row of 16
@@ -263,132 +257,152 @@ __device__ inline float groups4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// EPL consecutive elements of one partial O row (slot-head sh), as fp32.
+// Broadcast lane J of each 16-lane row to the whole row (DPP row_newbcast).
+template <int J>
+__device__ inline int row_bcast(int x) { return __builtin_amdgcn_update_dpp(0, x, 0x150 + J, 0xf, 0xf, false); }
+template <int J>
+__device__ inline float row_bcast(float x) { return __int_as_float(row_bcast<J>(__float_as_int(x))); }
+// Max / sum over each 16-lane row (DPP), in every lane of the row.
+template <typename Op>
+__device__ inline float row_reduce16(float x, Op op) {
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  x = op(x, dpp(x, std::integral_constant<int, 0xB1>{}));    // quad_perm [1,0,3,2]
+  x = op(x, dpp(x, std::integral_constant<int, 0x4E>{}));    // quad_perm [2,3,0,1]
+  x = op(x, dpp(x, std::integral_constant<int, 0x141>{}));   // row_half_mirror
+  return op(x, dpp(x, std::integral_constant<int, 0x140>{}));   // row_mirror
+}
+
+// EPL consecutive elements of one partial O row (slot-head sh) as raw words:
+// bf16 (O / l) or fp32 (unnormalised O).
 template <int D, int EPL>
-__device__ inline void load_partial_row(const MergeArgs& a, int64_t sh, int sub, float* v) {
+struct PartialRow {
+  static constexpr int WORDS = EPL;   // enough for fp32; bf16 uses the first EPL / 2
+  uint32_t w[WORDS];
+};
+template <int D, int EPL>
+__device__ inline void load_partial_row(const MergeArgs& a, int64_t sh, int sub, PartialRow<D, EPL>& r) {
   if (a.po_bf16) {
     const uint16_t* src = reinterpret_cast<const uint16_t*>(a.po) + sh * D + sub * EPL;
     if constexpr (EPL == 8) {
-      Elem<uint16_t>::unpack(*reinterpret_cast<const u32x4*>(src), v);
-    } else {
-      const u32x2 r = *reinterpret_cast<const u32x2*>(src);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        v[2 * e] = __uint_as_float(r[e] << 16);
-        v[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
-      }
+      for (int e = 0; e < 4; ++e) r.w[e] = v[e];
+    } else {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+      r.w[0] = v[0];
+      r.w[1] = v[1];
     }
   } else {
     const float* src = a.po + sh * D + sub * EPL;
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) {
-      const f32x4 r = *reinterpret_cast<const f32x4*>(src + e);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + e);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[e + k] = r[k];
+      for (int k = 0; k < 4; ++k) r.w[e + k] = v[k];
     }
   }
 }
+template <int D, int EPL>
+__device__ inline float partial_elem(const MergeArgs& a, const PartialRow<D, EPL>& r, int e) {
+  if (a.po_bf16) return __uint_as_float(e & 1 ? (r.w[e >> 1] & 0xffff0000u) : (r.w[e >> 1] << 16));
+  return __uint_as_float(r.w[e]);
+}
 
-// Merge of one (query qi, query head h) by one whole wave.
+// Merge of up to four (query, query head) rows per wave, one per 16-lane
+// row of lanes; `code` = qi * Hq + h for this lane's row, or -1 for none.
+// Lane sub of a row reads the metadata (slot id, m, l) of the row's slots
+// sub, sub + 16, ... and D/16 consecutive elements of every slot's partial O
+// row, so a row costs two rounds of dependent loads (the slot ids, then m, l
+// and the O rows together).  With M = max_s m_s and w_s = exp(m_s - M):
+//   fp32 unnormalised partials   out = sum_s w_s O_s / sum_s w_s l_s
+//   bf16 partials holding O_s/l_s out = sum_s w_s l_s (O_s/l_s) / sum_s w_s l_s
+// Rows with more than 16 slots take several rounds, rescaled online.
 template <typename T, int D>
-__device__ void merge_query_head(const MergeArgs& a, int qi, int h) {
+__device__ void merge_rows4(const MergeArgs& a, int code) {
   constexpr int EPL = D / 16;      // elements per lane
-  constexpr int KU = 4;            // slots per group read before any is accumulated
-  constexpr int PER_G = EPL / 4;   // output elements each lane stores
-  const int lane = threadIdx.x & 63;
-  const int grp = lane >> 4, sub = lane & 15;
-  // The query's slot list: fixed stride (padded with -1, read without a
+  const int lane = threadIdx.x & 63, sub = lane & 15;
+  const bool live = code >= 0;
+  const int qi = live ? code / a.hq : 0, h = live ? code % a.hq : 0;
+  // The row's slot list: fixed stride (padded with -1, read without a
   // dependent offset lookup) or CSR.
   const int32_t* list;
   int cnt;
   if (a.merge_stride > 0) {
     list = a.merge_slots + static_cast<size_t>(qi) * a.merge_stride;
-    cnt = a.merge_stride;
+    cnt = live ? a.merge_stride : 0;
   } else {
     const int s0 = a.query_slot_offsets[qi];
     list = a.query_slots + s0;
-    cnt = a.query_slot_offsets[qi + 1] - s0;
+    cnt = live ? a.query_slot_offsets[qi + 1] - s0 : 0;
   }
+  const int cmax = static_cast<int>(wave_max(static_cast<float>(cnt)));
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
   float mrun = kNegInf, wsum = 0.f;
-  for (int i0 = 0; i0 < cnt; i0 += 64) {
-    const int nmax = min(64, cnt - i0);
-    const int raw = list[i0 + (lane < nmax ? lane : 0)];
-    // valid entries form a prefix of the round (padding is at the end)
-    const bool ok = lane < nmax && raw >= 0;
-    const int n = __popcll(__ballot(ok));
-    if (n == 0) break;
-    // lanes past the list take its first slot and get weight 0
-    const int slot = ok ? raw : __shfl(raw, 0);
-    const int64_t sh = static_cast<int64_t>(slot) * a.hq + h;
-    const float mv = lane < n ? a.pm[sh] : kNegInf;
-    const float lv = lane < n ? a.pl[sh] : 0.f;
-    // first KU slots of each group, issued before the reductions
-    float vals[KU][EPL];
+  for (int i0 = 0; i0 < cmax; i0 += 16) {
+    const int raw = i0 + sub < cnt ? list[i0 + sub] : -1;
+    const bool ok = raw >= 0;                   // padding entries are -1
+    const int64_t sh = static_cast<int64_t>(ok ? raw : 0) * a.hq + h;
+    const float mv = ok ? a.pm[sh] : kNegInf;
+    const float lv = ok ? a.pl[sh] : 0.f;
+    // every slot's O row of this round, issued before any reduction
+    PartialRow<D, EPL> rows[16];
+    int sj[16];
+    sj[0] = row_bcast<0>(raw); sj[1] = row_bcast<1>(raw); sj[2] = row_bcast<2>(raw); sj[3] = row_bcast<3>(raw);
+    sj[4] = row_bcast<4>(raw); sj[5] = row_bcast<5>(raw); sj[6] = row_bcast<6>(raw); sj[7] = row_bcast<7>(raw);
+    sj[8] = row_bcast<8>(raw); sj[9] = row_bcast<9>(raw); sj[10] = row_bcast<10>(raw); sj[11] = row_bcast<11>(raw);
+    sj[12] = row_bcast<12>(raw); sj[13] = row_bcast<13>(raw); sj[14] = row_bcast<14>(raw); sj[15] = row_bcast<15>(raw);
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int j = grp + 4 * u;
-      const int sj = __shfl(slot, j < n ? j : 0);
-      load_partial_row<D, EPL>(a, static_cast<int64_t>(sj) * a.hq + h, sub, vals[u]);
-    }
-    const float mnew = fmaxf(mrun, wave_max(mv));
+    for (int j = 0; j < 16; ++j)
+      if (sj[j] >= 0) load_partial_row<D, EPL>(a, static_cast<int64_t>(sj[j]) * a.hq + h, sub, rows[j]);
+    const float mnew = fmaxf(mrun, row_reduce16(mv, [](float x, float y) { return fmaxf(x, y); }));
     const float w = mv == kNegInf ? 0.f : __expf(mv - mnew);
     const float wl = w * lv;
     const float wt = a.po_bf16 ? wl : w;      // weight of the stored O row
     const float rescale = mrun == kNegInf ? 0.f : __expf(mrun - mnew);
     mrun = mnew;
-    wsum = wsum * rescale + wave_sum(wl);
+    wsum = wsum * rescale + row_reduce16(wl, [](float x, float y) { return x + y; });
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] *= rescale;
+    float wj[16];
+    wj[0] = row_bcast<0>(wt); wj[1] = row_bcast<1>(wt); wj[2] = row_bcast<2>(wt); wj[3] = row_bcast<3>(wt);
+    wj[4] = row_bcast<4>(wt); wj[5] = row_bcast<5>(wt); wj[6] = row_bcast<6>(wt); wj[7] = row_bcast<7>(wt);
+    wj[8] = row_bcast<8>(wt); wj[9] = row_bcast<9>(wt); wj[10] = row_bcast<10>(wt); wj[11] = row_bcast<11>(wt);
+    wj[12] = row_bcast<12>(wt); wj[13] = row_bcast<13>(wt); wj[14] = row_bcast<14>(wt); wj[15] = row_bcast<15>(wt);
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int j = grp + 4 * u;
-      const float wj = __shfl(wt, j < n ? j : 63);
-      const float wu = j < n ? wj : 0.f;
+    for (int j = 0; j < 16; ++j)
+      if (sj[j] >= 0) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wu, vals[u][e], acc[e]);
-    }
-    for (int j0 = 4 * KU; j0 < n; j0 += 4) {
-      const int j = j0 + grp;
-      const int sj = __shfl(slot, j < n ? j : 0);
-      const float wj = __shfl(wt, j < n ? j : 63);
-      float v[EPL];
-      load_partial_row<D, EPL>(a, static_cast<int64_t>(sj) * a.hq + h, sub, v);
-      const float wu = j < n ? wj : 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wu, v[e], acc[e]);
-    }
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wj[j], partial_elem<D, EPL>(a, rows[j], e), acc[e]);
+      }
   }
-  // sum the four groups; every group then holds the full row
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = groups4_sum(acc[e]);
+  if (!live) return;
   const float inv = 1.f / wsum;
-  // group g stores elements [g * PER_G, (g + 1) * PER_G) of each lane's EPL
-  float x[PER_G];
+  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + sub * EPL;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t pk[EPL / 2];
 #pragma unroll
-  for (int k = 0; k < PER_G; ++k) {
-    x[k] = acc[k];
-#pragma unroll
-    for (int g = 1; g < 4; ++g) x[k] = grp == g ? acc[g * PER_G + k] : x[k];
-    x[k] *= inv;
-  }
-  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + sub * EPL + grp * PER_G;
-  if constexpr (sizeof(T) == 2 && PER_G == 2) {
-    const uint32_t pk = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + ob) = pk;
+    for (int e = 0; e < EPL / 2; ++e)
+      pk[e] = f32_to_bf16(acc[2 * e] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * e + 1] * inv)) << 16);
+    if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ob) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    else *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = u32x2{pk[0], pk[1]};
   } else {
 #pragma unroll
-    for (int k = 0; k < PER_G; ++k) Elem<T>::store(a.out, ob + k, x[k]);
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob + e) =
+          f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
   }
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= a.nq * a.hq) return;           // whole waves leave together
-  merge_query_head<T, D>(a, pair / a.hq, pair % a.hq);
+  const int wave0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
+  if (wave0 >= a.nq * a.hq) return;          // whole waves leave together
+  const int code = wave0 + ((threadIdx.x & 63) >> 4);
+  merge_rows4<T, D>(a, code < a.nq * a.hq ? code : -1);
 }
 
 // ---------------------------------------------------------------------------
@@ -433,13 +447,13 @@ __device__ void fused_merge_tail(const MergeArgs& m, const DevPlan& P, int32_t* 
     if (lane == 0) n_last[r0 / 64] = __popcll(bal);
   }
   __syncthreads();
-  // merge the rows this work-group completed, one wave per row
+  // merge the rows this work-group completed, four per wave
   const int nblk = (nr + 63) / 64;
   for (int b = 0; b < nblk; ++b) {
     const int cnt = n_last[b];
-    for (int k = w; k < cnt; k += nwave) {
-      const int code = last_list[b * 64 + k];
-      merge_query_head<T, D>(m, code / m.hq, code % m.hq);
+    for (int k = 4 * w; k < cnt; k += 4 * nwave) {
+      const int j = k + (lane >> 4);
+      merge_rows4<T, D>(m, j < cnt ? last_list[b * 64 + j] : -1);
     }
   }
 }
@@ -1375,7 +1389,7 @@ static int run_merge(const deft_plan* p, const deft_attn_desc* d, const float* p
   ma.nq = p->num_queries;
   ma.hq = d->num_q_heads;
   ma.po_bf16 = po_bf16 ? 1 : 0;
-  const int blocks = (ma.nq * ma.hq + 3) / 4;
+  const int blocks = (ma.nq * ma.hq + 15) / 16;   // 4 waves of 4 rows
   if (d->dtype == DEFT_DTYPE_BF16) {
     if (d->head_dim == 128) hipLaunchKernelGGL((lse_merge<uint16_t, 128>), dim3(blocks), dim3(256), 0, st, ma);
     else hipLaunchKernelGGL((lse_merge<uint16_t, 64>), dim3(blocks), dim3(256), 0, st, ma);
