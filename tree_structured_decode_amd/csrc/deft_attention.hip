@@ -1037,7 +1037,6 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
       qf[rt][ks] = *reinterpret_cast<const bf16x8*>(smem + STAGE_B + R * ROWB + (((4 * ks + lj) ^ (R % CH)) * 16));
     }
   lds_barrier();
-  static_assert(2 * KS == NI && DT == NI, "the next step's loads are spread one per two MFMA groups");
 
   // One step on ring stage STG (a compile-time constant, so every LDS address
   // is a per-lane base plus an immediate offset).
@@ -1057,36 +1056,43 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     const char* kb = ring + STG * STAGE_B;
     const uint32_t* mb = reinterpret_cast<const uint32_t*>(kb + 2 * TILE_B);
     const uint32_t nd = ring_lds + (STG ^ 1) * STAGE_B + h * TILE_B;   // this wave's half of the other stage
-    // The next step's loads are spread over this step's MFMAs (one after
-    // every second MFMA group), so the wave keeps the matrix unit busy while
-    // the memory pipeline takes them.
     const char* ptr[NI];
     if (next) load_ptrs(step + NSPLIT, ptr);
 
-    // S^T = K Q^T.  All of the step's K fragments (n = (ks, tt)) are read up
-    // front, so the MFMAs wait for the LDS latency once, not once per group.
-    // Waves raise their issue priority around MFMA runs so that the SIMD's
-    // other wave fills the gaps with its softmax arithmetic.
+    // The step runs row tile by row tile so that each tile's softmax
+    // arithmetic is issued between the MFMAs of the next product (S of tile
+    // 1, then PV of tile 0) and executes while the matrix unit works:
+    //   S(0) | softmax(0) max  | S(1) + softmax(0) exp | softmax(1) max |
+    //   PV(0) + softmax(1) exp | PV(1)
+    // Waves keep a raised issue priority for the whole step.
+    // The next step's loads go out first (the MFMA runs stay free of
+    // branches, so the arithmetic can be interleaved with them).
+    if (next) {
+#pragma unroll
+      for (int n = 0; n < NI; ++n) lds_dma16(ptr[n], nd + n * 1024);
+      if (h == 0) lds_dma4(mask_src + step + NSPLIT, ring_lds + (STG ^ 1) * STAGE_B + 2 * TILE_B);
+    }
     bf16x8 kfr[2 * KS];
 #pragma unroll
     for (int n = 0; n < 2 * KS; ++n) kfr[n] = *reinterpret_cast<const bf16x8*>(smem + STG * STAGE_B + koff[n]);
     __builtin_amdgcn_s_setprio(1);
+    // S^T = K Q^T for row tile rt: sacc[tt][rt] over the 4 k-steps; n = (ks, tt).
     f32x4 sacc[2][NRT];
+    auto s_tile = [&](auto rtc) {
+      constexpr int rt = decltype(rtc)::value;
 #pragma unroll
-    for (int n = 0; n < 2 * KS; ++n) {
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
+      for (int n = 0; n < 2 * KS; ++n) {
         sacc[n & 1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             kfr[n], qf[rt][n >> 1], n < 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[n & 1][rt], 0, 0, 0);
-      if (next && (n & 1)) lds_dma16(ptr[n >> 1], nd + (n >> 1) * 1024);
-    }
-    __builtin_amdgcn_s_setprio(0);
+      }
+    };
+    s_tile(std::integral_constant<int, 0>{});
 
     // V^T fragments for the PV product, read now so their LDS latency is
-    // hidden behind the softmax.  They come from transpose reads of the
-    // token-major rows: within each 16-lane group, ds_read_b64_tr_b16 hands
-    // lane i element (i % 4) of the 8 bytes that lane 4k + i/4 addresses, as
-    // its k-th element.  Lane (lr, lj) addresses row 8lj + 4h' + lr/4 at d
+    // hidden.  They come from transpose reads of the token-major rows:
+    // within each 16-lane group, ds_read_b64_tr_b16 hands lane i element
+    // (i % 4) of the 8 bytes that lane 4k + i/4 addresses, as its k-th
+    // element.  Lane (lr, lj) addresses row 8lj + 4h' + lr/4 at d
     // 16dt + 4(lr % 4), so it receives V[8lj + 4h' + k][16dt + lr], k = 0..3.
     bf16x8 vfr[DT];
 #pragma unroll
@@ -1106,26 +1112,26 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     // reduced.  The true max is tracked per lane and reduced at the end.  l
     // sums the probabilities as rounded to bf16 for the PV product.
     bf16x8 pb[NRT];
+    float z[NRT][8];
     const int valid_e = len - base - 8 * lj;   // tokens of this lane's 8 that exist
     const bool all_visible = full && valid_e >= 8;
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
+    auto soft_max = [&](auto rtc) {       // mask, maxima, lazy rescale
+      constexpr int rt = decltype(rtc)::value;
       const int rl = WROWS * h + rt * 16 + lr;   // row within the block
       const bool row_ok = rl < nr;
-      float z[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = e < 4 ? sacc[0][rt][e] : sacc[1][rt][e - 4];
+      for (int e = 0; e < 8; ++e) z[rt][e] = e < 4 ? sacc[0][rt][e] : sacc[1][rt][e - 4];
       if (!all_visible) {
         const uint32_t bits = row_ok ? (mb[rl] >> (8 * lj)) & 0xffu : 0u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = (((bits >> e) & 1u) && e < valid_e) ? z[e] : kNegInf;
+        for (int e = 0; e < 8; ++e) z[rt][e] = (((bits >> e) & 1u) && e < valid_e) ? z[rt][e] : kNegInf;
       } else if (!row_ok) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = kNegInf;
+        for (int e = 0; e < 8; ++e) z[rt][e] = kNegInf;
       }
-      float mx = z[0];
+      float mx = z[rt][0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[rt][e]);
       m_true[rt] = fmaxf(m_true[rt], mx);
       // (a running max of -inf is exceeded by any finite score)
       const bool high = mx > m_run[rt] + kRescaleSlack / cl2;
@@ -1139,11 +1145,14 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
       }
+    };
+    auto soft_exp = [&](auto rtc) {       // probabilities, bf16 P, running l
+      constexpr int rt = decltype(rtc)::value;
       // a row with nothing visible yet keeps m = -inf; its z are all -inf too
       const float mc = m_run[rt] == kNegInf ? 0.f : m_run[rt] * cl2;
       f32x8 p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(z[e], cl2, -mc));   // z = -inf gives 0
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(z[rt][e], cl2, -mc));   // z = -inf gives 0
       pb[rt] = __builtin_convertvector(p, bf16x8);
       const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
       float ls = l_part[rt];
@@ -1151,18 +1160,36 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
       for (int e = 0; e < 8; e += 2)
         ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[rt][e], pb[rt][e + 1]}, one, ls, false);
       l_part[rt] = ls;
-    }
-
-    // O^T += V^T P^T with the fragments read before the softmax.
-    __builtin_amdgcn_s_setprio(1);
+    };
+    // O^T += V^T P^T for row tile rt.
+    auto pv_tile = [&](auto rtc) {
+      constexpr int rt = decltype(rtc)::value;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
+      for (int dt = 0; dt < DT; ++dt) {
         o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[dt], pb[rt], o[dt][rt], 0, 0, 0);
-      if (next && (dt & 1)) lds_dma16(ptr[NI / 2 + (dt >> 1)], nd + (NI / 2 + (dt >> 1)) * 1024);
-    }
-    if (next && h == 0) lds_dma4(mask_src + step + NSPLIT, ring_lds + (STG ^ 1) * STAGE_B + 2 * TILE_B);
+      }
+    };
+    // one MFMA, then up to three VALU instructions, for each MFMA of the run
+    auto interleave = [] {
+#pragma unroll
+      for (int k = 0; k < DT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    };
+    static_assert(NRT == 2 && 2 * KS == DT, "the schedule is written for two row tiles");
+    soft_max(std::integral_constant<int, 0>{});
+    s_tile(std::integral_constant<int, 1>{});
+    soft_exp(std::integral_constant<int, 0>{});
+    interleave();
+    // keep tile 0's probabilities here (the compiler would otherwise sink
+    // them past tile 1's branches, next to their use)
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[0])), "v"(l_part[0]));
+    soft_max(std::integral_constant<int, 1>{});
+    pv_tile(std::integral_constant<int, 0>{});
+    soft_exp(std::integral_constant<int, 1>{});
+    interleave();
+    pv_tile(std::integral_constant<int, 1>{});
     __builtin_amdgcn_s_setprio(0);
   };
   for (int i = 0; i < iters; i += 2) {
