@@ -191,9 +191,10 @@ template <int RPI, int NT, int N, typename Mid>
 __device__ inline void stage_token_rows_n(int32_t* tok_row, const DevPlan& P, const int32_t* bt,
                                           int32_t cs, int32_t len, int32_t mul, int32_t add, Mid mid) {
   // N fixed loads per thread and no branches: indices past the chunk end
-  // re-read its last token, and their entries (t < N * NT <= kMaxChunkTokens,
-  // beyond the chunk's steps or masked in its last step) are stored but never
-  // used.  A conditional store would let the compiler sink the loads into it
+  // re-read its last token, and their entries (t < N * NT <= kMaxChunkTokens)
+  // are stored too, so every 32-token step up to N * NT has valid rows (the
+  // MFMA body reads a partial last step whole; its extra tokens are masked).
+  // A conditional store would also let the compiler sink the loads into it
   // and serialise them.
   int32_t lt[N];
 #pragma unroll
@@ -955,21 +956,15 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   for (int c = 0; c < NSW; ++c)
     lbase[c] = reinterpret_cast<const char*>(h ? vp : kp) + (lch ^ ((c * RPI + lrow) % CH)) * 16;
   auto load_ptrs = [&](int step, const char** ptr) {
-    const int base = step * 32;
+    // (the staged rows run to a multiple of 512 tokens, entries past the
+    // chunk end holding its last token, so a partial last step needs no
+    // special case)
     int32_t rows[NI];
-    if (base + 32 <= len) {
-      const int32_t* tr = tok_row + base + lrow * NI;   // the permuted layout
+    const int32_t* tr = tok_row + step * 32 + lrow * NI;   // the permuted layout
 #pragma unroll
-      for (int n = 0; n < NI; n += 4) {
-        const int4 v4 = *reinterpret_cast<const int4*>(tr + n);
-        rows[n] = v4.x; rows[n + 1] = v4.y; rows[n + 2] = v4.z; rows[n + 3] = v4.w;
-      }
-    } else {
-#pragma unroll
-      for (int n = 0; n < NI; ++n) {
-        const int t = min(base + n * RPI + lrow, len - 1);
-        rows[n] = tok_row[(t & ~31) + (t % RPI) * (32 / RPI) + (t & 31) / RPI];
-      }
+    for (int n = 0; n < NI; n += 4) {
+      const int4 v4 = *reinterpret_cast<const int4*>(tr + n);
+      rows[n] = v4.x; rows[n + 1] = v4.y; rows[n + 2] = v4.z; rows[n + 3] = v4.w;
     }
 #pragma unroll
     for (int n = 0; n < NI; ++n)
