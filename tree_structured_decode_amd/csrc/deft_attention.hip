@@ -250,6 +250,22 @@ __device__ inline float wave_reduce(float x, Op op) {
 }
 __device__ inline float wave_max(float x) { return wave_reduce(x, [](float a, float b) { return fmaxf(a, b); }); }
 __device__ inline float wave_sum(float x) { return wave_reduce(x, [](float a, float b) { return a + b; }); }
+// Reduction over lanes l ^ k for k = LPT .. 32 (the lanes that hold the same
+// position of different LPT-lane groups), in every lane: DPP row_ror:8 for
+// the lane^8 exchange within a 16-lane row, then permlane swaps.
+template <int LPT, typename Op>
+__device__ inline float cross_group_reduce(float x, Op op) {
+  static_assert(LPT == 8 || LPT == 16 || LPT == 32, "group width");
+  if constexpr (LPT <= 8)
+    x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));
+  if constexpr (LPT <= 16) {
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
 // Sum of lanes l, l^16, l^32, l^48 (the four 16-lane groups), in every lane.
 __device__ inline float groups4_sum(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -552,7 +568,12 @@ struct ValuShape {
 template <typename T, int D, int R, bool FUSED>
 __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int bid) {
   constexpr int EB = sizeof(T);
-  constexpr int EPL = 16 / EB;                     // elements per lane (16 bytes)
+  // bytes of each K and V row a lane holds: 32 for bf16 d=128 with up to 4
+  // rows (8 lanes per token: the per-token softmax work is shared by fewer
+  // lanes), else 16 (the rows' accumulators would not fit)
+  constexpr int LB = (EB == 2 && D == 128 && R <= 4) ? 32 : 16;
+  constexpr int NLD = LB / 16;                     // 16-byte reads per lane and row
+  constexpr int EPL = LB / EB;                     // elements per lane
   constexpr int LPT = D / EPL;                     // lanes per token
   constexpr int TPW = 64 / LPT;                    // tokens per wave pass
   // two waves per SIMD (latency hiding) while the rows' registers allow it
@@ -670,7 +691,7 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
 #pragma unroll
   for (int i = 0; i < NSTG - 1; ++i)
     if (i < my_steps) issue(i, i);
-  constexpr int QW = 4;   // 32-bit words of Q per lane and row
+  constexpr int QW = LB / 4;   // 32-bit words of Q per lane and row
   uint32_t qv[R][QW];
   for (int i = 0; i < my_steps; ++i) {
     const int stage = i % NSTG;
@@ -685,9 +706,12 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
       const char* qs = ring + (NSTG - 1) * STAGE_B;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(qs + r * ROWB + li * 16);
 #pragma unroll
-        for (int e = 0; e < QW; ++e) qv[r][e] = raw[e];
+        for (int j = 0; j < NLD; ++j) {
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(qs + r * ROWB + li * LB + j * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qv[r][4 * j + e] = raw[e];
+        }
       }
       // the Q reads complete before this stage is refilled below
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
@@ -702,22 +726,24 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
     for (int r = 0; r < R; ++r) mbits[r] = mw[r] >> (base & 31);
     // the step's K and V fragments for every pass, read before any is used
     constexpr int NPASS = STEP_T / TPW;
-    u32x4 kfr[NPASS], vfr[NPASS];
+    u32x4 kfr[NPASS][NLD], vfr[NPASS][NLD];
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int tr = ps * TPW + tg;
-      const int sw = (li ^ (tr % RPI)) * 16;
-      kfr[ps] = *reinterpret_cast<const u32x4*>(kb + tr * ROWB + sw);
-      vfr[ps] = *reinterpret_cast<const u32x4*>(kb + TILE_B + tr * ROWB + sw);
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int sw = ((li * NLD + j) ^ (tr % RPI)) * 16;   // slot of chunk li * NLD + j
+        kfr[ps][j] = *reinterpret_cast<const u32x4*>(kb + tr * ROWB + sw);
+        vfr[ps][j] = *reinterpret_cast<const u32x4*>(kb + TILE_B + tr * ROWB + sw);
+      }
     }
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int tr = ps * TPW + tg;                 // token within the step
       const bool valid = base + tr < len;
-      const u32x4& kr = kfr[ps];
-      const u32x4& vr = vfr[ps];
       float vf[EPL];
-      Elem<T>::unpack(vr, vf);
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) Elem<T>::unpack(vfr[ps][j], vf + j * (16 / EB));
       // All rows side by side (independent chains): scores, group sums,
       // mask, one branch for the rare rise of any running max, then the
       // probability and the O and l updates.
@@ -726,10 +752,11 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
       for (int r = 0; r < R; ++r) {
         float sc = 0.f;
         if constexpr (EB == 2) {
-          sc = dot8_bf16(kr, qv[r], sc);
+#pragma unroll
+          for (int j = 0; j < NLD; ++j) sc = dot8_bf16(kfr[ps][j], qv[r] + 4 * j, sc);
         } else {
 #pragma unroll
-          for (int e = 0; e < QW; ++e) sc = fmaf(__uint_as_float(qv[r][e]), __uint_as_float(kr[e]), sc);
+          for (int e = 0; e < QW; ++e) sc = fmaf(__uint_as_float(qv[r][e]), __uint_as_float(kfr[ps][0][e]), sc);
         }
         z[r] = sc;
       }
@@ -774,20 +801,12 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
   float* red = reinterpret_cast<float*>(smem);   // [NW][R][D + 2]
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    float mx = m_true[r];
+    auto add = [](float x, float y) { return x + y; };
+    const float mx = cross_group_reduce<LPT>(m_true[r], [](float x, float y) { return fmaxf(x, y); });
+    const float f = (m_run[r] == kNegInf) ? 0.f : fast_exp2(m_run[r] - mx);
+    const float lsum = cross_group_reduce<LPT>(l[r] * f, add);
 #pragma unroll
-    for (int x = LPT; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
-    const float f = (m_run[r] == kNegInf) ? 0.f : exp2f(m_run[r] - mx);
-    float lsum = l[r] * f;
-#pragma unroll
-    for (int x = LPT; x < 64; x <<= 1) lsum += __shfl_xor(lsum, x);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float ov = o[r][e] * f;
-#pragma unroll
-      for (int x = LPT; x < 64; x <<= 1) ov += __shfl_xor(ov, x);
-      o[r][e] = ov;
-    }
+    for (int e = 0; e < EPL; ++e) o[r][e] = cross_group_reduce<LPT>(o[r][e] * f, add);
     if (tg == 0) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) red[(w * R + r) * (D + 2) + li * EPL + e] = o[r][e];
@@ -798,23 +817,30 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
     }
   }
   lds_barrier();
-  for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
-    const int r = idx / D, e = idx % D;
+  // two consecutive elements of one row per thread
+  for (int idx = threadIdx.x; idx < nr * (D / 2); idx += blockDim.x) {
+    const int r = idx / (D / 2), e = 2 * (idx % (D / 2));
     float mx = kNegInf;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, red[(ww * R + r) * (D + 2) + D]);
-    float ov = 0.f, lsum = 0.f;
+    float o0 = 0.f, o1 = 0.f, lsum = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      const float mw = red[(ww * R + r) * (D + 2) + D];
-      const float f = (mw == kNegInf) ? 0.f : exp2f(mw - mx);
-      ov += f * red[(ww * R + r) * (D + 2) + e];
-      lsum += f * red[(ww * R + r) * (D + 2) + D + 1];
+      const float* rw = red + (ww * R + r) * (D + 2);
+      const float f = (rw[D] == kNegInf) ? 0.f : fast_exp2(rw[D] - mx);
+      o0 = fmaf(f, rw[e], o0);
+      o1 = fmaf(f, rw[e + 1], o1);
+      lsum = fmaf(f, rw[D + 1], lsum);
     }
     const int row = rb + r;
     const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
-    if (a.po_bf16) reinterpret_cast<uint16_t*>(a.po)[sh * D + e] = f32_to_bf16(ov / lsum);
-    else a.po[sh * D + e] = ov;
+    if (a.po_bf16) {
+      const float inv = 1.f / lsum;
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.po) + sh * D + e) =
+          f32_to_bf16(o0 * inv) | (static_cast<uint32_t>(f32_to_bf16(o1 * inv)) << 16);
+    } else {
+      *reinterpret_cast<u32x2*>(a.po + sh * D + e) = u32x2{__float_as_uint(o0), __float_as_uint(o1)};
+    }
     if (e == 0) {
       a.pm[sh] = mx == kNegInf ? kNegInf : mx * kLn2;
       a.pl[sh] = lsum;
