@@ -288,18 +288,19 @@ def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = 
        one query per leaf; chunks of 64 tokens.
     2: bf16, 32 q / 8 KV heads, d 128; 4096-token prefix plus a 64-node
        Medusa tree (branching 4/3/2/2), every tree node a query; values
-       scaled by 1/sqrt(d) unless `unscaled`.
+       scaled by 1/sqrt(d) unless `unscaled`; chunks of 544 tokens.
     3: bf16, 32/8, d 128; 2048-token prompt with 32 branches of 512 tokens,
        one query per branch; the 1152 pages in a seeded random order.
     4: bf16, 32/8, d 128; 1000-token root and a depth-6 reasoning tree
-       (branching 1..5, segments 20..400), first 100 leaves, one query each.
+       (branching 1..5, segments 20..400), first 100 leaves, one query each;
+       chunks of 1536 tokens.
     5: bf16, 64 q / 8 KV heads, d 128; 32768-token prefix plus a 256-node
        Medusa tree (branching 8/4/2/2/1), every tree node a query; pages at
        random positions of a `pool_pages` pool (default: just the used pages).
     6: bf16, 32/8, d 128; multi-token query nodes: a 2048-token prompt and a
        32-node Medusa tree (branching 4/3/2) whose nodes hold 8 draft tokens
        each, every draft token a query (256 queries, causal inside a node);
-       chunks of 256 tokens; values scaled by 1/sqrt(d).
+       chunks of 1024 tokens; values scaled by 1/sqrt(d).
     """
     rng = np.random.default_rng(seed)
     if cfg == 1:
@@ -311,7 +312,7 @@ def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = 
         tp, depths = medusa_token_tree(rng, (4, 3, 2, 2), 64)
         p, s, qn = prefix_plus_token_tree(4096, tp)
         scale = 1.0 if unscaled else 1.0 / math.sqrt(128)
-        return make_workload(WORKLOADS[2], p, s, qn, chunk_tokens=chunk_tokens or 520,
+        return make_workload(WORKLOADS[2], p, s, qn, chunk_tokens=chunk_tokens or 544,
                              hq=32, hkv=8, d=128, dtype=torch.bfloat16, seed=seed,
                              placement=placement or "identity", value_scale=scale,
                              meta={"depths": depths})
@@ -322,7 +323,7 @@ def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = 
                              placement=placement or "permuted")
     if cfg == 4:
         p, s, qn = reasoning_tree(rng)
-        return make_workload(WORKLOADS[4], p, s, qn, chunk_tokens=chunk_tokens or 512,
+        return make_workload(WORKLOADS[4], p, s, qn, chunk_tokens=chunk_tokens or 1536,
                              hq=32, hkv=8, d=128, dtype=torch.bfloat16, seed=seed,
                              placement=placement or "identity")
     if cfg == 5:
@@ -338,7 +339,7 @@ def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = 
         tp, depths = medusa_token_tree(rng, (4, 3, 2), 32)
         p, s, _ = prefix_plus_token_tree(2048, tp)
         p, s, qn, ql = multi_token_nodes(p, s, 8)
-        return make_workload(WORKLOADS[6], p, s, qn, chunk_tokens=chunk_tokens or 256,
+        return make_workload(WORKLOADS[6], p, s, qn, chunk_tokens=chunk_tokens or 1024,
                              hq=32, hkv=8, d=128, dtype=torch.bfloat16, seed=seed,
                              placement=placement or "permuted", value_scale=1.0 / math.sqrt(128),
                              meta={"depths": depths}, query_lens=ql)
