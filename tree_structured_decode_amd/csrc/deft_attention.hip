@@ -962,8 +962,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   // Row of the mask word this lane loads (lane i <-> row i of the block).
   const int32_t mask_slot = gofs + (rb + (lane < nr ? lane : 0)) / a.grp;
   if (threadIdx.x < 2 * NSPLIT) pair_ready[threadIdx.x >> 1][threadIdx.x & 1] = -1;
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // this wave's Q copies are in LDS
-  lds_barrier();
+  lds_barrier();   // the staged token rows are visible (the Q copies may still be in flight)
 
   char* ring = smem + sp * 2 * STAGE_B;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
@@ -1037,13 +1036,24 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
                      8 * (lr & 1);
     }
 
+  // The split's first step goes out before waiting for the Q copies; then
+  // each wave waits for its own Q copies only (they are older than the step's
+  // loads) and a barrier makes all of them visible.
   if (sp < nsteps) {
     const char* ptr[NI];
     load_ptrs(sp, ptr);
 #pragma unroll
     for (int n = 0; n < NI; ++n) lds_dma16(ptr[n], ring_lds + h * TILE_B + n * 1024);
-    if (h == 0) lds_dma4(mask_src + sp, ring_lds + 2 * TILE_B);
+    if (h == 0) {
+      lds_dma4(mask_src + sp, ring_lds + 2 * TILE_B);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NI + 1));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NI));
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
+  lds_barrier();
   // Q^T fragments (B operand of S^T = K Q^T) of this wave's 32 rows: lane
   // (lr, lj) takes d = 32 ks + 8 lj .. +7 of row R = 32h + 16rt + lr, i.e.
   // chunk 4 ks + lj, stored in slot (4 ks + lj) ^ (R % CH).  Every wave reads
