@@ -90,6 +90,27 @@ def test_random_trees(seed, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("branches", [1, 2, 20])
+def test_kernel_paths(branches, d, dtype):
+    """Each body and row capacity on purpose: a 300-token prompt shared by
+    `branches` queries, each on its own 90-token branch, 4 query heads per KV
+    head.  The prompt's group has 4 * branches rows (1 -> the 4-row VALU body,
+    whose bf16 d=128 lanes hold 32 bytes; 2 -> the 8-row VALU body; 20 -> the
+    MFMA body for bf16) and every branch chunk has 4 rows."""
+    p, s, qn = W.shared_prompt_branches(300, branches, 90)
+    wl = W.make_workload("paths", p, s, qn, chunk_tokens=96, hq=8, hkv=2, d=d, dtype=dtype,
+                         seed=branches * 7 + d, placement="scattered",
+                         pool_pages=2 * (-(-int(s.sum()) // 16)) + 5, value_scale=1.0 / np.sqrt(d))
+    say("paths", branches, d, str(dtype))
+    got, _ = run_gpu(wl)
+    want = oracle_out(wl)
+    check_close(got, want, TOL[dtype], f"paths {branches} {d}")
+    if dtype == torch.bfloat16:
+        _rms_check(got, want, f"paths {branches} {d}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_zero_keys_give_segment_weighted_mean(dtype):
     rng = np.random.default_rng(77)
     p, s, qn = W.random_tree(rng, 40, 1, 60, 30, forest_prob=0.05)
