@@ -110,6 +110,25 @@ def test_kernel_paths(branches, d, dtype):
         _rms_check(got, want, f"paths {branches} {d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("c", [16, 48, 144, 160, 176])
+def test_mfma_step_remainders(c, d):
+    """Chunk sizes whose 32-token step count leaves one or two steps after the
+    last whole round of the MFMA body's four token splits (1, 2, 5, 5 and 6
+    steps; partial last steps at 16, 48, 144 and 176).  20 branches on a
+    300-token prompt give MFMA groups of 80 rows (a full and a partial row
+    block), and the chunks across the prompt's end carry partial masks."""
+    p, s, qn = W.shared_prompt_branches(300, 20, 90)
+    wl = W.make_workload("tail", p, s, qn, chunk_tokens=c, hq=8, hkv=2, d=d, dtype=torch.bfloat16,
+                         seed=c + d, placement="scattered",
+                         pool_pages=2 * (-(-int(s.sum()) // 16)) + 5, value_scale=1.0 / np.sqrt(d))
+    say("tail", c, d)
+    got, _ = run_gpu(wl)
+    want = oracle_out(wl)
+    check_close(got, want, TOL[torch.bfloat16], f"tail {c} {d}")
+    _rms_check(got, want, f"tail {c} {d}")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_zero_keys_give_segment_weighted_mean(dtype):
     rng = np.random.default_rng(77)

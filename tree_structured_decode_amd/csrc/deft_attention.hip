@@ -181,7 +181,9 @@ __device__ inline u32x4 load16(const void* base, int64_t elem_off, int elem_byte
 // Pool row (page * 16 + slot) of every flat token of the chunk, into LDS,
 // stored as row * mul + add.  All flat-to-logical loads are issued before any
 // block-table load so the two dependent lookups cost two memory latencies,
-// not two per token; mid() runs right after the block-table loads are issued
+// not two per token; a chunk whose tokens are one run of consecutive logical
+// tokens (lstart >= 0, its first token's logical index) needs no
+// flat-to-logical lookup at all, only the block-table one.  mid() runs right after the block-table loads are issued
 // (callers issue their own independent loads there, so those overlap the
 // second lookup).  With RPI > 0 the rows of each 32-token step are stored
 // permuted, entry (t % RPI) * (32 / RPI) + (t % 32) / RPI, which puts the rows
@@ -189,7 +191,8 @@ __device__ inline u32x4 load16(const void* base, int64_t elem_off, int elem_byte
 // the work-group size.
 template <int RPI, int NT, int N, typename Mid>
 __device__ inline void stage_token_rows_n(int32_t* tok_row, const DevPlan& P, const int32_t* bt,
-                                          int32_t cs, int32_t len, int32_t mul, int32_t add, Mid mid) {
+                                          int32_t cs, int32_t len, int32_t lstart, int32_t mul, int32_t add,
+                                          Mid mid) {
   // N fixed loads per thread and no branches: indices past the chunk end
   // re-read its last token, and their entries (t < N * NT <= kMaxChunkTokens)
   // are stored too, so every 32-token step up to N * NT has valid rows (the
@@ -197,9 +200,14 @@ __device__ inline void stage_token_rows_n(int32_t* tok_row, const DevPlan& P, co
   // A conditional store would also let the compiler sink the loads into it
   // and serialise them.
   int32_t lt[N];
+  if (lstart >= 0) {
 #pragma unroll
-  for (int k = 0; k < N; ++k)
-    lt[k] = P.flat_to_logical[cs + min(static_cast<int>(threadIdx.x) + k * NT, len - 1)];
+    for (int k = 0; k < N; ++k) lt[k] = lstart + min(static_cast<int>(threadIdx.x) + k * NT, len - 1);
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      lt[k] = P.flat_to_logical[cs + min(static_cast<int>(threadIdx.x) + k * NT, len - 1)];
+  }
   int32_t pg[N];
 #pragma unroll
   for (int k = 0; k < N; ++k) pg[k] = bt[lt[k] >> 4];
@@ -214,17 +222,18 @@ __device__ inline void stage_token_rows_n(int32_t* tok_row, const DevPlan& P, co
 }
 template <int RPI, int NT, typename Mid>
 __device__ inline void stage_token_rows(int32_t* tok_row, const DevPlan& P, const int32_t* bt,
-                                        int32_t cs, int32_t len, int32_t mul, int32_t add, Mid mid) {
+                                        int32_t cs, int32_t len, int32_t lstart, int32_t mul, int32_t add,
+                                        Mid mid) {
   static_assert(kMaxChunkTokens <= 16 * NT, "at most 16 staging batches");
   // N * NT stays within kMaxChunkTokens: N is the power of two at or above
   // ceil(len / NT) and NT divides kMaxChunkTokens.
   static_assert(kMaxChunkTokens % NT == 0, "whole staging batches");
   const int nk = (len + NT - 1) / NT;
-  if (nk <= 1) stage_token_rows_n<RPI, NT, 1>(tok_row, P, bt, cs, len, mul, add, mid);
-  else if (nk <= 2) stage_token_rows_n<RPI, NT, 2>(tok_row, P, bt, cs, len, mul, add, mid);
-  else if (nk <= 4) stage_token_rows_n<RPI, NT, 4>(tok_row, P, bt, cs, len, mul, add, mid);
-  else if (nk <= 8) stage_token_rows_n<RPI, NT, 8>(tok_row, P, bt, cs, len, mul, add, mid);
-  else stage_token_rows_n<RPI, NT, 16>(tok_row, P, bt, cs, len, mul, add, mid);
+  if (nk <= 1) stage_token_rows_n<RPI, NT, 1>(tok_row, P, bt, cs, len, lstart, mul, add, mid);
+  else if (nk <= 2) stage_token_rows_n<RPI, NT, 2>(tok_row, P, bt, cs, len, lstart, mul, add, mid);
+  else if (nk <= 4) stage_token_rows_n<RPI, NT, 4>(tok_row, P, bt, cs, len, lstart, mul, add, mid);
+  else if (nk <= 8) stage_token_rows_n<RPI, NT, 8>(tok_row, P, bt, cs, len, lstart, mul, add, mid);
+  else stage_token_rows_n<RPI, NT, 16>(tok_row, P, bt, cs, len, lstart, mul, add, mid);
 }
 
 // ---------------------------------------------------------------------------
@@ -615,7 +624,7 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
   for (int r = 0; r < R; ++r) qrow[r] = P.slot_query[gofs + (rb + min(r, nr - 1)) / a.grp];
   // token rows as rows of this KV head (pool row * Hkv + g), permuted so a
   // lane's rows of one step are adjacent
-  stage_token_rows<RPI, 64 * NW>(tok_row, P, a.block_table, cs, len, a.hkv, g, [] {});
+  stage_token_rows<RPI, 64 * NW>(tok_row, P, a.block_table, cs, len, it1.w, a.hkv, g, [] {});
   // lane i loads the mask word of row i (rows past nr: the last row's)
   const int32_t mask_slot = gofs + (rb + min(lane, nr - 1)) / a.grp;
   const uint32_t* mask_src = P.slot_mask + static_cast<size_t>(mask_slot) * W;
@@ -949,7 +958,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     qsq[j] = P.slot_query[gofs + (rb + min(R, nr - 1)) / a.grp];
   }
   // token rows are stored as rows of this KV head: pool row * Hkv + g
-  stage_token_rows<RPI, 512>(tok_row, P, a.block_table, cs, len, a.hkv, g, [&] {
+  stage_token_rows<RPI, 512>(tok_row, P, a.block_table, cs, len, it1.w, a.hkv, g, [&] {
 #pragma unroll
     for (int j = 0; j < NQW; ++j) {
       const int R = RPQ * (NQW * w + j) + lane / CH;

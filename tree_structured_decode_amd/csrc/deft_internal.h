@@ -30,7 +30,9 @@ struct WorkItem {                  // two int4 on the device
   int32_t chunk_len;               // work-group reads one record before it
   int32_t group_offset;            // can start on the chunk's token rows
   int32_t full;
-  int32_t pad;
+  int32_t logical_start;           // logical index of the chunk's first token
+                                   // when its tokens are consecutive logical
+                                   // tokens (no flat-to-logical lookup), else -1
 };
 static_assert(sizeof(WorkItem) == 32, "work items are read as two int4");
 

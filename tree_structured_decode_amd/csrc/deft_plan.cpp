@@ -338,9 +338,12 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
     const bool use_mfma = d->dtype == DEFT_DTYPE_BF16 && (rows >= kMfmaMinRows || p->query_centric);
     const int32_t blk = use_mfma ? kMfmaRows : kValuRows;
     const int32_t cs = p->chunk_start[k], len = p->chunk_start[k + 1] - cs;
+    int32_t lstart = p->flat_to_logical[cs];
+    for (int32_t t = 1; t < len && lstart >= 0; ++t)
+      if (p->flat_to_logical[cs + t] != lstart + t) lstart = -1;
     for (int32_t r = 0; r < rows; r += blk)
       (use_mfma ? mfma : valu).push_back({k, r, std::min(blk, rows - r), cs, len, p->group_offsets[k],
-                                          p->chunk_full[k] ? 1 : 0, 0});
+                                          p->chunk_full[k] ? 1 : 0, lstart});
   }
   size_t w = 0;
   auto take = [&](size_t n) { size_t at = w; w = align_words(w + n); return at; };
