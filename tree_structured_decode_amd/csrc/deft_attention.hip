@@ -1011,14 +1011,22 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NRT], m_true[NRT], l_part[NRT];
+  // Per row tile: the running max m_run (raw score units) with its exp2
+  // offset mc = m_run * scale * log2(e) and rescale threshold thr, both
+  // updated only when m_run rises; the lane's true max; and the row sum of
+  // P, accumulated by the matrix core against a tile of ones (every element
+  // of lacc[rt] holds the sum of the lane's row).
+  const float cl2 = a.scale_log2;
+  float m_run[NRT], m_true[NRT], mc[NRT], thr[NRT];
+  f32x4 lacc[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     m_run[rt] = kNegInf;
     m_true[rt] = kNegInf;
-    l_part[rt] = 0.f;
+    mc[rt] = 0.f;
+    thr[rt] = kNegInf;
+    lacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float cl2 = a.scale_log2;
   const int nsteps = (len + 31) / 32;
   const int iters = (nsteps + NSPLIT - 1) / NSPLIT;   // the same for every wave
   typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -1080,6 +1088,10 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
 
   // One step on ring stage STG (a compile-time constant, so every LDS address
   // is a per-lane base plus an immediate offset).
+  // A operand of the row-sum product: 16 rows of ones.
+  const bf16x8 ones8 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f),
+                        static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f),
+                        static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
   auto step_body = [&](auto stg, int i) {
     constexpr int STG = decltype(stg)::value;
     const int step = sp + i * NSPLIT;
@@ -1174,40 +1186,37 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[rt][e]);
       m_true[rt] = fmaxf(m_true[rt], mx);
       // (a running max of -inf is exceeded by any finite score)
-      const bool high = mx > m_run[rt] + kRescaleSlack / cl2;
+      const bool high = mx > thr[rt];
       if (__any(high)) {
         const float rmx = rowmax4(mx);
-        const bool raise = rmx > m_run[rt] + kRescaleSlack / cl2;
+        const bool raise = rmx > thr[rt];
         const float mn = raise ? rmx : m_run[rt];
         const float alpha = raise ? fast_exp2((m_run[rt] - mn) * cl2) : 1.f;
         m_run[rt] = mn;
-        l_part[rt] *= alpha;
+        mc[rt] = mn == kNegInf ? 0.f : mn * cl2;
+        thr[rt] = mn + kRescaleSlack / cl2;
+        lacc[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
       }
     };
-    auto soft_exp = [&](auto rtc) {       // probabilities, bf16 P, running l
+    auto soft_exp = [&](auto rtc) {       // probabilities, bf16 P
       constexpr int rt = decltype(rtc)::value;
-      // a row with nothing visible yet keeps m = -inf; its z are all -inf too
-      const float mc = m_run[rt] == kNegInf ? 0.f : m_run[rt] * cl2;
+      // (a row with nothing visible yet has mc = 0 and z all -inf)
       f32x8 p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(z[rt][e], cl2, -mc));   // z = -inf gives 0
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(z[rt][e], cl2, -mc[rt]));   // z = -inf gives 0
       pb[rt] = __builtin_convertvector(p, bf16x8);
-      const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-      float ls = l_part[rt];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[rt][e], pb[rt][e + 1]}, one, ls, false);
-      l_part[rt] = ls;
     };
-    // O^T += V^T P^T for row tile rt.
+    // O^T += V^T P^T for row tile rt, and l += 1 P^T (the sums of the
+    // probabilities as rounded to bf16 for the product).
     auto pv_tile = [&](auto rtc) {
       constexpr int rt = decltype(rtc)::value;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[dt], pb[rt], o[dt][rt], 0, 0, 0);
       }
+      lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pb[rt], lacc[rt], 0, 0, 0);
     };
     // one MFMA, then up to three VALU instructions, for each MFMA of the run
     auto interleave = [] {
@@ -1224,7 +1233,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     interleave();
     // keep tile 0's probabilities here (the compiler would otherwise sink
     // them past tile 1's branches, next to their use)
-    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[0])), "v"(l_part[0]));
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[0])));
     soft_max(std::integral_constant<int, 1>{});
     pv_tile(std::integral_constant<int, 0>{});
     soft_exp(std::integral_constant<int, 1>{});
@@ -1246,7 +1255,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   // f_q = exp2(m_run_q - M), l = sum f_q l_q, O = sum f_q O_q.
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    const float ls = rowsum4(l_part[rt]);
+    const float ls = lacc[rt][0];
     const float mt = rowmax4(m_true[rt]);
     if (lj == 0) {
       stats[w][rt * 16 + lr][0] = m_run[rt];
