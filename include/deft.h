@@ -244,7 +244,12 @@ int deft_plan_upload(deft_plan* plan, const deft_attn_desc* desc, void* dev_plan
  * desc must equal the desc of the last deft_plan_upload.  workspace_bytes
  * must be at least the size from deft_plan_device_bytes.  block_table
  * entries are not range-checked on the device; an entry outside
- * [0, num_pages) is undefined behaviour.
+ * [0, num_pages) is undefined behaviour.  With the environment variable
+ * DEFT_VALIDATE=1, this call, deft_tree_attention_fused and
+ * deft_partial_attention first copy the entries of the tree's logical pages
+ * to the host on `stream` and synchronise it (so not under graph capture),
+ * and return DEFT_ERR_INVALID_ARGUMENT, launching nothing, if one is out of
+ * range.
  */
 int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_table, const deft_plan* plan, void* out,

@@ -15,6 +15,7 @@ from oracle import attention as OA
 from oracle.plan import ref_plan
 from tree_structured_decode_amd import workloads as W
 from tree_structured_decode_amd import deft as D
+from tree_structured_decode_amd.runner import TreeAttention
 
 from gpu_helpers import DEV, TOL, check_close, gpu_inputs, oracle_out, run_gpu, say
 
@@ -379,3 +380,31 @@ def test_long_context_spec_tree_sampled():
             assert np.isfinite(got).all(), f"C={c} rep {rep}: non-finite output"
             check_close(got[pick], want, 2e-2, f"long context C={c}")
             _rms_check(got[pick], want, f"long context C={c}")
+
+
+def test_validate_block_table_host_check(monkeypatch):
+    """With DEFT_VALIDATE=1 a block-table entry outside [0, num_pages) is
+    reported before anything is launched, and a valid table runs as usual.
+    The pool holds two pages more than desc declares, so the out-of-range
+    entry still names memory that exists."""
+    p, s, qn = W.shared_prompt_branches(64, 2, 32)
+    n_lp = -(-int(s.sum()) // 16)
+    wl = W.make_workload("validate", p, s, qn, chunk_tokens=32, hq=8, hkv=2, d=64,
+                         dtype=torch.float32, seed=11, placement="identity", pool_pages=n_lp + 2)
+    say("validate", n_lp)
+    monkeypatch.setenv("DEFT_VALIDATE", "1")
+    q, kc, vc, bt = gpu_inputs(wl)
+    desc = D.make_desc(wl.dtype, 8, 2, 64, n_lp)
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, 32, desc, device=DEV)
+    bad = bt.clone()
+    bad[1] = n_lp
+    out = torch.full_like(q, float("nan"))
+    with pytest.raises(D.DeftError) as err:
+        ta(q, kc, vc, bad, out)
+    assert err.value.code == D.DEFT_ERR_INVALID_ARGUMENT
+    assert "block_table[1]" in str(err.value)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+    ta(q, kc, vc, bt, out)
+    torch.cuda.synchronize()
+    check_close(out.double().cpu().numpy(), oracle_out(wl), TOL[torch.float32], "validate")

@@ -33,7 +33,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <cstdlib>
+#include <string>
 #include <cstdint>
 #include <type_traits>
 #include <vector>
@@ -1393,6 +1396,29 @@ static int check_ready(const deft_plan* p, const deft_attn_desc* d) {
   return DEFT_OK;
 }
 
+// Opt-in host check of the block table (environment DEFT_VALIDATE=1): the
+// entries of the tree's logical pages are copied back on the stream, which
+// is synchronised, and each must lie in [0, num_pages).  Off by default: the
+// kernels never range-check block-table entries themselves.
+static int validate_block_table(const deft_plan* p, const deft_attn_desc* d, const int32_t* bt,
+                                hipStream_t st) {
+  const char* env = std::getenv("DEFT_VALIDATE");
+  if (!env || env[0] != '1') return DEFT_OK;
+  if (!bt) return fail(DEFT_ERR_INVALID_ARGUMENT, "block_table is NULL");
+  int32_t last = -1;
+  for (int32_t lt : p->flat_to_logical) last = std::max(last, lt);
+  const size_t n = static_cast<size_t>(last / kPageSize + 1);
+  std::vector<int32_t> h(n);
+  hipError_t e = hipMemcpyAsync(h.data(), bt, n * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_check(e, "DEFT_VALIDATE block-table copy");
+  for (size_t i = 0; i < n; ++i)
+    if (h[i] < 0 || h[i] >= d->num_pages)
+      return fail(DEFT_ERR_INVALID_ARGUMENT, "block_table[" + std::to_string(i) + "] = " + std::to_string(h[i]) +
+                                                 " is outside [0, num_pages = " + std::to_string(d->num_pages) + ")");
+  return DEFT_OK;
+}
+
 template <typename T, int D>
 static int launch_partials(const PartialArgs& pa, hipStream_t st) {
   const int hkv = pa.hkv;
@@ -1514,6 +1540,8 @@ int deft_partial_attention(const void* q, const void* k_cache, const void* v_cac
                            int32_t partial_format, void* stream) {
   int rc = deft::check_ready(plan, desc);
   if (rc) return rc;
+  rc = deft::validate_block_table(plan, desc, block_table, static_cast<hipStream_t>(stream));
+  if (rc) return rc;
   rc = check_format(desc, partial_format);
   if (rc) return rc;
   return deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, static_cast<float*>(part_o),
@@ -1537,6 +1565,8 @@ int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
                         const deft_attn_desc* desc, void* workspace, size_t workspace_bytes,
                         void* stream) {
   int rc = deft::check_ready(plan, desc);
+  if (rc) return rc;
+  rc = deft::validate_block_table(plan, desc, block_table, static_cast<hipStream_t>(stream));
   if (rc) return rc;
   if (!workspace || !out) return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace and out must not be NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
@@ -1562,6 +1592,8 @@ int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_
                               const deft_attn_desc* desc, void* workspace, size_t workspace_bytes,
                               void* stream) {
   int rc = deft::check_ready(plan, desc);
+  if (rc) return rc;
+  rc = deft::validate_block_table(plan, desc, block_table, static_cast<hipStream_t>(stream));
   if (rc) return rc;
   if (!workspace || !out) return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace and out must not be NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
