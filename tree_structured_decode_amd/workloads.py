@@ -293,14 +293,14 @@ def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = 
        one query per branch; the 1152 pages in a seeded random order.
     4: bf16, 32/8, d 128; 1000-token root and a depth-6 reasoning tree
        (branching 1..5, segments 20..400), first 100 leaves, one query each;
-       chunks of 1536 tokens.
+       chunks of 2176 tokens.
     5: bf16, 64 q / 8 KV heads, d 128; 32768-token prefix plus a 256-node
        Medusa tree (branching 8/4/2/2/1), every tree node a query; pages at
        random positions of a `pool_pages` pool (default: just the used pages).
     6: bf16, 32/8, d 128; multi-token query nodes: a 2048-token prompt and a
        32-node Medusa tree (branching 4/3/2) whose nodes hold 8 draft tokens
        each, every draft token a query (256 queries, causal inside a node);
-       chunks of 1024 tokens; values scaled by 1/sqrt(d).
+       chunks of 1280 tokens; values scaled by 1/sqrt(d).
     """
     rng = np.random.default_rng(seed)
     if cfg == 1:
@@ -323,7 +323,7 @@ def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = 
                              placement=placement or "permuted")
     if cfg == 4:
         p, s, qn = reasoning_tree(rng)
-        return make_workload(WORKLOADS[4], p, s, qn, chunk_tokens=chunk_tokens or 1536,
+        return make_workload(WORKLOADS[4], p, s, qn, chunk_tokens=chunk_tokens or 2176,
                              hq=32, hkv=8, d=128, dtype=torch.bfloat16, seed=seed,
                              placement=placement or "identity")
     if cfg == 5:
@@ -339,7 +339,7 @@ def standard_workload(cfg: int, seed: int = 0, *, chunk_tokens: Optional[int] = 
         tp, depths = medusa_token_tree(rng, (4, 3, 2), 32)
         p, s, _ = prefix_plus_token_tree(2048, tp)
         p, s, qn, ql = multi_token_nodes(p, s, 8)
-        return make_workload(WORKLOADS[6], p, s, qn, chunk_tokens=chunk_tokens or 1024,
+        return make_workload(WORKLOADS[6], p, s, qn, chunk_tokens=chunk_tokens or 1280,
                              hq=32, hkv=8, d=128, dtype=torch.bfloat16, seed=seed,
                              placement=placement or "permuted", value_scale=1.0 / math.sqrt(128),
                              meta={"depths": depths}, query_lens=ql)
