@@ -749,60 +749,130 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
         vfr[ps][j] = *reinterpret_cast<const u32x4*>(kb + TILE_B + tr * ROWB + sw);
       }
     }
+    if constexpr (EB == 2) {
+      // bf16: the passes go in pairs, a lane's two tokens side by side.  V
+      // element e of both sits in one dword (v_perm), the two probabilities
+      // in one bf16x2, so each O accumulator (and l) takes one dot2 for two
+      // tokens; P is rounded to bf16 as in the matrix-core path.
+      static_assert(NPASS % 2 == 0, "passes come in pairs");
 #pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int tr = ps * TPW + tg;                 // token within the step
-      const bool valid = base + tr < len;
-      float vf[EPL];
+      for (int pp = 0; pp < NPASS; pp += 2) {
+        const int tr0 = pp * TPW + tg, tr1 = tr0 + TPW;   // tokens within the step
+        const bool valid0 = base + tr0 < len, valid1 = base + tr1 < len;
+        uint32_t vp[EPL];
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) Elem<T>::unpack(vfr[ps][j], vf + j * (16 / EB));
-      // All rows side by side (independent chains): scores, group sums,
-      // mask, one branch for the rare rise of any running max, then the
-      // probability and the O and l updates.
-      float z[R];
+        for (int j = 0; j < NLD; ++j)
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float sc = 0.f;
-        if constexpr (EB == 2) {
-#pragma unroll
-          for (int j = 0; j < NLD; ++j) sc = dot8_bf16(kfr[ps][j], qv[r] + 4 * j, sc);
-        } else {
-#pragma unroll
-          for (int e = 0; e < QW; ++e) sc = fmaf(__uint_as_float(qv[r][e]), __uint_as_float(kfr[ps][0][e]), sc);
-        }
-        z[r] = sc;
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) z[r] = group_sum<LPT>(z[r]) * qscale;
-      bool raise[R];
-      bool any_raise = false;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const bool vis = valid && ((mbits[r] >> tr) & 1u);
-        z[r] = vis ? z[r] : kNegInf;
-        m_true[r] = fmaxf(m_true[r], z[r]);
-        // the running max rises only when a score exceeds it by the slack
-        // (a running max of -inf is exceeded by any finite score)
-        raise[r] = z[r] > m_run[r] + kRescaleSlack;
-        any_raise |= raise[r];
-      }
-      if (__any(any_raise)) {
+          for (int i = 0; i < 4; ++i) {
+            vp[j * 8 + 2 * i] = __builtin_amdgcn_perm(vfr[pp + 1][j][i], vfr[pp][j][i], 0x05040100u);
+            vp[j * 8 + 2 * i + 1] = __builtin_amdgcn_perm(vfr[pp + 1][j][i], vfr[pp][j][i], 0x07060302u);
+          }
+        float z0[R], z1[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const float mn = raise[r] ? z[r] : m_run[r];
-          const float alpha = raise[r] ? fast_exp2(m_run[r] - mn) : 1.f;   // m = -inf gives 0
-          m_run[r] = mn;
-          l[r] *= alpha;
+          float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
+          for (int j = 0; j < NLD; ++j) {
+            s0 = dot8_bf16(kfr[pp][j], qv[r] + 4 * j, s0);
+            s1 = dot8_bf16(kfr[pp + 1][j], qv[r] + 4 * j, s1);
+          }
+          z0[r] = s0;
+          z1[r] = s1;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          z0[r] = group_sum<LPT>(z0[r]) * qscale;
+          z1[r] = group_sum<LPT>(z1[r]) * qscale;
+        }
+        bool raise[R];
+        float zm[R];
+        bool any_raise = false;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          z0[r] = valid0 && ((mbits[r] >> tr0) & 1u) ? z0[r] : kNegInf;
+          z1[r] = valid1 && ((mbits[r] >> tr1) & 1u) ? z1[r] : kNegInf;
+          zm[r] = fmaxf(z0[r], z1[r]);
+          m_true[r] = fmaxf(m_true[r], zm[r]);
+          raise[r] = zm[r] > m_run[r] + kRescaleSlack;
+          any_raise |= raise[r];
+        }
+        if (__any(any_raise)) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const float mn = raise[r] ? zm[r] : m_run[r];
+            const float alpha = raise[r] ? fast_exp2(m_run[r] - mn) : 1.f;   // m = -inf gives 0
+            m_run[r] = mn;
+            l[r] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
+          }
+        }
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        typedef float f32x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const bool none = m_run[r] == kNegInf;
+          const float p0 = none ? 0.f : fast_exp2(z0[r] - m_run[r]);   // z = -inf gives 0
+          const float p1 = none ? 0.f : fast_exp2(z1[r] - m_run[r]);
+          const bf16x2_t pb = __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t);
+          l[r] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l[r], false);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            o[r][e] = __builtin_amdgcn_fdot2_f32_bf16(pb, __builtin_bit_cast(bf16x2_t, vp[e]), o[r][e], false);
         }
       }
+    } else {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float p = m_run[r] == kNegInf ? 0.f : fast_exp2(z[r] - m_run[r]);   // z = -inf gives 0
-        l[r] += p;
+      for (int ps = 0; ps < NPASS; ++ps) {
+        const int tr = ps * TPW + tg;                 // token within the step
+        const bool valid = base + tr < len;
+        float vf[EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
+        for (int j = 0; j < NLD; ++j) Elem<T>::unpack(vfr[ps][j], vf + j * (16 / EB));
+        // All rows side by side (independent chains): scores, group sums,
+        // mask, one branch for the rare rise of any running max, then the
+        // probability and the O and l updates.
+        float z[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float sc = 0.f;
+#pragma unroll
+          for (int e = 0; e < QW; ++e) sc = fmaf(__uint_as_float(qv[r][e]), __uint_as_float(kfr[ps][0][e]), sc);
+          z[r] = sc;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) z[r] = group_sum<LPT>(z[r]) * qscale;
+        bool raise[R];
+        bool any_raise = false;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const bool vis = valid && ((mbits[r] >> tr) & 1u);
+          z[r] = vis ? z[r] : kNegInf;
+          m_true[r] = fmaxf(m_true[r], z[r]);
+          // the running max rises only when a score exceeds it by the slack
+          // (a running max of -inf is exceeded by any finite score)
+          raise[r] = z[r] > m_run[r] + kRescaleSlack;
+          any_raise |= raise[r];
+        }
+        if (__any(any_raise)) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const float mn = raise[r] ? z[r] : m_run[r];
+            const float alpha = raise[r] ? fast_exp2(m_run[r] - mn) : 1.f;   // m = -inf gives 0
+            m_run[r] = mn;
+            l[r] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float p = m_run[r] == kNegInf ? 0.f : fast_exp2(z[r] - m_run[r]);   // z = -inf gives 0
+          l[r] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
+        }
       }
     }
   }
