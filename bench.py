@@ -268,10 +268,15 @@ def main():
         step(0)
         torch.cuda.synchronize()
     wall, ev_ms = timed(g_step)
+
+    def timed_median(g, reps=5):
+        """Per-kernel legs: median event time of `reps` timed replays."""
+        return sorted(timed(g)[1] for _ in range(reps))[reps // 2]
+
     g_part = capture("partial", 0, args.steps)
-    _, part_ms = timed(g_part)
+    part_ms = timed_median(g_part)
     g_merge = capture("merge", 0, args.steps)
-    _, merge_ms = timed(g_merge)
+    merge_ms = timed_median(g_merge)
     # single-dispatch variant (last work-group of each row merges it): same
     # results bit for bit, timed the same way
     g_fused = capture("fused", 0, args.steps)
@@ -387,7 +392,7 @@ def main():
         "achieved_hbm_gbs": algo_step / (latency_us * 1e-6) / 1e9,
         "achieved_hbm_frac": algo_step / (latency_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "queries_per_s": nq / (latency_us * 1e-6),
-        "timing": "hipGraph of the K steps, replayed once untimed then once timed",
+        "timing": "hipGraph of the K steps, replayed once untimed then once timed; the per-kernel legs (partial, merge) are the median of 5 timed replays of K launches of that kernel alone",
         "step_us_events": ev_ms * 1e3 / args.steps,
         "partial_kernel_us_mean": mean_part,
         "merge_kernel_us_mean": mean_merge,
