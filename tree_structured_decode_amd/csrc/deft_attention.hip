@@ -147,48 +147,29 @@ __device__ inline float dot8_bf16(const u32x4& a, const uint32_t* b, float s) {
   return s;
 }
 
-__device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
-
-__device__ inline uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                      // round to nearest even
-  return static_cast<uint16_t>(u >> 16);
+// Two floats rounded to bf16 (nearest even) by one v_cvt_pk_bf16_f32, lo in
+// the low half.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
-  static constexpr int kPerLoad = 4;
   __device__ static void unpack(const u32x4& r, float* out) {
     for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(r[i]);
   }
-  __device__ static void store(void* base, size_t idx, float x) { static_cast<float*>(base)[idx] = x; }
 };
-template <> struct Elem<uint16_t> {
-  static constexpr int kPerLoad = 8;
-  __device__ static void unpack(const u32x4& r, float* out) {
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __uint_as_float(r[i] << 16);
-      out[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
-    }
-  }
-  __device__ static void store(void* base, size_t idx, float x) {
-    static_cast<uint16_t*>(base)[idx] = f32_to_bf16(x);
-  }
-};
-
-__device__ inline u32x4 load16(const void* base, int64_t elem_off, int elem_bytes) {
-  return *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + elem_off * elem_bytes);
-}
 
 // Pool row (page * 16 + slot) of every flat token of the chunk, into LDS,
 // stored as row * mul + add.  All flat-to-logical loads are issued before any
 // block-table load so the two dependent lookups cost two memory latencies,
 // not two per token; a chunk whose tokens are one run of consecutive logical
 // tokens (lstart >= 0, its first token's logical index) needs no
-// flat-to-logical lookup at all, only the block-table one.  mid() runs right after the block-table loads are issued
-// (callers issue their own independent loads there, so those overlap the
-// second lookup).  With RPI > 0 the rows of each 32-token step are stored
+// flat-to-logical lookup at all, only the block-table one.  mid() runs right
+// after the block-table loads are issued (callers issue their own
+// independent loads there, so those overlap the last lookup).  With RPI > 0 the rows of each 32-token step are stored
 // permuted, entry (t % RPI) * (32 / RPI) + (t % 32) / RPI, which puts the rows
 // one lane of a direct-to-LDS load sequence needs next to each other.  NT is
 // the work-group size.
@@ -415,7 +396,7 @@ __device__ void merge_rows4(const MergeArgs& a, int code) {
     uint32_t pk[EPL / 2];
 #pragma unroll
     for (int e = 0; e < EPL / 2; ++e)
-      pk[e] = f32_to_bf16(acc[2 * e] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * e + 1] * inv)) << 16);
+      pk[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
     if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ob) = u32x4{pk[0], pk[1], pk[2], pk[3]};
     else *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = u32x2{pk[0], pk[1]};
   } else {
@@ -550,14 +531,16 @@ __device__ inline void pair_sync(int32_t* mine, int32_t* theirs, int32_t i, int 
 // rows per work-group (R = 4 or 8, the smaller that holds the plan's largest
 // VALU work item; larger groups are split into items of 8 rows that share
 // the chunk's KV through L2).  Scores and the PV update are wavefront arithmetic:
-// lanes are grouped LPT per token (each lane holds 16 bytes of the token's
-// K and V row), dot products are summed across the group with DPP moves.
-// The work is a stream over the chunk's KV rows with little arithmetic per
-// byte, so memory is fed like the MFMA kernel: each of the 4 waves takes the
-// chunk's steps (4 KB of K rows per step) w, w+4, ... and streams them with
-// direct-to-LDS loads into a private NSTG-stage ring, NSTG-1 steps ahead,
-// with explicit waits.  Each lane group keeps its own online-softmax state
-// (running max raised lazily); groups and waves are merged at the end.
+// lanes are grouped LPT per token (each lane holds 16 or 32 bytes of the
+// token's K and V row), dot products are summed across the group with DPP
+// moves; with bf16 inputs a lane's two tokens of a step share one dot2 per
+// O element.  The work is a stream over the chunk's KV rows with little
+// arithmetic per byte, so memory is fed like the MFMA kernel: each of the NW
+// waves takes the chunk's steps (4 KB of K rows per step) w, w+NW, ... and
+// streams them with direct-to-LDS loads into a private NSTG-stage ring,
+// NSTG-1 steps ahead, with explicit waits.  Each lane group keeps its own
+// online-softmax state (running max raised lazily); groups and waves are
+// merged at the end.
 // ---------------------------------------------------------------------------
 template <int R> constexpr int valu_waves() { return R <= 8 ? 8 : 4; }
 
@@ -726,7 +709,7 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
         }
       }
       // the Q reads complete before this stage is refilled below
-      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     }
     // refill the stage read in step i-1 (its reads have all returned)
     if (i + NSTG - 1 < my_steps) issue(i + NSTG - 1, (i + NSTG - 1) % NSTG);
@@ -919,7 +902,7 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
     if (a.po_bf16) {
       const float inv = 1.f / lsum;
       *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.po) + sh * D + e) =
-          f32_to_bf16(o0 * inv) | (static_cast<uint32_t>(f32_to_bf16(o1 * inv)) << 16);
+          pack_bf16x2(o0 * inv, o1 * inv);
     } else {
       *reinterpret_cast<u32x2*>(a.po + sh * D + e) = u32x2{__float_as_uint(o0), __float_as_uint(o1)};
     }
@@ -941,12 +924,14 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
 // the chunk's 32-token steps sp, sp+4, ...  The two waves of a split share a
 // two-stage LDS ring; per step one of them loads the K rows and the 64 rows'
 // mask words, the other the V rows, by direct-to-LDS loads (no VGPRs), one
-// step ahead, with one work-group barrier per step.  Per step and wave:
+// step ahead; the two rendezvous through LDS flags once per step (no
+// work-group barrier inside the loop).  Per step and wave:
 //   S^T = K Q^T   16x16x32 MFMA, A = K rows (LDS), B = Q^T (registers), for
 //                 2 token tiles x 2 row tiles;
 //   mask, online softmax on the S^T fragments in registers;
 //   O^T += V^T P^T  A = V^T from LDS transpose reads of the token-major V
-//                 rows, B = P^T taken straight from the S^T fragments.
+//                 rows, B = P^T taken straight from the S^T fragments; the
+//                 row sums l by the same product with a tile of ones as A.
 // K tile rows are permuted so every lane ends up holding 8 consecutive tokens
 // of one row, which is the B-operand layout of the PV product.  Rows in LDS
 // are stored with their 16-byte chunks XOR-swizzled by the row index.  The
@@ -1104,7 +1089,6 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   const int iters = (nsteps + NSPLIT - 1) / NSPLIT;   // the same for every wave
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
   // LDS byte offsets (from the block's LDS base: stage 0 of this split's
   // ring; stage 1 adds STAGE_B as an immediate) of this lane's operand
@@ -1377,8 +1361,8 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
           acc += f[q] * reinterpret_cast<const f32x4*>(smem + q * 2 * STAGE_B + hh * RED_W)[(dt * NRT + rt) * 64 + ln];
         const int64_t at = sh * D + dt * 16 + (ln >> 4) * 4;
         if (a.po_bf16) {
-          const uint32_t lo = f32_to_bf16(acc[0] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[1] * inv)) << 16);
-          const uint32_t hi = f32_to_bf16(acc[2] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[3] * inv)) << 16);
+          const uint32_t lo = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+          const uint32_t hi = pack_bf16x2(acc[2] * inv, acc[3] * inv);
           *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + at) = u32x2{lo, hi};
         } else {
           *reinterpret_cast<f32x4*>(a.po + at) = acc;
