@@ -125,8 +125,8 @@ def main():
                     help="run a plain elementwise copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X: the tree-attention path runs on a single GPU in "
-              "this build (no multi-GPU sharding); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one MI355X: the tree-attention path runs on a single GPU "
+              "(it has no multi-GPU sharding); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
