@@ -66,7 +66,7 @@ extern "C" {
 #define DEFT_OK                     0
 #define DEFT_ERR_INVALID_ARGUMENT  -1  /* null pointer, bad count, buffer too small, plan/desc mismatch */
 #define DEFT_ERR_INVALID_TREE      -2  /* parents/seg_lens/query_nodes break the encoding above */
-#define DEFT_ERR_UNSUPPORTED       -3  /* valid request outside what this build implements */
+#define DEFT_ERR_UNSUPPORTED       -3  /* valid request outside what the kernels implement */
 #define DEFT_ERR_HIP               -4  /* a HIP call or kernel launch failed */
 #define DEFT_ERR_NO_MEMORY         -5  /* host allocation failed */
 
