@@ -251,6 +251,14 @@ int deft_plan_upload(deft_plan* plan, const deft_attn_desc* desc, void* dev_plan
  * and return DEFT_ERR_INVALID_ARGUMENT, launching nothing, if one is out of
  * range.
  */
+/*
+ * Work items (deft_plan_device_bytes, deft_plan_upload): bf16 groups of 16
+ * or more rows take the matrix-core kernel in items of 64 rows, or of 128
+ * rows for groups of more than 64 when the 64-row items would fill the
+ * current device's compute units at least twice (each chunk is then streamed
+ * by half as many work-groups).  DEFT_MFMA_WIDE=1 or 0 in the environment
+ * forces 128-row items on or off (tests); the choice is made at upload.
+ */
 int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_table, const deft_plan* plan, void* out,
                         const deft_attn_desc* desc, void* workspace, size_t workspace_bytes,

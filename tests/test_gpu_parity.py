@@ -408,3 +408,38 @@ def test_validate_block_table_host_check(monkeypatch):
     ta(q, kc, vc, bt, out)
     torch.cuda.synchronize()
     check_close(out.double().cpu().numpy(), oracle_out(wl), TOL[torch.float32], "validate")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("c", [48, 96, 544])
+def test_wide_mfma_items_match_oracle(monkeypatch, c, d):
+    """128-row MFMA items (two token splits of four 32-row waves, split 1
+    merged into split 0 in registers), forced on: groups of 80 rows (a
+    partial wide item) on the shared-prompt tree, at chunk sizes with one,
+    three and seventeen 32-token steps."""
+    monkeypatch.setenv("DEFT_MFMA_WIDE", "1")
+    p, s, qn = W.shared_prompt_branches(300, 20, 90)
+    wl = W.make_workload("wide", p, s, qn, chunk_tokens=c, hq=8, hkv=2, d=d, dtype=torch.bfloat16,
+                         seed=3 * c + d, placement="scattered",
+                         pool_pages=2 * (-(-int(s.sum()) // 16)) + 5, value_scale=1.0 / np.sqrt(d))
+    say("wide", c, d)
+    got, _ = run_gpu(wl)
+    want = oracle_out(wl)
+    check_close(got, want, TOL[torch.bfloat16], f"wide {c} {d}")
+    _rms_check(got, want, f"wide {c} {d}")
+
+
+def test_wide_mfma_items_standard_tree_and_fused(monkeypatch):
+    """The 4K-prefix tree (256-row groups: two full 128-row items per chunk
+    and KV head) with 128-row items forced on: against the oracle, and the
+    single-dispatch path bit-identical to the two-dispatch one."""
+    monkeypatch.setenv("DEFT_MFMA_WIDE", "1")
+    wl = W.standard_workload(2)
+    say("wide standard", wl.chunk_tokens)
+    q, kc, vc, bt = gpu_inputs(wl)
+    got, ta = run_gpu(wl, inputs=(q, kc, vc, bt))
+    check_close(got, oracle_out(wl), TOL[torch.bfloat16], "wide cfg2")
+    out2 = torch.full_like(q, float("nan"))
+    D.deft_tree_attention_fused(q, kc, vc, bt, ta.plan, out2, ta.desc, ta.workspace)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.double().cpu().numpy(), got)

@@ -72,7 +72,7 @@ struct DevPlan {
   const int4* valu_items;
   int32_t* tickets;          // [Nq * Hq], zero between calls (fused merge)
   const int32_t* merge_slots;   // [Nq][merge_stride] slot ids padded with -1, or unused
-  int32_t n_mfma, n_valu, mask_words, num_queries, merge_stride;
+  int32_t n_mfma_wide, n_mfma, n_valu, mask_words, num_queries, merge_stride;   // mfma_items: wide, then 64-row
 };
 
 // Operands of the per-(query, head) merge (the merge kernel and the fused
@@ -525,6 +525,24 @@ __device__ inline void pair_sync(int32_t* mine, int32_t* theirs, int32_t i, int 
     __builtin_amdgcn_s_sleep(1);
   }
 }
+// The same for N waves: wave `me` publishes `i` in flags[me], then waits
+// until every other flag reaches `i` (bounded like pair_sync).
+template <int N>
+__device__ inline void group_sync(int32_t* flags, int me, int32_t i, int lane) {
+  if constexpr (N == 2) {
+    pair_sync(&flags[me], &flags[me ^ 1], i, lane);
+  } else {
+    if (lane == 0) __hip_atomic_store(&flags[me], i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int spin = 0; spin < (1 << 20); ++spin) {
+      bool done = true;
+#pragma unroll
+      for (int k = 0; k < N; ++k)
+        if (k != me) done &= __hip_atomic_load(&flags[k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= i;
+      if (done) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // VALU partial kernel: groups below one MFMA tile, and fp32 inputs; up to R
@@ -937,27 +955,32 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
 // are stored with their 16-byte chunks XOR-swizzled by the row index.  The
 // four token splits of each row half are merged through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NSPLIT>
 struct MfmaShape {
+  static constexpr int NGRP = 8 / NSPLIT;        // waves sharing a split's ring
+  static constexpr int ROWS = 32 * NGRP;         // rows of a work item
   static constexpr int ROWB = D * 2;
   static constexpr int TILE_B = 32 * ROWB;
-  static constexpr int STAGE_B = 2 * TILE_B + 256;
-  static constexpr int RING_B = 4 * 2 * STAGE_B;
-  // LDS carve-out: rings (and the epilogue's reduction), staged token rows,
-  // split statistics, pair flags, fused-merge lists
-  static constexpr int TOK_OFF = RING_B;
+  static constexpr int STAGE_B = 2 * TILE_B + 4 * ROWS;   // K, V, a mask word per row
+  static constexpr int RING_B = NSPLIT * 2 * STAGE_B;
+  // LDS carve-out: rings (and the epilogue's reduction), the Q rows (in
+  // stage 1 of split 0 with four splits, a region of their own with two),
+  // staged token rows, split statistics, group flags, fused-merge lists
+  static constexpr int QOFF = NSPLIT == 4 ? STAGE_B : RING_B;
+  static constexpr int TOK_OFF = NSPLIT == 4 ? RING_B : RING_B + ROWS * ROWB;
   static constexpr int STATS_OFF = TOK_OFF + 4 * kMaxChunkTokens;
   static constexpr int FLAGS_OFF = STATS_OFF + 8 * 32 * 3 * 4;
-  static constexpr int LIST_OFF = FLAGS_OFF + 4 * 2 * 4;
-  static constexpr int LDS_B = LIST_OFF + 4 * (kMfmaRows + 4);
+  static constexpr int LIST_OFF = FLAGS_OFF + 4 * 8;
+  static constexpr int LDS_B = LIST_OFF + 4 * (ROWS + 4);
 };
 
-template <int D, bool FUSED>
-__device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int bid) {
+template <int D, bool FUSED, int NSPLIT>
+__device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int bid, int item_base) {
   constexpr int NWAVE = 8;
-  constexpr int NSPLIT = 4;
+  constexpr int NGRP = NWAVE / NSPLIT;  // waves per split, one per 32-row group
   constexpr int NRT = 2;                // row tiles per wave
   constexpr int WROWS = NRT * 16;       // rows per wave
+  constexpr int ROWS = NGRP * WROWS;    // rows of the work item
   constexpr int KS = D / 32;            // k-steps of S = K Q^T
   constexpr int DT = D / 16;            // d-tiles of O^T
   constexpr int CH = D / 8;             // 16-byte chunks per token row
@@ -965,24 +988,31 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   constexpr int TILE_B = 32 * ROWB;     // K (or V) bytes of one 32-token step
   constexpr int NI = TILE_B / 1024;     // 1 KB direct loads per tile
   constexpr int RPI = 64 / CH;          // token rows per direct load
-  constexpr int STAGE_B = 2 * TILE_B + 256;   // K, V, 64 mask words
+  constexpr int STAGE_B = 2 * TILE_B + 4 * ROWS;   // K, V, a mask word per row
   constexpr int RING_B = NSPLIT * 2 * STAGE_B;
   constexpr int RED_W = DT * NRT * 64 * 16;   // one wave's O^T fragments (epilogue)
-  static_assert(2 * RED_W <= 2 * STAGE_B, "a split's two waves reduce through their own ring");
+  // A step's loads are shared by the NGRP waves of a split: NL direct loads
+  // each (the K tile's, then the V tile's, in order), and the mask words of
+  // 64 rows for each of the first ROWS / 64 waves.
+  constexpr int NL = 2 * NI / NGRP;
   static_assert(NI == 8 || NI == 4, "token rows per lane come in groups of 4 or 8");
-  static_assert(kMfmaRows == 2 * WROWS, "a work item is two row halves");
-  using Shape = MfmaShape<D>;
-  static_assert(Shape::RING_B == RING_B && Shape::STAGE_B == STAGE_B, "shape constants agree");
-  static_assert(NWAVE == 8 && WROWS == 32 && NSPLIT == 4, "carve-out sizes");
+  static_assert(NSPLIT == 4 || NSPLIT == 2, "64-row items in four splits, 128-row items in two");
+  static_assert(NL >= 2 && (NL == NI || 2 * NL == NI), "whole halves of a tile per wave");
+  using Shape = MfmaShape<D, NSPLIT>;
+  static_assert(Shape::RING_B == RING_B && Shape::STAGE_B == STAGE_B && Shape::ROWS == ROWS, "shape constants agree");
+  static_assert(NSPLIT == 2 || 2 * RED_W <= 2 * STAGE_B, "a split's two waves reduce through their own ring");
+  static_assert(NSPLIT == 4 || (2 * RED_W <= ROWS * ROWB && 2 * RED_W <= 2 * STAGE_B),
+                "split 1's waves publish through the Q region and their own ring");
   char* smem = lds;
   int32_t* tok_row = reinterpret_cast<int32_t*>(lds + Shape::TOK_OFF);
   float (*stats)[WROWS][3] = reinterpret_cast<float (*)[WROWS][3]>(lds + Shape::STATS_OFF);
-  int32_t (*pair_ready)[2] = reinterpret_cast<int32_t (*)[2]>(lds + Shape::FLAGS_OFF);
+  int32_t (*grp_ready)[NGRP] = reinterpret_cast<int32_t (*)[NGRP]>(lds + Shape::FLAGS_OFF);
 
   const DevPlan& P = a.plan;
   const int g = bid % a.hkv;
-  const int4 it0 = P.mfma_items[2 * (bid / a.hkv)];
-  const int4 it1 = P.mfma_items[2 * (bid / a.hkv) + 1];
+  const int item = item_base + bid / a.hkv;
+  const int4 it0 = P.mfma_items[2 * item];
+  const int4 it1 = P.mfma_items[2 * item + 1];
   const int32_t rb = it0.y, nr = it0.z, cs = it0.w;
   const int32_t len = it1.x, gofs = it1.y;
   const bool full = it1.z != 0;
@@ -990,25 +1020,29 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = w & 1, sp = w >> 1;
+  const int gr = w % NGRP, sp = w / NGRP;   // row group (rows 32 gr ..) and token split
+  const int kvsel = gr * NL / NI;           // this wave loads K (0) or V (1) rows
+  const int n0 = gr * NL % NI;              // its first load of that tile
+  const bool loads_mask = gr < ROWS / 64;
   const int lr = lane & 15, lj = lane >> 4;
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const uint16_t* kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* vp = static_cast<const uint16_t*>(a.v);
 
-  // The block's 64 Q rows (64 * 2D bytes) are copied once into LDS, into
-  // stage 1 of split 0's ring (first refilled in the loop, after every wave
-  // has read its fragments).  Copy n (1 KB, NQW per wave) holds rows RPQ*n
+  // The block's Q rows (ROWS * 2D bytes) are copied once into LDS: into
+  // stage 1 of split 0's ring with four splits (first refilled in the loop,
+  // after every wave has read its fragments), into a region of their own with
+  // two.  Copy n (1 KB, NQW per wave) holds rows RPQ*n
   // .. RPQ*n + RPQ-1; its lane i takes 16-byte chunk (i % CH) ^ (R % CH) of
   // row R = RPQ*n + i / CH, so the fragment reads below avoid bank
   // conflicts.  The rows' queries are looked up alongside the flat-to-logical
   // lookups of the staging, the copies are issued alongside its block-table
   // lookups.  Rows past nr copy a valid row; they are masked later.
   constexpr int RPQ = 1024 / ROWB;
-  constexpr int NQW = kMfmaRows * ROWB / 1024 / NWAVE;
-  static_assert(kMfmaRows * ROWB <= STAGE_B, "the block's Q rows fit in one ring stage");
-  static_assert(NQW >= 1 && NQW * NWAVE * 1024 == kMfmaRows * ROWB, "whole 1 KB Q copies per wave");
-  const uint32_t q_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + STAGE_B));
+  constexpr int NQW = ROWS * ROWB / 1024 / NWAVE;
+  static_assert(NSPLIT == 2 || ROWS * ROWB <= STAGE_B, "the block's Q rows fit in one ring stage");
+  static_assert(NQW >= 1 && NQW * NWAVE * 1024 == ROWS * ROWB, "whole 1 KB Q copies per wave");
+  const uint32_t q_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + Shape::QOFF));
   int32_t qsq[NQW];
 #pragma unroll
   for (int j = 0; j < NQW; ++j) {
@@ -1026,9 +1060,11 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
       lds_dma16(qp + (static_cast<int64_t>(qsq[j]) * a.hq + head) * D + c * 8, q_lds + (NQW * w + j) * 1024);
     }
   });
-  // Row of the mask word this lane loads (lane i <-> row i of the block).
-  const int32_t mask_slot = gofs + (rb + (lane < nr ? lane : 0)) / a.grp;
-  if (threadIdx.x < 2 * NSPLIT) pair_ready[threadIdx.x >> 1][threadIdx.x & 1] = -1;
+  // Row of the mask word this lane loads (lane i <-> row 64 gr + i of the
+  // block, for the waves that load mask words).
+  const int mrow = 64 * (loads_mask ? gr : 0) + lane;
+  const int32_t mask_slot = gofs + (rb + (mrow < nr ? mrow : 0)) / a.grp;
+  if (threadIdx.x < NSPLIT * NGRP) grp_ready[threadIdx.x / NGRP][threadIdx.x % NGRP] = -1;
   lds_barrier();   // the staged token rows are visible (the Q copies may still be in flight)
 
   char* ring = smem + sp * 2 * STAGE_B;
@@ -1036,8 +1072,9 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   const int lrow = lane / CH;            // row of each direct load this lane fetches
   const int lch = lane % CH;             // its 16-byte LDS slot in that row
 
-  // This wave's half of a step's loads (h = 0: K rows and mask words; h = 1:
-  // V rows).  Load n fetches rows n*RPI + lrow; lane (lrow, lch) fetches chunk
+  // This wave's share of a step's loads: loads n0 .. n0 + NL - 1 of the K
+  // (kvsel = 0) or V tile, and mask words.  Load n fetches rows n*RPI + lrow;
+  // lane (lrow, lch) fetches chunk
   // lch ^ (R % CH) of row R, so LDS slot p of row R holds chunk p ^ (R % CH).
   // The swizzle depends on n only through n % NSW, so each lane keeps NSW base
   // pointers and a load address is one shift-add of the staged head row.
@@ -1046,21 +1083,26 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   const char* lbase[NSW];
 #pragma unroll
   for (int c = 0; c < NSW; ++c)
-    lbase[c] = reinterpret_cast<const char*>(h ? vp : kp) + (lch ^ ((c * RPI + lrow) % CH)) * 16;
+    lbase[c] = reinterpret_cast<const char*>(kvsel ? vp : kp) + (lch ^ ((c * RPI + lrow) % CH)) * 16;
   auto load_ptrs = [&](int step, const char** ptr) {
     // (the staged rows run to a multiple of 512 tokens, entries past the
     // chunk end holding its last token, so a partial last step needs no
     // special case)
-    int32_t rows[NI];
-    const int32_t* tr = tok_row + step * 32 + lrow * NI;   // the permuted layout
+    int32_t rows[NL];
+    const int32_t* tr = tok_row + step * 32 + lrow * NI + n0;   // the permuted layout
+    if constexpr (NL >= 4) {
 #pragma unroll
-    for (int n = 0; n < NI; n += 4) {
-      const int4 v4 = *reinterpret_cast<const int4*>(tr + n);
-      rows[n] = v4.x; rows[n + 1] = v4.y; rows[n + 2] = v4.z; rows[n + 3] = v4.w;
+      for (int j = 0; j < NL; j += 4) {
+        const int4 v4 = *reinterpret_cast<const int4*>(tr + j);
+        rows[j] = v4.x; rows[j + 1] = v4.y; rows[j + 2] = v4.z; rows[j + 3] = v4.w;
+      }
+    } else {
+      const int2 v2 = *reinterpret_cast<const int2*>(tr);
+      rows[0] = v2.x; rows[1] = v2.y;
     }
 #pragma unroll
-    for (int n = 0; n < NI; ++n)
-      ptr[n] = lbase[n % NSW] + (static_cast<uint64_t>(static_cast<uint32_t>(rows[n])) * ROWB);
+    for (int j = 0; j < NL; ++j)
+      ptr[j] = lbase[(n0 + j) % NSW] + (static_cast<uint64_t>(static_cast<uint32_t>(rows[j])) * ROWB);
   };
   const uint32_t* mask_src = P.slot_mask + static_cast<size_t>(mask_slot) * W;
 
@@ -1114,22 +1156,22 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   // each wave waits for its own Q copies only (they are older than the step's
   // loads) and a barrier makes all of them visible.
   if (sp < nsteps) {
-    const char* ptr[NI];
+    const char* ptr[NL];
     load_ptrs(sp, ptr);
 #pragma unroll
-    for (int n = 0; n < NI; ++n) lds_dma16(ptr[n], ring_lds + h * TILE_B + n * 1024);
-    if (h == 0) {
-      lds_dma4(mask_src + sp, ring_lds + 2 * TILE_B);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NI + 1));
+    for (int j = 0; j < NL; ++j) lds_dma16(ptr[j], ring_lds + kvsel * TILE_B + (n0 + j) * 1024);
+    if (loads_mask) {
+      lds_dma4(mask_src + sp, ring_lds + 2 * TILE_B + gr * 256);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL + 1));
     } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NI));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
     }
   } else {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
   lds_barrier();
   // Q^T fragments (B operand of S^T = K Q^T) of this wave's 32 rows: lane
-  // (lr, lj) takes d = 32 ks + 8 lj .. +7 of row R = 32h + 16rt + lr, i.e.
+  // (lr, lj) takes d = 32 ks + 8 lj .. +7 of row R = 32gr + 16rt + lr, i.e.
   // chunk 4 ks + lj, stored in slot (4 ks + lj) ^ (R % CH).  Every wave reads
   // them before any wave refills stage 1 of split 0 (the barrier below; this
   // step's loads above go to stage 0).
@@ -1138,8 +1180,8 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int R = WROWS * h + rt * 16 + lr;
-      qf[rt][ks] = *reinterpret_cast<const bf16x8*>(smem + STAGE_B + R * ROWB + (((4 * ks + lj) ^ (R % CH)) * 16));
+      const int R = WROWS * gr + rt * 16 + lr;
+      qf[rt][ks] = *reinterpret_cast<const bf16x8*>(smem + Shape::QOFF + R * ROWB + (((4 * ks + lj) ^ (R % CH)) * 16));
     }
   lds_barrier();
 
@@ -1152,20 +1194,20 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
   auto step_body = [&](auto stg, int i) {
     constexpr int STG = decltype(stg)::value;
     const int step = sp + i * NSPLIT;
-    // This wave's loads for `step` are done.  Only the two waves of a split
+    // This wave's loads for `step` are done.  Only the waves of a split
     // share a ring, so they synchronise with each other instead of the whole
-    // work-group: each publishes "my half of iteration i is in LDS and I have
-    // finished iteration i-1", then waits for the partner to say the same,
-    // after which the other stage can be refilled with step i+1.
+    // work-group: each publishes "my share of iteration i is in LDS and I
+    // have finished iteration i-1", then waits for the others to say the
+    // same, after which the other stage can be refilled with step i+1.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    pair_sync(&pair_ready[sp][h], &pair_ready[sp][h ^ 1], i, lane);
+    group_sync<NGRP>(grp_ready[sp], gr, i, lane);
     if (step >= nsteps) return;
     const bool next = step + NSPLIT < nsteps;
     const int base = step * 32;
     const char* kb = ring + STG * STAGE_B;
     const uint32_t* mb = reinterpret_cast<const uint32_t*>(kb + 2 * TILE_B);
-    const uint32_t nd = ring_lds + (STG ^ 1) * STAGE_B + h * TILE_B;   // this wave's half of the other stage
-    const char* ptr[NI];
+    const uint32_t nd = ring_lds + (STG ^ 1) * STAGE_B + kvsel * TILE_B;   // this wave's tile in the other stage
+    const char* ptr[NL];
     if (next) load_ptrs(step + NSPLIT, ptr);
 
     // The step runs row tile by row tile so that each tile's softmax
@@ -1178,8 +1220,8 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     // branches, so the arithmetic can be interleaved with them).
     if (next) {
 #pragma unroll
-      for (int n = 0; n < NI; ++n) lds_dma16(ptr[n], nd + n * 1024);
-      if (h == 0) lds_dma4(mask_src + step + NSPLIT, ring_lds + (STG ^ 1) * STAGE_B + 2 * TILE_B);
+      for (int j = 0; j < NL; ++j) lds_dma16(ptr[j], nd + (n0 + j) * 1024);
+      if (loads_mask) lds_dma4(mask_src + step + NSPLIT, ring_lds + (STG ^ 1) * STAGE_B + 2 * TILE_B + gr * 256);
     }
     bf16x8 kfr[2 * KS];
 #pragma unroll
@@ -1226,7 +1268,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     const bool all_visible = full && valid_e >= 8;
     auto soft_max = [&](auto rtc) {       // mask, maxima, lazy rescale
       constexpr int rt = decltype(rtc)::value;
-      const int rl = WROWS * h + rt * 16 + lr;   // row within the block
+      const int rl = WROWS * gr + rt * 16 + lr;   // row within the block
       const bool row_ok = rl < nr;
 #pragma unroll
       for (int e = 0; e < 8; ++e) z[rt][e] = e < 4 ? sacc[0][rt][e] : sacc[1][rt][e - 4];
@@ -1320,59 +1362,113 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
       stats[w][rt * 16 + lr][2] = ls;
     }
   }
-  pair_sync(&pair_ready[sp][h], &pair_ready[sp][h ^ 1], iters, lane);   // both past their last step
-  {
-    f32x4* mine = reinterpret_cast<f32x4*>(smem + sp * 2 * STAGE_B + h * RED_W);
+  if constexpr (NSPLIT == 4) {
+    group_sync<NGRP>(grp_ready[sp], gr, iters, lane);   // the split is past its last step
+    {
+      f32x4* mine = reinterpret_cast<f32x4*>(smem + sp * 2 * STAGE_B + gr * RED_W);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) mine[(dt * NRT + rt) * 64 + lane] = o[dt][rt];
-  }
-  lds_barrier();
-  {
-    static_assert(2 * NRT * 64 * 2 == 512, "thread -> (d half, row half, row tile, lane)");
-    const int ln = threadIdx.x & 63, rt = (threadIdx.x >> 6) % NRT;
-    const int hh = (threadIdx.x >> 6) / NRT % 2, dq = threadIdx.x >> 8;
-    const int rw = rt * 16 + (ln & 15), r = WROWS * hh + rw;
-    float mx = kNegInf;
-#pragma unroll
-    for (int q = 0; q < NSPLIT; ++q) mx = fmaxf(mx, stats[2 * q + hh][rw][1]);
-    float f[NSPLIT], ls = 0.f;
-#pragma unroll
-    for (int q = 0; q < NSPLIT; ++q) {
-      const float mr = stats[2 * q + hh][rw][0];
-      f[q] = (mr == kNegInf) ? 0.f : fast_exp2((mr - mx) * cl2);
-      ls += f[q] * stats[2 * q + hh][rw][2];
+        for (int rt = 0; rt < NRT; ++rt) mine[(dt * NRT + rt) * 64 + lane] = o[dt][rt];
     }
-    if (r < nr) {
-      const int row = rb + r;
-      const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
-      if (ln < 16 && dq == 0) {
-        a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
-        a.pl[sh] = ls;
+    lds_barrier();
+    {
+      static_assert(NGRP == 2 && 2 * NRT * 64 * 2 == 512, "thread -> (d half, row half, row tile, lane)");
+      const int ln = threadIdx.x & 63, rt = (threadIdx.x >> 6) % NRT;
+      const int hh = (threadIdx.x >> 6) / NRT % 2, dq = threadIdx.x >> 8;
+      const int rw = rt * 16 + (ln & 15), r = WROWS * hh + rw;
+      float mx = kNegInf;
+#pragma unroll
+      for (int q = 0; q < NSPLIT; ++q) mx = fmaxf(mx, stats[2 * q + hh][rw][1]);
+      float f[NSPLIT], ls = 0.f;
+#pragma unroll
+      for (int q = 0; q < NSPLIT; ++q) {
+        const float mr = stats[2 * q + hh][rw][0];
+        f[q] = (mr == kNegInf) ? 0.f : fast_exp2((mr - mx) * cl2);
+        ls += f[q] * stats[2 * q + hh][rw][2];
       }
-      const float inv = 1.f / ls;
+      if (r < nr) {
+        const int row = rb + r;
+        const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
+        if (ln < 16 && dq == 0) {
+          a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
+          a.pl[sh] = ls;
+        }
+        const float inv = 1.f / ls;
 #pragma unroll
-      for (int k = 0; k < DT / 2; ++k) {
-        const int dt = dq * (DT / 2) + k;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < DT / 2; ++k) {
+          const int dt = dq * (DT / 2) + k;
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < NSPLIT; ++q)
-          acc += f[q] * reinterpret_cast<const f32x4*>(smem + q * 2 * STAGE_B + hh * RED_W)[(dt * NRT + rt) * 64 + ln];
-        const int64_t at = sh * D + dt * 16 + (ln >> 4) * 4;
-        if (a.po_bf16) {
-          const uint32_t lo = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-          const uint32_t hi = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + at) = u32x2{lo, hi};
-        } else {
-          *reinterpret_cast<f32x4*>(a.po + at) = acc;
+          for (int q = 0; q < NSPLIT; ++q)
+            acc += f[q] * reinterpret_cast<const f32x4*>(smem + q * 2 * STAGE_B + hh * RED_W)[(dt * NRT + rt) * 64 + ln];
+          const int64_t at = sh * D + dt * 16 + (ln >> 4) * 4;
+          if (a.po_bf16) {
+            const uint32_t lo = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+            const uint32_t hi = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + at) = u32x2{lo, hi};
+          } else {
+            *reinterpret_cast<f32x4*>(a.po + at) = acc;
+          }
+        }
+      }
+    }
+  } else {
+    // Two splits: split 1's waves publish their O^T fragments once their
+    // split is past its last step, row groups 0 and 1 in the Q region (free
+    // since the prologue), 2 and 3 in their own ring; after one barrier each
+    // split-0 wave merges its partner's rows (same row group) into its own
+    // registers and writes them.
+    auto red_of = [&](int grp) {
+      return reinterpret_cast<f32x4*>(smem + (grp < 2 ? Shape::QOFF + grp * RED_W : 2 * STAGE_B + (grp - 2) * RED_W));
+    };
+    if (sp == 1) {
+      group_sync<NGRP>(grp_ready[1], gr, iters, lane);
+      f32x4* mine = red_of(gr);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) mine[(dt * NRT + rt) * 64 + lane] = o[dt][rt];
+    }
+    lds_barrier();
+    if (sp == 0) {
+      const int pw = NGRP + gr;   // the split-1 wave of this row group
+      const f32x4* theirs = red_of(gr);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int rw = rt * 16 + lr, r = WROWS * gr + rw;
+        const float m1 = stats[pw][rw][0];
+        const float mx = fmaxf(stats[w][rw][1], stats[pw][rw][1]);
+        const float f0 = m_run[rt] == kNegInf ? 0.f : fast_exp2((m_run[rt] - mx) * cl2);
+        const float f1 = m1 == kNegInf ? 0.f : fast_exp2((m1 - mx) * cl2);
+        const float ls = f0 * stats[w][rw][2] + f1 * stats[pw][rw][2];
+        if (r < nr) {
+          const int row = rb + r;
+          const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
+          if (lj == 0) {
+            a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
+            a.pl[sh] = ls;
+          }
+          const float inv = 1.f / ls;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const f32x4 acc = f0 * o[dt][rt] + f1 * theirs[(dt * NRT + rt) * 64 + lane];
+            const int64_t at = sh * D + dt * 16 + lj * 4;
+            if (a.po_bf16) {
+              const uint32_t lo = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+              const uint32_t hi = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+              *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + at) = u32x2{lo, hi};
+            } else {
+              *reinterpret_cast<f32x4*>(a.po + at) = acc;
+            }
+          }
         }
       }
     }
   }
   if constexpr (FUSED) {
     int32_t* last_list = reinterpret_cast<int32_t*>(lds + Shape::LIST_OFF);
-    fused_merge_tail<uint16_t, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, last_list + kMfmaRows);
+    fused_merge_tail<uint16_t, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, last_list + ROWS);
   }
 }
 
@@ -1388,21 +1484,39 @@ template <typename T, int D, int R, bool FUSED>
 __global__ __launch_bounds__(512) void partial_attention(PartialArgs a) {
   static_assert(64 * valu_waves<R>() == 512, "both bodies run 8 waves");
   constexpr int VB = ValuShape<T, D, R>::LDS_B;
-  constexpr int MB = sizeof(T) == 2 ? MfmaShape<D>::LDS_B : 0;
+  constexpr int MB4 = sizeof(T) == 2 ? MfmaShape<D, 4>::LDS_B : 0;
+  constexpr int MB2 = sizeof(T) == 2 ? MfmaShape<D, 2>::LDS_B : 0;
+  constexpr int MB = MB4 > MB2 ? MB4 : MB2;
   __shared__ __attribute__((aligned(1024))) char lds[VB > MB ? VB : MB];
+  const int nw = a.plan.n_mfma_wide * a.hkv;
   const int nm = a.plan.n_mfma * a.hkv;
+  const int b = static_cast<int>(blockIdx.x);
   if constexpr (sizeof(T) == 2) {
-    if (static_cast<int>(blockIdx.x) < nm) {
-      mfma_body<D, FUSED>(a, lds, blockIdx.x);
+    if (b < nw) {
+      mfma_body<D, FUSED, 2>(a, lds, b, 0);
+      return;
+    }
+    if (b < nw + nm) {
+      mfma_body<D, FUSED, 4>(a, lds, b - nw, a.plan.n_mfma_wide);
       return;
     }
   }
-  valu_body<T, D, R, FUSED>(a, lds, static_cast<int>(blockIdx.x) - nm);
+  valu_body<T, D, R, FUSED>(a, lds, b - nw - nm);
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();   // leave no error behind for a later launch check
+    return 256;
+  }
+  return n;
+}
 
 static DevPlan make_dev_plan(const deft_plan* p) {
   const int32_t* b = static_cast<const int32_t*>(p->dev);
@@ -1421,6 +1535,7 @@ static DevPlan make_dev_plan(const deft_plan* p) {
   d.tickets = const_cast<int32_t*>(b) + L.tickets;
   d.merge_slots = b + L.merge_slots;
   d.merge_stride = L.merge_stride;
+  d.n_mfma_wide = L.n_mfma_wide;
   d.n_mfma = L.n_mfma;
   d.n_valu = L.n_valu;
   d.mask_words = p->mask_words;
@@ -1476,8 +1591,9 @@ static int validate_block_table(const deft_plan* p, const deft_attn_desc* d, con
 template <typename T, int D>
 static int launch_partials(const PartialArgs& pa, hipStream_t st) {
   const int hkv = pa.hkv;
-  if (sizeof(T) != 2 && pa.plan.n_mfma > 0) return fail(DEFT_ERR_UNSUPPORTED, "MFMA work for fp32 inputs");
-  const dim3 grid((pa.plan.n_mfma + pa.plan.n_valu) * hkv), block(512);
+  if (sizeof(T) != 2 && pa.plan.n_mfma + pa.plan.n_mfma_wide > 0)
+    return fail(DEFT_ERR_UNSUPPORTED, "MFMA work for fp32 inputs");
+  const dim3 grid((pa.plan.n_mfma_wide + pa.plan.n_mfma + pa.plan.n_valu) * hkv), block(512);
   if (grid.x == 0) return DEFT_OK;
   // the VALU body's row capacity: 4 when every VALU item fits, else 8
   static_assert(kValuRows == 8, "VALU row capacities are 4 and 8");

@@ -19,6 +19,7 @@ constexpr int kPageSize = 16;
 // a chunk: rows of chunk c are r = j * G + hh for the chunk's j-th slot and
 // the hh-th query head of the KV head being processed (G = Hq / Hkv).
 constexpr int kMfmaRows = 64;      // rows per MFMA work item (4 tiles of 16)
+constexpr int kMfmaWideRows = 128; // rows per wide MFMA work item (groups of more than kMfmaRows rows)
 constexpr int kMfmaMinRows = 16;   // a chunk needs this many rows to use MFMA
 constexpr int kValuRows = 8;       // rows per VALU work item
 
@@ -40,7 +41,7 @@ static_assert(sizeof(WorkItem) == 32, "work items are read as two int4");
 struct ImageLayout {
   size_t chunk_start, group_offsets, chunk_full, slot_query, slot_mask, flat_to_logical,
       query_slot_offsets, query_slots, mfma_items, valu_items, tickets, merge_slots, total_words;
-  int32_t n_mfma, n_valu;
+  int32_t n_mfma_wide, n_mfma, n_valu;   // mfma_items holds the wide items, then the 64-row ones
   // Merge lists at a fixed stride (each query's slots, padded with -1), so
   // the merge reads a query's slot ids without first reading its offsets;
   // 0 when the plan's slot counts are too uneven for that (CSR lists only).
@@ -77,6 +78,9 @@ namespace deft {
 int build_image(deft_plan* p, const deft_attn_desc* desc, std::vector<int32_t>* image,
                 ImageLayout* layout);
 int check_desc(const deft_plan* p, const deft_attn_desc* desc);
+// Compute units of the current device (256, the MI355X count, when it cannot
+// be queried); the planner sizes its work items to it.
+int device_cu_count();
 // Workspace: partial O (bf16 O / l for bf16 inputs, fp32 unnormalised O for
 // fp32 inputs), then part_m and part_l, each 256-byte aligned.
 size_t partial_o_words(const deft_plan* p, const deft_attn_desc* desc);
