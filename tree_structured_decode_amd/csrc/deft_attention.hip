@@ -25,7 +25,8 @@
 // One partial kernel (partial_attention) runs two bodies on one work description:
 //   mfma_body  bf16 groups with >= 16 rows: 16x16x32 bf16 MFMA for S = K Q^T
 //              and O^T = V^T P^T, 64 rows per work-group, the chunk's
-//              tokens split across 4 wave pairs and the splits merged in LDS;
+//              tokens split across 4 wave pairs and the splits merged in LDS
+//              (or 128 rows, 2 splits of 4 waves, for wide items);
 //   valu_body  fp32 inputs and bf16 groups below one MFMA tile: per-token
 //              dot products with wavefront reductions.
 // Scores are kept in log2 units (scale * log2(e) folded in) so exp2 is used;
@@ -954,6 +955,10 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
 // of one row, which is the B-operand layout of the PV product.  Rows in LDS
 // are stored with their 16-byte chunks XOR-swizzled by the row index.  The
 // four token splits of each row half are merged through LDS at the end.
+// Wide items (NSPLIT = 2) cover 128 rows instead: four 32-row groups per
+// split (gr = w % 4, sp = w / 4) share each split's ring and its loads (a
+// quarter each), rendezvous through four flags, and split 1's results are
+// merged into split 0's registers at the end.
 // ---------------------------------------------------------------------------
 template <int D, int NSPLIT>
 struct MfmaShape {
@@ -1473,12 +1478,13 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
 }
 
 // ---------------------------------------------------------------------------
-// One launch for all partial work: the plan's MFMA items take the first
-// n_mfma * Hkv work-groups (dispatched first: the longest), the VALU items
-// the rest, so both kinds share the chip instead of running one after the
-// other.  Block b of either kind takes KV head b % Hkv (n_mfma * Hkv is a
-// multiple of Hkv, so a head keeps its XCD).  One LDS block serves whichever
-// body the work-group runs.
+// One launch for all partial work: the plan's wide (128-row) MFMA items take
+// the first n_mfma_wide * Hkv work-groups, the 64-row MFMA items the next
+// n_mfma * Hkv (dispatched first: the longest), the VALU items the rest, so
+// all kinds share the chip instead of running one after the other.  Block b
+// of any kind takes KV head b % Hkv (each range is a multiple of Hkv, so a
+// head keeps its XCD).  One LDS block serves whichever body the work-group
+// runs.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int R, bool FUSED>
 __global__ __launch_bounds__(512) void partial_attention(PartialArgs a) {
