@@ -164,8 +164,12 @@ def test_constant_values_bf16():
     np.testing.assert_allclose(got, np.broadcast_to(want, got.shape), rtol=2 ** -8, atol=0)
 
 
-@pytest.mark.parametrize("cfg,c", [(1, 64), (3, 512), (2, 256)])
-def test_partials_match_oracle(cfg, c):
+@pytest.mark.parametrize("cfg,c,wide", [(1, 64, None), (3, 512, None), (2, 256, None), (2, 256, "1")])
+def test_partials_match_oracle(monkeypatch, cfg, c, wide):
+    """Per-slot fp32 partials (m, l, unnormalised O) against the oracle's;
+    wide = "1" forces 128-row MFMA items (their own epilogue)."""
+    if wide is not None:
+        monkeypatch.setenv("DEFT_MFMA_WIDE", wide)
     wl = W.standard_workload(cfg, unscaled=True) if cfg == 2 else W.standard_workload(cfg)
     if cfg == 2:
         wl.q = wl.q[:, :8].contiguous()     # keep the oracle quick: 2 KV heads
@@ -191,9 +195,11 @@ def test_partials_match_oracle(cfg, c):
     check_close(po / scale, o / scale, tol, "O / l")
 
 
-@pytest.mark.parametrize("cfg,c", [(3, 512), (2, 520)])
-def test_bf16_normalised_partials_match_oracle(cfg, c):
+@pytest.mark.parametrize("cfg,c,wide", [(3, 512, None), (2, 520, None), (2, 520, "1")])
+def test_bf16_normalised_partials_match_oracle(monkeypatch, cfg, c, wide):
     """The internal partial format of bf16 inputs: O / l rounded to bf16."""
+    if wide is not None:
+        monkeypatch.setenv("DEFT_MFMA_WIDE", wide)
     wl = W.standard_workload(cfg, unscaled=True) if cfg == 2 else W.standard_workload(cfg)
     if cfg == 2:
         wl.q = wl.q[:, :8].contiguous()
