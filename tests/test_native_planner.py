@@ -227,3 +227,25 @@ def test_attention_rejects_plan_without_upload():
     assert rc == D.DEFT_ERR_INVALID_ARGUMENT and "aligned" in D.deft_last_error()
     rc = L.deft_plan_upload(plan.handle, ctypes.byref(desc), None, 1 << 20, None)
     assert rc == D.DEFT_ERR_INVALID_ARGUMENT
+
+
+def test_wide_mfma_item_rule(monkeypatch):
+    """Work items of 128 rows are chosen when the 64-row items would fill the
+    device's compute units twice (256 when no device can be queried): the
+    32K-prefix tree takes them, the 4K-prefix tree does not.  The image holds
+    8 ints per work item, so its size tells the two apart; DEFT_MFMA_WIDE
+    forces either choice."""
+    def plan_bytes(cfg, force):
+        if force is None:
+            monkeypatch.delenv("DEFT_MFMA_WIDE", raising=False)
+        else:
+            monkeypatch.setenv("DEFT_MFMA_WIDE", force)
+        wl = W.standard_workload(cfg)
+        plan = D.deft_plan_create(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens)
+        desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+        return D.deft_plan_device_bytes(plan, desc)[0]
+
+    big_auto, big_wide, big_narrow = plan_bytes(5, None), plan_bytes(5, "1"), plan_bytes(5, "0")
+    assert big_auto == big_wide < big_narrow
+    small_auto, small_wide, small_narrow = plan_bytes(2, None), plan_bytes(2, "1"), plan_bytes(2, "0")
+    assert small_auto == small_narrow > small_wide
