@@ -313,12 +313,16 @@ def test_node_granularity_plan_matches_oracle(cfg):
         _rms_check(got, want, "node granularity")
 
 
-def test_multi_token_workload_matches_oracle():
+@pytest.mark.parametrize("wide", [None, "1"])
+def test_multi_token_workload_matches_oracle(monkeypatch, wide):
     """Multi-token query nodes (a query per draft token, causal inside its
     node): whole output, partials of the internal format, and the
-    single-dispatch variant."""
+    single-dispatch variant; wide = "1" forces 128-row MFMA items on (the
+    prompt chunks' groups have 1024 rows)."""
+    if wide is not None:
+        monkeypatch.setenv("DEFT_MFMA_WIDE", wide)
     wl = W.standard_workload(6)
-    say("multi-token workload")
+    say("multi-token workload", wide)
     q, kc, vc, bt = inputs = gpu_inputs(wl)
     got, ta = run_gpu(wl, inputs=inputs)
     want = oracle_out(wl)
