@@ -142,7 +142,8 @@ typedef struct {
  * Errors: INVALID_ARGUMENT for null pointers, num_nodes < 1,
  * num_queries < 1 or chunk_tokens < 1; INVALID_TREE for parents[i] outside
  * [-1, i), seg_lens[i] < 1, query_nodes[q] outside [0, num_nodes), or more
- * than 2^31 - 1 tokens in total; NO_MEMORY.  *out_plan is set on success.
+ * than 2^31 - 1 tokens in total; UNSUPPORTED for more than 2^31 - 1
+ * (chunk, query) slots; NO_MEMORY.  *out_plan is set on success.
  */
 int deft_plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
                      const int32_t* query_nodes, int32_t num_queries, int32_t chunk_tokens,
@@ -203,8 +204,9 @@ int deft_plan_create_multi_token(const int32_t* parents, const int32_t* seg_lens
                                  const int32_t* query_nodes, const int32_t* query_lens,
                                  int32_t num_queries, int32_t chunk_tokens, deft_plan** out_plan);
 
-/* Free a plan (NULL is ignored).  The caller must first let every stream that
- * consumes its device image get past that work. */
+/* Free a plan (NULL is ignored); waits for its last upload's copy to have
+ * run.  The caller must first let every stream that consumes its device
+ * image get past that work (the image is caller memory and stays). */
 void deft_plan_destroy(deft_plan* plan);
 
 /* Fill *out_view with the plan's arrays (see deft_plan_view). */
@@ -218,7 +220,9 @@ int deft_plan_export(const deft_plan* plan, deft_plan_view* out_view);
  *                     padded to 256 bytes
  * Either output pointer may be NULL.  UNSUPPORTED if desc is outside this
  * build (head_dim not 64/128, page_size != 16, Hq % Hkv != 0, chunk_tokens
- * > 4096); INVALID_ARGUMENT for non-positive shapes.
+ * > 4096), if num_queries * num_q_heads reaches 2^28, or if the work items
+ * times num_kv_heads exceed 2^23 - 1 (one launch's grid; a larger
+ * chunk_tokens makes fewer items); INVALID_ARGUMENT for non-positive shapes.
  */
 int deft_plan_device_bytes(deft_plan* plan, const deft_attn_desc* desc,
                            size_t* plan_bytes, size_t* workspace_bytes);
@@ -228,8 +232,11 @@ int deft_plan_device_bytes(deft_plan* plan, const deft_attn_desc* desc,
  * flattened-to-logical map, merge lists and the kernels' work lists) and copy
  * it into dev_plan (device memory of at least plan_bytes, 256-byte aligned)
  * on `stream`.  The plan remembers dev_plan and desc; later attention calls
- * read the image from there.  The plan's host staging buffer must stay alive
- * until the copy has run (keep the plan alive until the stream passes it).
+ * read the image from there.  The copy's source is a host staging buffer
+ * owned by the plan: a later upload of the same plan, and deft_plan_destroy,
+ * first wait (on the host) for the previous copy to have run, so the caller
+ * need not synchronise for it.  The copy is from pageable memory: not for
+ * use under stream capture.
  */
 int deft_plan_upload(deft_plan* plan, const deft_attn_desc* desc, void* dev_plan,
                      size_t dev_plan_bytes, void* stream);

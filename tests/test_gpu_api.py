@@ -54,3 +54,41 @@ def test_workspace_and_desc_checked():
         D.deft_tree_attention(q, kc, vc, bt, ta.plan, out, other, ta.workspace)
     assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
+
+
+def test_back_to_back_uploads_keep_each_image():
+    """Uploads of one plan for two descs in a row, with no synchronisation
+    between them: the second upload waits for the first copy before it
+    rebuilds the plan's host staging buffer, so both device images are
+    whole (each equals a fresh, synchronised upload of the same desc), and
+    the attention call on the second image matches the oracle."""
+    say("api: back-to-back uploads")
+    wl = W.standard_workload(2)
+    plan = D.deft_plan_create(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens)
+    d_bf16 = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    d_f32 = D.make_desc(torch.float32, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    images = []
+    for desc in (d_f32, d_bf16):
+        pb, _ = D.deft_plan_device_bytes(plan, desc)
+        images.append(torch.zeros(pb // 4, dtype=torch.int32, device=DEV))
+    D.deft_plan_upload(plan, d_f32, images[0])
+    D.deft_plan_upload(plan, d_bf16, images[1])
+    torch.cuda.synchronize()
+    for desc, img in zip((d_f32, d_bf16), images):
+        ref = torch.zeros_like(img)
+        fresh = D.deft_plan_create(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens)
+        D.deft_plan_upload(fresh, desc, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(img, ref)
+        D.deft_plan_destroy(fresh)
+    q, kc, vc, bt = gpu_inputs(wl)
+    _, wb = D.deft_plan_device_bytes(plan, d_bf16)
+    ws = torch.empty(wb, dtype=torch.uint8, device=DEV)
+    out = torch.full_like(q, float("nan"))
+    D.deft_tree_attention(q, kc, vc, bt, plan, out, d_bf16, ws)
+    torch.cuda.synchronize()
+    sel = list(range(0, wl.num_queries, 8))
+    got = out.double().cpu().numpy()[sel]
+    from gpu_helpers import check_close, oracle_out, TOL
+    check_close(got, oracle_out(wl, queries=sel), TOL[torch.bfloat16], "after back-to-back uploads")
+    D.deft_plan_destroy(plan)

@@ -249,3 +249,23 @@ def test_wide_mfma_item_rule(monkeypatch):
     assert big_auto == big_wide < big_narrow
     small_auto, small_wide, small_narrow = plan_bytes(2, None), plan_bytes(2, "1"), plan_bytes(2, "0")
     assert small_auto == small_narrow > small_wide
+
+
+def test_launch_size_limits():
+    """Shapes whose rows or work-groups would not fit one launch's 32-bit
+    grid are refused at sizing time, before anything reaches the device:
+    num_queries * num_q_heads must stay below 2^28 (the merge covers 16 rows
+    per 256-thread work-group), and the partial kernel's work items times
+    the KV heads must stay within 2^23 - 1 work-groups of 512 threads."""
+    plan = D.deft_plan_create([-1, 0], [16, 16], [1] * 65, 32)   # one chunk, 65 slots
+    # 65 * 2^21 rows (below 2^28), two 64-row items per KV head: 2^22 work-groups
+    D.deft_plan_device_bytes(plan, D.make_desc(torch.bfloat16, 1 << 21, 1 << 21, 64, 1))
+    with pytest.raises(D.DeftError) as e:
+        D.deft_plan_device_bytes(plan, D.make_desc(torch.bfloat16, 1 << 22, 1 << 22, 64, 1))
+    assert e.value.code == D.DEFT_ERR_UNSUPPORTED and "2^28" in str(e.value)
+    # one query over 32 one-token chunks: 32 one-row VALU items per KV head
+    small = D.deft_plan_create([-1], [32], [0], 1)
+    D.deft_plan_device_bytes(small, D.make_desc(torch.float32, 1 << 17, 1 << 17, 64, 1))  # 2^22
+    with pytest.raises(D.DeftError) as e:
+        D.deft_plan_device_bytes(small, D.make_desc(torch.float32, 1 << 18, 1 << 18, 64, 1))  # 2^23
+    assert e.value.code == D.DEFT_ERR_UNSUPPORTED and "grid" in str(e.value)

@@ -1524,6 +1524,20 @@ int device_cu_count() {
   return n;
 }
 
+// The staging buffer is the source of an asynchronous copy from pageable
+// memory; it is rebuilt or freed only after that copy has run.
+static hipError_t wait_upload(deft_plan* p) {
+  return p->staging_done ? hipEventSynchronize(static_cast<hipEvent_t>(p->staging_done)) : hipSuccess;
+}
+
+void release_upload(deft_plan* p) {
+  if (!p->staging_done) return;
+  (void)wait_upload(p);
+  (void)hipEventDestroy(static_cast<hipEvent_t>(p->staging_done));
+  p->staging_done = nullptr;
+  (void)hipGetLastError();
+}
+
 static DevPlan make_dev_plan(const deft_plan* p) {
   const int32_t* b = static_cast<const int32_t*>(p->dev);
   const ImageLayout& L = p->layout;
@@ -1688,14 +1702,29 @@ int deft_plan_upload(deft_plan* p, const deft_attn_desc* d, void* dev_plan, size
   if (!p || !dev_plan) return fail(DEFT_ERR_INVALID_ARGUMENT, "plan and dev_plan must not be NULL");
   if (reinterpret_cast<uintptr_t>(dev_plan) % 256 != 0)
     return fail(DEFT_ERR_INVALID_ARGUMENT, "dev_plan must be 256-byte aligned");
+  int rc = deft::hip_check(deft::wait_upload(p), "wait for the previous upload of this plan");
+  if (rc) return rc;
+  deft::release_upload(p);
   deft::ImageLayout L{};
-  int rc = deft::build_image(p, d, &p->staging, &L);
+  rc = deft::build_image(p, d, &p->staging, &L);
   if (rc) return rc;
   if (bytes < 4 * L.total_words) return fail(DEFT_ERR_INVALID_ARGUMENT, "dev_plan buffer too small");
+  hipStream_t st = static_cast<hipStream_t>(stream);
   rc = deft::hip_check(hipMemcpyAsync(dev_plan, p->staging.data(), 4 * L.total_words,
-                                      hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)),
+                                      hipMemcpyHostToDevice, st),
                        "hipMemcpyAsync of the plan image");
   if (rc) return rc;
+  // mark the copy's completion on the current device; without an event,
+  // finish the copy now
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess && hipEventRecord(e, st) == hipSuccess) {
+    p->staging_done = e;
+  } else {
+    if (e) (void)hipEventDestroy(e);
+    (void)hipGetLastError();
+    rc = deft::hip_check(hipStreamSynchronize(st), "hipStreamSynchronize after the plan image copy");
+    if (rc) return rc;
+  }
   p->layout = L;
   p->desc = *d;
   p->dev = dev_plan;

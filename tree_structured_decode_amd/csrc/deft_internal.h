@@ -22,6 +22,8 @@ constexpr int kMfmaRows = 64;      // rows per MFMA work item (4 tiles of 16)
 constexpr int kMfmaWideRows = 128; // rows per wide MFMA work item (groups of more than kMfmaRows rows)
 constexpr int kMfmaMinRows = 16;   // a chunk needs this many rows to use MFMA
 constexpr int kValuRows = 8;       // rows per VALU work item
+constexpr int64_t kMaxQueryRows = int64_t{1} << 28;       // num_queries * num_q_heads < this
+constexpr int64_t kMaxPartialBlocks = (int64_t{1} << 23) - 1; // grid x 512 threads < 2^32
 
 struct WorkItem {                  // two int4 on the device
   int32_t chunk;
@@ -70,7 +72,8 @@ struct deft_plan {
   void* dev = nullptr;
   size_t dev_bytes = 0;
   deft::ImageLayout layout{};
-  std::vector<int32_t> staging;
+  std::vector<int32_t> staging;   // host source of the last upload's copy
+  void* staging_done = nullptr;   // hipEvent_t recorded after that copy
 };
 
 namespace deft {
@@ -81,6 +84,9 @@ int check_desc(const deft_plan* p, const deft_attn_desc* desc);
 // Compute units of the current device (256, the MI355X count, when it cannot
 // be queried); the planner sizes its work items to it.
 int device_cu_count();
+// Waits for the last upload's copy out of the staging buffer and releases
+// its event (called by deft_plan_destroy).
+void release_upload(deft_plan* p);
 // Workspace: partial O (bf16 O / l for bf16 inputs, fp32 unnormalised O for
 // fp32 inputs), then part_m and part_l, each 256-byte aligned.
 size_t partial_o_words(const deft_plan* p, const deft_attn_desc* desc);

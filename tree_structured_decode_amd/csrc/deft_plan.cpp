@@ -112,6 +112,8 @@ static int build_plan(deft_plan* p, const int32_t* parents, const int32_t* seg_l
         touch_pos.push_back(group_count[last]++);
       }
     }
+    if (touch_chunk.size() > static_cast<size_t>(INT32_MAX))
+      return fail(DEFT_ERR_UNSUPPORTED, "more than 2^31 - 1 (chunk, query) slots");
     touch_off[q + 1] = static_cast<int32_t>(touch_chunk.size());
   }
   p->group_offsets.assign(nc + 1, 0);
@@ -310,6 +312,10 @@ int check_desc(const deft_plan* p, const deft_attn_desc* d) {
     return fail(DEFT_ERR_UNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
   if (p && p->chunk_tokens > kMaxChunkTokens)
     return fail(DEFT_ERR_UNSUPPORTED, "chunk_tokens above 4096 is not supported by the kernels");
+  // (query, query head) rows are indexed in 32 bits on the device, and the
+  // merge launch covers them with 16 rows per 256-thread work-group
+  if (p && static_cast<int64_t>(p->num_queries) * d->num_q_heads >= kMaxQueryRows)
+    return fail(DEFT_ERR_UNSUPPORTED, "num_queries * num_q_heads must be below 2^28");
   return DEFT_OK;
 }
 
@@ -362,6 +368,10 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
       (use_wide ? wide : use_mfma ? mfma : valu)
           .push_back({k, r, std::min(blk, rows - r), cs, len, p->group_offsets[k], p->chunk_full[k] ? 1 : 0, lstart});
   }
+  // one launch of 512-thread work-groups covers every item for every KV head
+  if (static_cast<int64_t>(wide.size() + mfma.size() + valu.size()) * d->num_kv_heads > kMaxPartialBlocks)
+    return fail(DEFT_ERR_UNSUPPORTED,
+                "work items x num_kv_heads above 2^23 - 1, the partial kernel's grid limit (raise chunk_tokens)");
   size_t w = 0;
   auto take = [&](size_t n) { size_t at = w; w = align_words(w + n); return at; };
   const int32_t nc = p->num_chunks, S = p->num_slots, W = p->mask_words;
@@ -507,7 +517,11 @@ int deft_plan_create_multi_token(const int32_t* parents, const int32_t* seg_lens
                      out_plan, query_lens);
 }
 
-void deft_plan_destroy(deft_plan* plan) { delete plan; }
+void deft_plan_destroy(deft_plan* plan) {
+  if (!plan) return;
+  deft::release_upload(plan);
+  delete plan;
+}
 
 int deft_plan_export(const deft_plan* p, deft_plan_view* v) {
   if (!p || !v) return fail(DEFT_ERR_INVALID_ARGUMENT, "plan and view must not be NULL");
