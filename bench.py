@@ -372,7 +372,7 @@ def main():
             roof["traffic_detail"] = ent
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == 2 else f"tree-attn latency (us) + achieved HBM GB/s, {wl.name}",
         "value": latency_us,
         "unit": "us",
         "n_gpus": 1,
