@@ -269,3 +269,39 @@ def test_launch_size_limits():
     with pytest.raises(D.DeftError) as e:
         D.deft_plan_device_bytes(small, D.make_desc(torch.float32, 1 << 18, 1 << 18, 64, 1))  # 2^23
     assert e.value.code == D.DEFT_ERR_UNSUPPORTED and "grid" in str(e.value)
+
+
+def test_binding_checks_tensor_shapes():
+    """The attention wrappers check every tensor against the plan and the
+    descriptor before a pointer is taken: a wrong dtype, shape or size is a
+    DeftError (INVALID_ARGUMENT) naming the argument; right-shaped host
+    tensors get as far as the device-pointer conversion, which refuses them."""
+    plan = D.deft_plan_create([-1, 0, 0], [40, 8, 9], [1, 2, 2], 32)   # 57 tokens: 4 pages
+    desc = D.make_desc(torch.bfloat16, 8, 2, 64, 10)
+    bf = torch.bfloat16
+    good = dict(q=torch.zeros(3, 8, 64, dtype=bf), k=torch.zeros(10, 16, 2, 64, dtype=bf),
+                v=torch.zeros(12, 16, 2, 64, dtype=bf), bt=torch.zeros(4, dtype=torch.int32),
+                out=torch.zeros(3, 8, 64, dtype=bf), ws=torch.zeros(1 << 16, dtype=torch.uint8))
+
+    def call(**kw):
+        a = {**good, **kw}
+        D.deft_tree_attention(a["q"], a["k"], a["v"], a["bt"], plan, a["out"], desc, a["ws"])
+
+    for kw, name in [({"q": torch.zeros(3, 8, 64)}, "q"),                        # dtype
+                     ({"q": torch.zeros(2, 8, 64, dtype=bf)}, "q"),              # queries
+                     ({"out": torch.zeros(3, 8, 128, dtype=bf)}, "out"),
+                     ({"k": torch.zeros(9, 16, 2, 64, dtype=bf)}, "k_cache"),   # fewer pages
+                     ({"v": torch.zeros(10, 16, 4, 64, dtype=bf)}, "v_cache"),  # KV heads
+                     ({"bt": torch.zeros(3, dtype=torch.int32)}, "block_table"),
+                     ({"bt": torch.zeros(4, dtype=torch.int64)}, "block_table")]:
+        with pytest.raises(D.DeftError) as e:
+            call(**kw)
+        assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT and str(e.value).split(": ")[1] == name
+    with pytest.raises(ValueError, match="device tensor"):
+        call()
+    s = plan.num_slots
+    for po, pm in [(torch.zeros(s, 8, 64), torch.zeros(s, 8)),                   # bf16 O expected
+                   (torch.zeros(s + 1, 8, 64, dtype=bf), torch.zeros(s, 8))]:
+        with pytest.raises(D.DeftError) as e:
+            D.deft_lse_merge(plan, desc, po, pm, pm, good["out"], D.DEFT_PARTIAL_BF16_NORM)
+        assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT and "part_o" in str(e.value)

@@ -4,7 +4,10 @@ Every function has the name of the C entry point it wraps (include/deft.h)
 and does nothing but convert arguments: torch tensors become device pointers,
 numpy arrays become host pointers, the torch stream becomes a hipStream_t.
 All computation happens inside libdeft.so.  A failing call raises DeftError
-with the library's code and message.
+with the library's code and message.  Since the C ABI sees bare pointers,
+the wrappers of the attention calls first check each tensor's dtype, shape
+and size against the plan and the descriptor (DeftError with
+DEFT_ERR_INVALID_ARGUMENT), so a mis-shaped tensor never reaches a kernel.
 
 torch is imported before the library is loaded so that the process holds one
 HIP runtime (torch's), which libdeft then binds to.
@@ -140,10 +143,15 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 class Plan:
-    """Owns a deft_plan* and frees it on garbage collection."""
+    """Owns a deft_plan* and frees it on garbage collection.  Also keeps the
+    sizes the tensor checks need: queries, slots and logical tokens."""
 
-    def __init__(self, handle: ctypes.c_void_p):
+    def __init__(self, handle: ctypes.c_void_p, logical_tokens: int):
         self.handle = handle
+        v = deft_plan_view()
+        _check(lib().deft_plan_export(handle, ctypes.byref(v)))
+        self.num_queries, self.num_slots = int(v.num_queries), int(v.num_slots)
+        self.logical_tokens = int(logical_tokens)
 
     def __del__(self):
         if getattr(self, "handle", None) and _lib is not None:
@@ -156,7 +164,7 @@ def deft_plan_create(parents, seg_lens, query_nodes, chunk_tokens: int) -> Plan:
     h = _P()
     _check(lib().deft_plan_create(_ptr_i32(p), _ptr_i32(s), int(p.shape[0]), _ptr_i32(q),
                                   int(q.shape[0]), int(chunk_tokens), ctypes.byref(h)))
-    return Plan(h)
+    return Plan(h, int(s.sum(dtype=np.int64)))
 
 
 def deft_plan_create_query_centric(parents, seg_lens, query_nodes, chunk_tokens: int) -> Plan:
@@ -164,7 +172,7 @@ def deft_plan_create_query_centric(parents, seg_lens, query_nodes, chunk_tokens:
     h = _P()
     _check(lib().deft_plan_create_query_centric(_ptr_i32(p), _ptr_i32(s), int(p.shape[0]), _ptr_i32(q),
                                                 int(q.shape[0]), int(chunk_tokens), ctypes.byref(h)))
-    return Plan(h)
+    return Plan(h, int(s.sum(dtype=np.int64)))
 
 
 def deft_plan_create_node_chunks(parents, seg_lens, query_nodes, chunk_tokens: int) -> Plan:
@@ -172,7 +180,7 @@ def deft_plan_create_node_chunks(parents, seg_lens, query_nodes, chunk_tokens: i
     h = _P()
     _check(lib().deft_plan_create_node_chunks(_ptr_i32(p), _ptr_i32(s), int(p.shape[0]), _ptr_i32(q),
                                               int(q.shape[0]), int(chunk_tokens), ctypes.byref(h)))
-    return Plan(h)
+    return Plan(h, int(s.sum(dtype=np.int64)))
 
 
 def deft_plan_create_multi_token(parents, seg_lens, query_nodes, query_lens, chunk_tokens: int) -> Plan:
@@ -185,7 +193,7 @@ def deft_plan_create_multi_token(parents, seg_lens, query_nodes, query_lens, chu
     _check(lib().deft_plan_create_multi_token(_ptr_i32(p), _ptr_i32(s), int(p.shape[0]), _ptr_i32(q),
                                               None if ql is None else _ptr_i32(ql), int(q.shape[0]),
                                               int(chunk_tokens), ctypes.byref(h)))
-    return Plan(h)
+    return Plan(h, int(s.sum(dtype=np.int64)))
 
 
 def deft_plan_destroy(plan: Plan):
@@ -240,7 +248,55 @@ def deft_plan_upload(plan: Plan, desc: deft_attn_desc, dev_plan: torch.Tensor, s
     plan.dev_plan = dev_plan          # keep the device image alive with the plan
 
 
+_DTYPES = {DEFT_DTYPE_F32: torch.float32, DEFT_DTYPE_BF16: torch.bfloat16}
+
+
+def _expect(t, what, dtype, shape=None, min_numel=None, min_rows=None):
+    """shape: the exact shape, or with min_rows the shape after the first
+    dimension, which then needs at least min_rows entries."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        bad = True
+    else:
+        if shape is not None and min_rows is not None:
+            ok_shape = t.dim() == len(shape) + 1 and t.shape[0] >= min_rows and tuple(t.shape[1:]) == tuple(shape)
+        else:
+            ok_shape = shape is None or tuple(t.shape) == tuple(shape)
+        bad = t.dtype != dtype or not ok_shape or (min_numel is not None and t.numel() < min_numel)
+    if bad:
+        want = f"{dtype}" + (f" of shape {tuple(shape)}" if shape is not None and min_rows is None else "") + \
+            (f" of shape (>= {min_rows}, {', '.join(map(str, shape))})" if min_rows is not None else "") + \
+            (f" with at least {min_numel} elements" if min_numel is not None else "")
+        got = f"{t.dtype} of shape {tuple(t.shape)}" if isinstance(t, torch.Tensor) else type(t).__name__
+        raise DeftError(DEFT_ERR_INVALID_ARGUMENT, f"{what}: expected {want}, got {got}")
+
+
+def _check_inputs(plan: Plan, desc, q=None, k_cache=None, v_cache=None, block_table=None, out=None):
+    dt = _DTYPES.get(desc.dtype)
+    if dt is None:
+        return                                   # the library reports the unsupported dtype
+    nq, hq, hkv, d = plan.num_queries, desc.num_q_heads, desc.num_kv_heads, desc.head_dim
+    _expect(q, "q", dt, (nq, hq, d))
+    _expect(out, "out", dt, (nq, hq, d))
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):    # pages [num_pages, page, Hkv, d]
+        _expect(t, name, dt, (desc.page_size, hkv, d), min_rows=desc.num_pages)
+    _expect(block_table, "block_table", torch.int32,
+            min_numel=-(-plan.logical_tokens // max(desc.page_size, 1)))
+
+
+def _check_partials(plan: Plan, desc, fmt, part_o, part_m, part_l):
+    if fmt not in (DEFT_PARTIAL_F32, DEFT_PARTIAL_BF16_NORM):
+        return                                   # the library reports the format
+    s, hq, d = plan.num_slots, desc.num_q_heads, desc.head_dim
+    odt = torch.bfloat16 if fmt == DEFT_PARTIAL_BF16_NORM else torch.float32
+    _expect(part_o, "part_o", odt, (s, hq, d))
+    _expect(part_m, "part_m", torch.float32, (s, hq))
+    _expect(part_l, "part_l", torch.float32, (s, hq))
+
+
 def deft_tree_attention(q, k_cache, v_cache, block_table, plan: Plan, out, desc, workspace, stream=None):
+    _check_inputs(plan, desc, q, k_cache, v_cache, block_table, out)
     _check(lib().deft_tree_attention(_dev(q), _dev(k_cache), _dev(v_cache), _dev(block_table),
                                      plan.handle, _dev(out), ctypes.byref(desc), _dev(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -248,6 +304,7 @@ def deft_tree_attention(q, k_cache, v_cache, block_table, plan: Plan, out, desc,
 
 def deft_tree_attention_fused(q, k_cache, v_cache, block_table, plan: Plan, out, desc, workspace,
                               stream=None):
+    _check_inputs(plan, desc, q, k_cache, v_cache, block_table, out)
     _check(lib().deft_tree_attention_fused(_dev(q), _dev(k_cache), _dev(v_cache), _dev(block_table),
                                            plan.handle, _dev(out), ctypes.byref(desc), _dev(workspace),
                                            workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -255,6 +312,8 @@ def deft_tree_attention_fused(q, k_cache, v_cache, block_table, plan: Plan, out,
 
 def deft_partial_attention(q, k_cache, v_cache, block_table, plan: Plan, desc, part_o, part_m,
                            part_l, partial_format=DEFT_PARTIAL_F32, stream=None):
+    _check_inputs(plan, desc, q, k_cache, v_cache, block_table)
+    _check_partials(plan, desc, partial_format, part_o, part_m, part_l)
     _check(lib().deft_partial_attention(_dev(q), _dev(k_cache), _dev(v_cache), _dev(block_table),
                                         plan.handle, ctypes.byref(desc), _dev(part_o), _dev(part_m),
                                         _dev(part_l), int(partial_format), _stream(stream)))
@@ -262,5 +321,7 @@ def deft_partial_attention(q, k_cache, v_cache, block_table, plan: Plan, desc, p
 
 def deft_lse_merge(plan: Plan, desc, part_o, part_m, part_l, out, partial_format=DEFT_PARTIAL_F32,
                    stream=None):
+    _check_inputs(plan, desc, out=out)
+    _check_partials(plan, desc, partial_format, part_o, part_m, part_l)
     _check(lib().deft_lse_merge(plan.handle, ctypes.byref(desc), _dev(part_o), _dev(part_m),
                                 _dev(part_l), int(partial_format), _dev(out), _stream(stream)))
