@@ -121,6 +121,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
                     help="eager steps only (for rocprofv3 kernel traces and counters)")
+    ap.add_argument("--profile-graph", action="store_true",
+                    help="with --profile-run: replay the partial kernel's timed graph instead")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain elementwise copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -220,8 +222,22 @@ def main():
         step(i)
     torch.cuda.synchronize()
     if args.profile_run:
-        for i in range(args.steps):
-            step(i)
+        if args.profile_graph:
+            # the partial kernel's timed leg as bench.py runs it: a graph of
+            # K partial-only launches over the cold copies, replayed 1 + 5 times
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.graph(g, stream=s):
+                for i in range(args.steps):
+                    step(i, "partial")
+            torch.cuda.synchronize()
+            for _ in range(6):
+                g.replay()
+                torch.cuda.synchronize()
+        else:
+            for i in range(args.steps):
+                step(i)
         torch.cuda.synchronize()
         print(json.dumps({"profile_run": wl.name, "chunk_tokens": wl.chunk_tokens, "steps": args.steps,
                           "copies": copies, "kv_bytes": kv_bytes, "q_bytes": q_bytes,
