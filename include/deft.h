@@ -25,7 +25,9 @@
  *     device memory of the current device;
  *   - streams are hipStream_t passed as void* (NULL = the null stream);
  *   - every device-side call is asynchronous on its stream and never
- *     synchronises the host;
+ *     synchronises the host, with the exceptions each call states
+ *     (deft_plan_upload and deft_plan_destroy wait for the plan's previous
+ *     upload copy; DEFT_VALIDATE=1 synchronises the attention calls);
  *   - the library never allocates device memory: plan images, workspaces,
  *     KV pools and outputs all belong to the caller;
  *   - a call returns DEFT_OK or a negative code; deft_last_error() then
