@@ -155,7 +155,8 @@ int deft_plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t nu
  * Query-centric baseline plan, for measuring what KV-Guided Grouping saves
  * on the same hardware (the pages contrast DeFT with per-query attention
  * that reloads the shared prefix for every query: abstract; Guide, "The
- * Memory Wall and Redundant IO").  Same arguments and errors as
+ * Tree-Attention Bottleneck: Redundant Memory IO and Severe Load
+ * Imbalances", "1. Massive Redundant Memory Access (IO)").  Same arguments and errors as
  * deft_plan_create (plus INVALID_TREE if the summed path lengths exceed
  * 2^31 - 1).  Each query's root-to-node path tokens (root segment first, each
  * segment in order) form their own run of the flat index space, queries in
@@ -274,10 +275,15 @@ int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
                         void* stream);
 
 /*
- * deft_tree_attention in one dispatch per partial kernel (the method's
- * single-pass variant: partial results are merged where they are produced,
- * "2. Flattened Tree KV Splitting" / "The Online Softmax Tile Accumulation").
- * Every work-group, after writing its partials, takes a device-scope
+ * deft_tree_attention in one dispatch per partial kernel: the per-chunk
+ * partials are merged by the partial kernel itself instead of a second
+ * kernel (the Guide's "3. Fused In-SRAM Online Softmax Merging" describes
+ * merging partial results where they are produced; "The Online Softmax Tile
+ * Accumulation" gives the rule).  Unlike that description, partials still
+ * pass through memory: the workspace holds them as for deft_tree_attention
+ * (4.46 MB written and read back on the 4K-prefix / 64-node tree), because
+ * the chunks of one query run on different compute units.  Every
+ * work-group, after writing its partials, takes a device-scope
  * acquire-release ticket for each (query, head) row it wrote; the one that
  * takes a row's last ticket merges that row and writes `out`, then resets the
  * ticket.  The tickets live in the plan's device image (zero after upload and

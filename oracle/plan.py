@@ -182,8 +182,9 @@ def ref_plan(parents, seg_lens, query_nodes, chunk_tokens: int, query_lens=None)
 
 def ref_plan_query_centric(parents, seg_lens, query_nodes, chunk_tokens: int) -> dict:
     """The query-centric baseline plan (no KV sharing), the per-query reading
-    of attention that DeFT's abstract and the Guide's "The Memory Wall and
-    Redundant IO" contrast it with: each query's root-to-node path tokens
+    of attention that DeFT's abstract and the Guide's "The Tree-Attention
+    Bottleneck: Redundant Memory IO and Severe Load Imbalances" ("1. Massive
+    Redundant Memory Access (IO)") contrast it with: each query's root-to-node path tokens
     (root segment first, every segment in order) form their own run of the
     flat index space, queries one after another; each run is cut into
     chunk_tokens windows from its own start; every chunk holds one slot (its

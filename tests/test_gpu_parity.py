@@ -370,26 +370,27 @@ def test_single_node_single_query_and_duplicates():
             check_close(got, oracle_out(wl), TOL[dtype], "edge")
 
 
-def test_long_context_spec_tree_sampled():
+@pytest.mark.timeout(900)
+def test_long_context_spec_tree_all_queries():
     """The 32K-prefix / 256-node tree in a pool filling ~60% of HBM, pages at
-    random positions; a sample of queries checked against the oracle, at long
-    chunks (many pipeline steps per wave, several work-groups per CU in turn),
-    repeated because a stale-operand race would show up only in some runs."""
+    random positions: every query and head against the oracle (computed once,
+    about half a minute of host time), at long chunks (many pipeline steps
+    per wave, several work-groups per CU in turn, 128-row items that cover
+    every row block of every chunk), repeated because a stale-operand race
+    would show up only in some runs."""
     total = torch.cuda.get_device_properties(0).total_memory
     pages = W.hbm_pool_pages(total)
     wl = W.standard_workload(5, pool_pages=pages)
     say("long context", "pool pages", pages)
     inputs = gpu_inputs(wl)
-    depth = wl.meta["depths"]
-    pick = sorted({0, 1, len(wl.query_nodes) - 1, int(np.argmax(depth)), 100, 200})
-    want = oracle_out(wl, queries=pick)
+    say("long context", "oracle over", len(wl.query_nodes), "queries")
+    want = oracle_out(wl)
     for c in (4096, 2048):
         for rep in range(2):
             say("long context C", c, "rep", rep)
             got, _ = run_gpu(wl, chunk_tokens=c, inputs=inputs)
-            assert np.isfinite(got).all(), f"C={c} rep {rep}: non-finite output"
-            check_close(got[pick], want, 2e-2, f"long context C={c}")
-            _rms_check(got[pick], want, f"long context C={c}")
+            check_close(got, want, 2e-2, f"long context C={c} rep {rep}")
+            _rms_check(got, want, f"long context C={c} rep {rep}")
 
 
 def test_validate_block_table_host_check(monkeypatch):
