@@ -297,6 +297,36 @@ int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_
                               void* stream);
 
 /*
+ * Size of the device scratch that deft_tree_attention_noalloc uses for the
+ * partial results (one copy per GPU the library runs on, held until the
+ * process ends).
+ */
+#define DEFT_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * deft_tree_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same two kernels and results, bit for bit, but the
+ * per-slot partials go to a library-owned device scratch of
+ * DEFT_NOALLOC_SCRATCH_BYTES instead of a caller workspace, and the call
+ * allocates nothing.  The caller still passes q, the KV pool, block_table,
+ * the uploaded plan and out (device pointers, layouts as for
+ * deft_tree_attention).  The scratch's device address is looked up on the
+ * first call on each device (with that device current) and kept.  Every
+ * call on one GPU shares that GPU's scratch, so calls that overlap on one
+ * GPU (on different streams, or from several threads) race and must be
+ * ordered by the caller; nothing in the scratch needs to start at zero.
+ * DEFT_VALIDATE is not honoured here (that check copies to host memory and
+ * synchronises).  Errors: those of deft_tree_attention, and
+ * DEFT_ERR_UNSUPPORTED when the plan's workspace size (deft_plan_device_bytes)
+ * exceeds DEFT_NOALLOC_SCRATCH_BYTES (a larger chunk_tokens means fewer
+ * slots), before anything is launched.
+ */
+int deft_tree_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const deft_plan* plan, void* out,
+                                const deft_attn_desc* desc, void* stream);
+
+/*
  * The partial-attention kernel on its own ("The Online Softmax Tile
  * Accumulation" applied per chunk).  For every slot s (chunk c, query q) and
  * query head h, over the chunk's tokens visible to q:

@@ -39,6 +39,7 @@
 #include <cstdlib>
 #include <string>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -1692,6 +1693,39 @@ static int run_merge(const deft_plan* p, const deft_attn_desc* d, const float* p
   return hip_check(hipGetLastError(), "launch of lse_merge");
 }
 
+// Workspace of deft_tree_attention_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  Host code
+// never passes `scratch` itself to a kernel (its host-side name is not a
+// device address); it looks the device address up once per device with
+// hipGetSymbolAddress and passes that pointer.
+static_assert(DEFT_NOALLOC_SCRATCH_BYTES % 256 == 0, "whole 256-byte blocks");
+static __device__ __align__(256) char scratch[DEFT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call for that device (with it current) and kept.
+static int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxScratchDevices] = {};
+  int dev = 0;
+  int rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc) return rc;
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(DEFT_ERR_UNSUPPORTED, "device ordinal " + std::to_string(dev) + " above the no-alloc path's " +
+                                          std::to_string(kMaxScratchDevices) + " devices");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    rc = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress of the no-alloc scratch");
+    if (rc) return rc;
+    if (!p) return fail(DEFT_ERR_HIP, "hipGetSymbolAddress returned NULL for the no-alloc scratch");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return DEFT_OK;
+}
+
 }  // namespace deft
 
 using deft::fail;
@@ -1815,6 +1849,35 @@ int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_
   // (query, head) row merges it (fused_merge_tail).
   return deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, po, pm, pl, po_bf16,
                             static_cast<hipStream_t>(stream), out);
+}
+
+int deft_tree_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const deft_plan* plan, void* out,
+                                const deft_attn_desc* desc, void* stream) {
+  int rc = deft::check_ready(plan, desc);
+  if (rc) return rc;
+  const size_t need = deft::workspace_bytes_for(plan, desc);
+  if (need > DEFT_NOALLOC_SCRATCH_BYTES)
+    return fail(DEFT_ERR_UNSUPPORTED, "this plan's partial results need " + std::to_string(need) +
+                                          " bytes, above the no-alloc scratch of " +
+                                          std::to_string(static_cast<size_t>(DEFT_NOALLOC_SCRATCH_BYTES)) +
+                                          " bytes (use deft_tree_attention with a workspace, or a larger "
+                                          "chunk_tokens)");
+  void* ws = nullptr;
+  rc = deft::scratch_address(&ws);
+  if (rc) return rc;
+  if (!out) return fail(DEFT_ERR_INVALID_ARGUMENT, "out must not be NULL");
+  // the same kernels and partial format as deft_tree_attention, on the scratch
+  const bool po_bf16 = desc->dtype == DEFT_DTYPE_BF16;
+  const size_t sh = static_cast<size_t>(plan->num_slots) * desc->num_q_heads;
+  auto align = [](size_t n) { return (n + 63) & ~static_cast<size_t>(63); };
+  float* po = static_cast<float*>(ws);
+  float* pm = po + align(deft::partial_o_words(plan, desc));
+  float* pl = pm + align(sh);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, po, pm, pl, po_bf16, st);
+  if (rc) return rc;
+  return deft::run_merge(plan, desc, po, pm, pl, out, po_bf16, st);
 }
 
 }  // extern "C"

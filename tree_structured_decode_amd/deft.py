@@ -38,8 +38,9 @@ EXPORTED_SYMBOLS = (
     "deft_plan_create", "deft_plan_create_query_centric", "deft_plan_create_node_chunks",
     "deft_plan_create_multi_token", "deft_plan_destroy", "deft_plan_export", "deft_plan_device_bytes",
     "deft_plan_upload", "deft_tree_attention", "deft_tree_attention_fused", "deft_partial_attention",
-    "deft_lse_merge", "deft_last_error",
+    "deft_lse_merge", "deft_last_error", "deft_tree_attention_noalloc",
 )
+DEFT_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _P = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -96,6 +97,7 @@ def lib() -> ctypes.CDLL:
     L.deft_tree_attention.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.POINTER(deft_attn_desc),
                                       _P, ctypes.c_size_t, _P]
     L.deft_tree_attention_fused.argtypes = L.deft_tree_attention.argtypes
+    L.deft_tree_attention_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.POINTER(deft_attn_desc), _P]
     L.deft_partial_attention.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(deft_attn_desc),
                                          _P, _P, _P, ctypes.c_int32, _P]
     L.deft_lse_merge.argtypes = [_P, ctypes.POINTER(deft_attn_desc), _P, _P, _P, ctypes.c_int32,
@@ -104,8 +106,8 @@ def lib() -> ctypes.CDLL:
     for name in ("deft_plan_create", "deft_plan_create_query_centric", "deft_plan_create_node_chunks",
                  "deft_plan_create_multi_token", "deft_plan_export",
                  "deft_plan_device_bytes", "deft_plan_upload",
-                 "deft_tree_attention", "deft_tree_attention_fused", "deft_partial_attention",
-                 "deft_lse_merge"):
+                 "deft_tree_attention", "deft_tree_attention_fused", "deft_tree_attention_noalloc",
+                 "deft_partial_attention", "deft_lse_merge"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -308,6 +310,12 @@ def deft_tree_attention_fused(q, k_cache, v_cache, block_table, plan: Plan, out,
     _check(lib().deft_tree_attention_fused(_dev(q), _dev(k_cache), _dev(v_cache), _dev(block_table),
                                            plan.handle, _dev(out), ctypes.byref(desc), _dev(workspace),
                                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def deft_tree_attention_noalloc(q, k_cache, v_cache, block_table, plan: Plan, out, desc, stream=None):
+    _check_inputs(plan, desc, q, k_cache, v_cache, block_table, out)
+    _check(lib().deft_tree_attention_noalloc(_dev(q), _dev(k_cache), _dev(v_cache), _dev(block_table),
+                                             plan.handle, _dev(out), ctypes.byref(desc), _stream(stream)))
 
 
 def deft_partial_attention(q, k_cache, v_cache, block_table, plan: Plan, desc, part_o, part_m,
