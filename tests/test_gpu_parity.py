@@ -164,12 +164,18 @@ def test_constant_values_bf16():
     np.testing.assert_allclose(got, np.broadcast_to(want, got.shape), rtol=2 ** -8, atol=0)
 
 
-@pytest.mark.parametrize("cfg,c,wide", [(1, 64, None), (3, 512, None), (2, 256, None), (2, 256, "1")])
-def test_partials_match_oracle(monkeypatch, cfg, c, wide):
+FORCE_WIDE = ("DEFT_MFMA_WIDE", "1")
+FORCE_GROUP = ("DEFT_MFMA_GROUP", "1")
+
+
+@pytest.mark.parametrize("cfg,c,force", [(1, 64, None), (3, 512, None), (2, 256, None), (2, 256, FORCE_WIDE),
+                                         (2, 96, FORCE_GROUP)])
+def test_partials_match_oracle(monkeypatch, cfg, c, force):
     """Per-slot fp32 partials (m, l, unnormalised O) against the oracle's;
-    wide = "1" forces 128-row MFMA items (their own epilogue)."""
-    if wide is not None:
-        monkeypatch.setenv("DEFT_MFMA_WIDE", wide)
+    `force` selects 128-row MFMA items or whole-group items (each with its
+    own epilogue)."""
+    if force is not None:
+        monkeypatch.setenv(*force)
     wl = W.standard_workload(cfg, unscaled=True) if cfg == 2 else W.standard_workload(cfg)
     if cfg == 2:
         wl.q = wl.q[:, :8].contiguous()     # keep the oracle quick: 2 KV heads
@@ -195,11 +201,12 @@ def test_partials_match_oracle(monkeypatch, cfg, c, wide):
     check_close(po / scale, o / scale, tol, "O / l")
 
 
-@pytest.mark.parametrize("cfg,c,wide", [(3, 512, None), (2, 520, None), (2, 520, "1")])
-def test_bf16_normalised_partials_match_oracle(monkeypatch, cfg, c, wide):
+@pytest.mark.parametrize("cfg,c,force", [(3, 512, None), (2, 520, None), (2, 520, FORCE_WIDE),
+                                         (2, 136, FORCE_GROUP)])
+def test_bf16_normalised_partials_match_oracle(monkeypatch, cfg, c, force):
     """The internal partial format of bf16 inputs: O / l rounded to bf16."""
-    if wide is not None:
-        monkeypatch.setenv("DEFT_MFMA_WIDE", wide)
+    if force is not None:
+        monkeypatch.setenv(*force)
     wl = W.standard_workload(cfg, unscaled=True) if cfg == 2 else W.standard_workload(cfg)
     if cfg == 2:
         wl.q = wl.q[:, :8].contiguous()
@@ -450,6 +457,45 @@ def test_wide_mfma_items_standard_tree_and_fused(monkeypatch):
     q, kc, vc, bt = gpu_inputs(wl)
     got, ta = run_gpu(wl, inputs=(q, kc, vc, bt))
     check_close(got, oracle_out(wl), TOL[torch.bfloat16], "wide cfg2")
+    out2 = torch.full_like(q, float("nan"))
+    D.deft_tree_attention_fused(q, kc, vc, bt, ta.plan, out2, ta.desc, ta.workspace)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.double().cpu().numpy(), got)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("c", [16, 48, 96, 144, 544])
+@pytest.mark.parametrize("branches", [20, 70])
+def test_group_items_match_oracle(monkeypatch, branches, c, d):
+    """Whole-group MFMA items (up to 256 rows, no token split, a shared
+    four-stage ring), forced on: 20 branches on a 300-token prompt give
+    80-row groups (three of eight waves with rows, a partial row tile), 70
+    branches give 280-row groups (a full 256-row item and a 24-row one), at
+    chunk sizes of one, two, three, five and seventeen 32-token steps
+    (ring reuse, partial last steps)."""
+    monkeypatch.setenv("DEFT_MFMA_GROUP", "1")
+    p, s, qn = W.shared_prompt_branches(300, branches, 90)
+    wl = W.make_workload("group", p, s, qn, chunk_tokens=c, hq=8, hkv=2, d=d, dtype=torch.bfloat16,
+                         seed=5 * c + d + branches, placement="scattered",
+                         pool_pages=2 * (-(-int(s.sum()) // 16)) + 5, value_scale=1.0 / np.sqrt(d))
+    say("group", branches, c, d)
+    got, _ = run_gpu(wl)
+    want = oracle_out(wl)
+    check_close(got, want, TOL[torch.bfloat16], f"group {branches} {c} {d}")
+    _rms_check(got, want, f"group {branches} {c} {d}")
+
+
+def test_group_items_standard_tree_and_fused(monkeypatch):
+    """The 4K-prefix tree at C = 128 (256-row groups, 33 chunks) with
+    whole-group items forced on: against the oracle, and the single-dispatch
+    path bit-identical to the two-dispatch one."""
+    monkeypatch.setenv("DEFT_MFMA_GROUP", "1")
+    wl = W.standard_workload(2, chunk_tokens=128)
+    say("group standard", wl.chunk_tokens)
+    q, kc, vc, bt = gpu_inputs(wl)
+    got, ta = run_gpu(wl, inputs=(q, kc, vc, bt))
+    check_close(got, oracle_out(wl), TOL[torch.bfloat16], "group cfg2")
+    _rms_check(got, oracle_out(wl), "group cfg2")
     out2 = torch.full_like(q, float("nan"))
     D.deft_tree_attention_fused(q, kc, vc, bt, ta.plan, out2, ta.desc, ta.workspace)
     torch.cuda.synchronize()

@@ -74,7 +74,7 @@ struct DevPlan {
   const int4* valu_items;
   int32_t* tickets;          // [Nq * Hq], zero between calls (fused merge)
   const int32_t* merge_slots;   // [Nq][merge_stride] slot ids padded with -1, or unused
-  int32_t n_mfma_wide, n_mfma, n_valu, mask_words, num_queries, merge_stride;   // mfma_items: wide, then 64-row
+  int32_t n_mfma_group, n_mfma_wide, n_mfma, n_valu, mask_words, num_queries, merge_stride;   // mfma_items: group, wide, 64-row
 };
 
 // Operands of the per-(query, head) merge (the merge kernel and the fused
@@ -1479,6 +1479,399 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
 }
 
 // ---------------------------------------------------------------------------
+// MFMA partial kernel for whole groups (bf16): one work-group takes every
+// row of a chunk's group for one KV head, up to 256 rows (8 waves of 32 rows,
+// two 16-row tiles each), and streams the chunk's KV into LDS once for all of
+// them ("1. KV-Guided Grouping": the group's KV is loaded on chip once and
+// every grouped query scores against it).  There is no token split: every
+// wave runs every 32-token step of the chunk on its own rows, so a wave's
+// (O, m, l) is final after the loop and is written straight from registers
+// (no merge through LDS, no wait for a slower split).  The 8 waves share one
+// NSTG-stage LDS ring filled NSTG-1 steps ahead by direct-to-LDS loads, each
+// wave loading 1/8 of a step's K and V rows (and, for waves 0-3, the mask
+// words of 64 rows); one work-group barrier per step both publishes step i's
+// loads and frees the stage read in step i-1.  The arithmetic of a step
+// (S^T = K Q^T, mask, online softmax with the lazily raised running max, O^T
+// += V^T P^T, row sums on the matrix core) is that of mfma_body.
+// ---------------------------------------------------------------------------
+template <int D>
+struct MfmaGroupShape {
+  static constexpr int NWAVE = 8;
+  static constexpr int ROWS = 32 * NWAVE;        // rows of a work item
+  static constexpr int NSTG = 4;                 // ring stages (NSTG - 1 steps ahead)
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILE_B = 32 * ROWB;
+  static constexpr int STAGE_B = 2 * TILE_B + 4 * ROWS;   // K, V, a mask word per row
+  static constexpr int RING_B = NSTG * STAGE_B;
+  // LDS carve-out: ring, the block's Q rows, staged token rows, fused-merge lists
+  static constexpr int QOFF = RING_B;
+  static constexpr int TOK_OFF = QOFF + ROWS * ROWB;
+  static constexpr int LIST_OFF = TOK_OFF + 4 * kMaxChunkTokens;
+  static constexpr int LDS_B = LIST_OFF + 4 * (ROWS + 4);
+};
+
+template <int D, bool FUSED>
+__device__ __forceinline__ void mfma_group_body(const PartialArgs& a, char* lds, int bid, int item_base) {
+  using Shape = MfmaGroupShape<D>;
+  constexpr int NWAVE = Shape::NWAVE;
+  constexpr int NSTG = Shape::NSTG;
+  constexpr int NRT = 2;                // row tiles per wave
+  constexpr int WROWS = NRT * 16;       // rows per wave
+  constexpr int ROWS = Shape::ROWS;
+  constexpr int KS = D / 32;            // k-steps of S = K Q^T
+  constexpr int DT = D / 16;            // d-tiles of O^T
+  constexpr int CH = D / 8;             // 16-byte chunks per token row
+  constexpr int ROWB = Shape::ROWB;
+  constexpr int TILE_B = Shape::TILE_B;
+  constexpr int STAGE_B = Shape::STAGE_B;
+  constexpr int NI = TILE_B / 1024;     // 1 KB direct loads per tile
+  constexpr int RPI = 64 / CH;          // token rows per direct load
+  constexpr int NL = 2 * NI / NWAVE;    // direct loads per wave and step
+  constexpr int MASK_WAVES = ROWS / 64; // waves that also load 64 rows' mask words
+  static_assert(NL >= 1 && NL * NWAVE == 2 * NI, "a step's K and V loads split evenly over the waves");
+  static_assert(NI % NL == 0, "a wave's loads lie in one tile");
+  static_assert(Shape::LDS_B <= 160 * 1024, "LDS carve-out");
+  char* smem = lds;
+  int32_t* tok_row = reinterpret_cast<int32_t*>(lds + Shape::TOK_OFF);
+
+  const DevPlan& P = a.plan;
+  const int g = bid % a.hkv;
+  const int item = item_base + bid / a.hkv;
+  const int4 it0 = P.mfma_items[2 * item];
+  const int4 it1 = P.mfma_items[2 * item + 1];
+  const int32_t rb = it0.y, nr = it0.z, cs = it0.w;
+  const int32_t len = it1.x, gofs = it1.y;
+  const bool full = it1.z != 0;
+  const int W = P.mask_words;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kvsel = w * NL / NI;        // this wave loads K (0) or V (1) rows
+  const int n0 = w * NL % NI;           // its first load of that tile
+  const bool loads_mask = w < MASK_WAVES;
+  const bool active = WROWS * w < nr;   // the wave has rows to compute
+  const int lr = lane & 15, lj = lane >> 4;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k);
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v);
+
+  // The block's Q rows (ROWS * 2D bytes) are copied once into their own LDS
+  // region, 1 KB per copy (NQW per wave): copy n holds rows RPQ*n ..
+  // RPQ*n + RPQ-1, its lane i taking 16-byte chunk (i % CH) ^ (R % CH) of row
+  // R = RPQ*n + i / CH.  The rows' queries are looked up alongside the
+  // staging's flat-to-logical lookups and the copies issued alongside its
+  // block-table lookups.  Rows past nr copy a valid row (masked later).
+  constexpr int RPQ = 1024 / ROWB;
+  constexpr int NQW = ROWS * ROWB / 1024 / NWAVE;
+  static_assert(NQW >= 1 && NQW * NWAVE * 1024 == ROWS * ROWB, "whole 1 KB Q copies per wave");
+  const uint32_t q_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + Shape::QOFF));
+  int32_t qsq[NQW];
+#pragma unroll
+  for (int j = 0; j < NQW; ++j) {
+    const int R = RPQ * (NQW * w + j) + lane / CH;
+    qsq[j] = P.slot_query[gofs + (rb + min(R, nr - 1)) / a.grp];
+  }
+  // token rows are stored as rows of this KV head: pool row * Hkv + g
+  stage_token_rows<RPI, 512>(tok_row, P, a.block_table, cs, len, it1.w, a.hkv, g, [&] {
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) {
+      const int R = RPQ * (NQW * w + j) + lane / CH;
+      const int row = rb + min(R, nr - 1);
+      const int head = g * a.grp + row % a.grp;
+      const int c = (lane % CH) ^ (R % CH);
+      lds_dma16(qp + (static_cast<int64_t>(qsq[j]) * a.hq + head) * D + c * 8, q_lds + (NQW * w + j) * 1024);
+    }
+  });
+  // Row of the mask word this lane loads (lane i <-> row 64 w + i).
+  const int mrow = 64 * (loads_mask ? w : 0) + lane;
+  const int32_t mask_slot = gofs + (rb + (mrow < nr ? mrow : 0)) / a.grp;
+  const uint32_t* mask_src = P.slot_mask + static_cast<size_t>(mask_slot) * W;
+  lds_barrier();   // the staged token rows are visible (the Q copies may still be in flight)
+
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const int lrow = lane / CH;            // row of each direct load this lane fetches
+  const int lch = lane % CH;             // its 16-byte LDS slot in that row
+  // Load n fetches rows n*RPI + lrow of a step; lane (lrow, lch) fetches
+  // chunk lch ^ (R % CH) of row R (LDS slot p of row R holds chunk
+  // p ^ (R % CH)); the swizzle depends on n only through n % NSW.
+  constexpr int NSW = RPI < CH ? CH / RPI : 1;
+  const char* lbase[NSW];
+#pragma unroll
+  for (int c = 0; c < NSW; ++c)
+    lbase[c] = reinterpret_cast<const char*>(kvsel ? vp : kp) + (lch ^ ((c * RPI + lrow) % CH)) * 16;
+  // This wave's loads of `step` into ring stage `stage` (staged rows run to a
+  // multiple of 512 tokens, entries past the chunk end holding its last
+  // token, so a partial last step needs no special case).
+  constexpr int OPS_K = NL;                       // vector-memory operations per step
+  auto issue = [&](int step, int stage) {
+    int32_t rows[NL];
+    const int32_t* tr = tok_row + step * 32 + lrow * NI + n0;   // the permuted layout
+    if constexpr (NL >= 4) {
+#pragma unroll
+      for (int j = 0; j < NL; j += 4) {
+        const int4 v4 = *reinterpret_cast<const int4*>(tr + j);
+        rows[j] = v4.x; rows[j + 1] = v4.y; rows[j + 2] = v4.z; rows[j + 3] = v4.w;
+      }
+    } else if constexpr (NL == 2) {
+      const int2 v2 = *reinterpret_cast<const int2*>(tr);
+      rows[0] = v2.x; rows[1] = v2.y;
+    } else {
+      rows[0] = tr[0];
+    }
+    const uint32_t sd = ring_lds + stage * STAGE_B;
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+      lds_dma16(lbase[(n0 + j) % NSW] + static_cast<uint64_t>(static_cast<uint32_t>(rows[j])) * ROWB,
+                sd + kvsel * TILE_B + (n0 + j) * 1024);
+    if (loads_mask) lds_dma4(mask_src + step, sd + 2 * TILE_B + w * 256);
+  };
+  // waits until at most `later` steps' loads of this wave are outstanding
+  auto wait_steps = [&](int later) {
+    if (loads_mask) {
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * (OPS_K + 1)));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(OPS_K + 1));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    } else {
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * OPS_K));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(OPS_K));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+  };
+  static_assert(NSTG == 4, "wait_steps covers up to two later steps");
+
+  const int nsteps = (len + 31) / 32;
+  // The first NSTG-1 steps go out before the wait for the Q copies, which
+  // are older: waiting until only those steps' loads are outstanding covers
+  // the copies.
+  const int pro = min(NSTG - 1, nsteps);
+  for (int s = 0; s < pro; ++s) issue(s, s);
+  if (loads_mask) {
+    if (pro == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * (OPS_K + 1)));
+    else if (pro == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * (OPS_K + 1)));
+    else if (pro == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(OPS_K + 1));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  } else {
+    if (pro == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * OPS_K));
+    else if (pro == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * OPS_K));
+    else if (pro == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(OPS_K));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  }
+  static_assert(NSTG - 1 == 3, "the prologue waits cover up to three steps");
+  lds_barrier();
+  // Q^T fragments (B operand of S^T = K Q^T) of this wave's 32 rows: lane
+  // (lr, lj) takes d = 32 ks + 8 lj .. +7 of row R = 32w + 16rt + lr, i.e.
+  // chunk 4 ks + lj, stored in slot (4 ks + lj) ^ (R % CH).
+  bf16x8 qf[NRT][KS];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int R = WROWS * w + rt * 16 + lr;
+      qf[rt][ks] = *reinterpret_cast<const bf16x8*>(smem + Shape::QOFF + R * ROWB + (((4 * ks + lj) ^ (R % CH)) * 16));
+    }
+
+  f32x4 o[DT][NRT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Per row tile: the running max m_run (raw score units) with its exp2
+  // offset mc = m_run * scale * log2(e) and rescale threshold thr, both
+  // updated only when m_run rises; the lane's true max; and the row sum of
+  // P, accumulated by the matrix core against a tile of ones.
+  const float cl2 = a.scale_log2;
+  float m_run[NRT], m_true[NRT], mc[NRT], thr[NRT];
+  f32x4 lacc[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    m_run[rt] = kNegInf;
+    m_true[rt] = kNegInf;
+    mc[rt] = 0.f;
+    thr[rt] = kNegInf;
+    lacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+
+  // LDS byte offsets (within a stage) of this lane's operand fragments: K
+  // fragment n = (ks, tt) for S, and the two halves of V^T d-tile dt for PV.
+  const int rk0 = 8 * (lr >> 2) + (lr & 3);   // K rows of this lane, per token tile
+  int koff[2 * KS], voff[DT][2];
+#pragma unroll
+  for (int n = 0; n < 2 * KS; ++n) {
+    const int ks = n >> 1, R = rk0 + 4 * (n & 1);
+    koff[n] = R * ROWB + (((ks * 4 + lj) ^ (R % CH)) * 16);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int R = 8 * lj + 4 * hh + (lr >> 2);
+      voff[dt][hh] = TILE_B + R * ROWB + (((2 * dt + ((lr & 3) >> 1)) ^ (R % CH)) * 16) + 8 * (lr & 1);
+    }
+  const bf16x8 ones8 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f),
+                        static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f),
+                        static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+  // Step i on ring stage STG = i % NSTG (a compile-time constant, so every LDS
+  // address is a per-lane base plus an immediate offset).
+  auto step_body = [&](auto stg, int i) {
+    constexpr int STG = decltype(stg)::value;
+    // this wave's loads of step i are done; the barrier makes every wave's
+    // visible and tells that every wave has finished step i-1, whose stage
+    // is refilled next
+    wait_steps(min(NSTG - 2, nsteps - 1 - i));
+    lds_barrier();
+    if (i + NSTG - 1 < nsteps) issue(i + NSTG - 1, (STG + NSTG - 1) % NSTG);
+    if (!active) return;
+    const int base = i * 32;
+    const char* kb = smem + STG * STAGE_B;
+    const uint32_t* mb = reinterpret_cast<const uint32_t*>(kb + 2 * TILE_B);
+    bf16x8 kfr[2 * KS];
+#pragma unroll
+    for (int n = 0; n < 2 * KS; ++n) kfr[n] = *reinterpret_cast<const bf16x8*>(kb + koff[n]);
+    __builtin_amdgcn_s_setprio(1);
+    f32x4 sacc[2][NRT];
+    auto s_tile = [&](auto rtc) {
+      constexpr int rt = decltype(rtc)::value;
+#pragma unroll
+      for (int n = 0; n < 2 * KS; ++n) {
+        sacc[n & 1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            kfr[n], qf[rt][n >> 1], n < 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[n & 1][rt], 0, 0, 0);
+      }
+    };
+    s_tile(std::integral_constant<int, 0>{});
+    // V^T fragments by transpose reads of the token-major V rows (lane (lr,
+    // lj) receives V[8lj + 4h' + k][16dt + lr], k = 0..3)
+    bf16x8 vfr[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      u32x2 half[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        half[hh] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                       (lds_s16x4_t)(kb + voff[dt][hh])));
+      vfr[dt] = __builtin_bit_cast(bf16x8, u32x4{half[0][0], half[0][1], half[1][0], half[1][1]});
+    }
+    bf16x8 pb[NRT];
+    float z[NRT][8];
+    const int valid_e = len - base - 8 * lj;   // tokens of this lane's 8 that exist
+    const bool all_visible = full && valid_e >= 8;
+    auto soft_max = [&](auto rtc) {       // mask, maxima, lazy rescale
+      constexpr int rt = decltype(rtc)::value;
+      const int rl = WROWS * w + rt * 16 + lr;   // row within the block
+      const bool row_ok = rl < nr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[rt][e] = e < 4 ? sacc[0][rt][e] : sacc[1][rt][e - 4];
+      if (!all_visible) {
+        const uint32_t bits = row_ok ? (mb[rl] >> (8 * lj)) & 0xffu : 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[rt][e] = (((bits >> e) & 1u) && e < valid_e) ? z[rt][e] : kNegInf;
+      } else if (!row_ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[rt][e] = kNegInf;
+      }
+      float mx = z[rt][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[rt][e]);
+      m_true[rt] = fmaxf(m_true[rt], mx);
+      const bool high = mx > thr[rt];
+      if (__any(high)) {
+        const float rmx = rowmax4(mx);
+        const bool raise = rmx > thr[rt];
+        const float mn = raise ? rmx : m_run[rt];
+        const float alpha = raise ? fast_exp2((m_run[rt] - mn) * cl2) : 1.f;
+        m_run[rt] = mn;
+        mc[rt] = mn == kNegInf ? 0.f : mn * cl2;
+        thr[rt] = mn + kRescaleSlack / cl2;
+        lacc[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+      }
+    };
+    auto soft_exp = [&](auto rtc) {       // probabilities, bf16 P
+      constexpr int rt = decltype(rtc)::value;
+      f32x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(z[rt][e], cl2, -mc[rt]));   // z = -inf gives 0
+      pb[rt] = __builtin_convertvector(p, bf16x8);
+    };
+    auto pv_tile = [&](auto rtc) {
+      constexpr int rt = decltype(rtc)::value;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[dt], pb[rt], o[dt][rt], 0, 0, 0);
+      }
+      lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pb[rt], lacc[rt], 0, 0, 0);
+    };
+    auto interleave = [] {
+#pragma unroll
+      for (int k = 0; k < DT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    };
+    static_assert(NRT == 2 && 2 * KS == DT, "the schedule is written for two row tiles");
+    soft_max(std::integral_constant<int, 0>{});
+    s_tile(std::integral_constant<int, 1>{});
+    soft_exp(std::integral_constant<int, 0>{});
+    interleave();
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[0])));
+    soft_max(std::integral_constant<int, 1>{});
+    pv_tile(std::integral_constant<int, 0>{});
+    soft_exp(std::integral_constant<int, 1>{});
+    interleave();
+    pv_tile(std::integral_constant<int, 1>{});
+    __builtin_amdgcn_s_setprio(0);
+  };
+  for (int i = 0; i < nsteps; i += NSTG) {
+    step_body(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < nsteps) step_body(std::integral_constant<int, 1>{}, i + 1);
+    if (i + 2 < nsteps) step_body(std::integral_constant<int, 2>{}, i + 2);
+    if (i + 3 < nsteps) step_body(std::integral_constant<int, 3>{}, i + 3);
+  }
+
+  // The wave's rows are final: M = the row's true max, f = exp2((m_run - M)
+  // * scale * log2 e) renormalises l and O to it.  Lane (lr, lj) holds
+  // d = 16 dt + 4 lj .. +3 of row 16 rt + lr.
+  if (active) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int r = WROWS * w + rt * 16 + lr;
+      const float mx = rowmax4(m_true[rt]);
+      const float f = (m_run[rt] == kNegInf) ? 0.f : fast_exp2((m_run[rt] - mx) * cl2);
+      const float ls = f * lacc[rt][0];
+      if (r < nr) {
+        const int row = rb + r;
+        const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
+        if (lj == 0) {
+          a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
+          a.pl[sh] = ls;
+        }
+        if (a.po_bf16) {
+          const float inv = 1.f / lacc[rt][0];    // O / l, independent of the offset
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const f32x4 acc = o[dt][rt];
+            const uint32_t lo = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+            const uint32_t hi = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + sh * D + dt * 16 + lj * 4) = u32x2{lo, hi};
+          }
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<f32x4*>(a.po + sh * D + dt * 16 + lj * 4) = f * o[dt][rt];
+        }
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    int32_t* last_list = reinterpret_cast<int32_t*>(lds + Shape::LIST_OFF);
+    fused_merge_tail<uint16_t, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, last_list + ROWS);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // One launch for all partial work: the plan's wide (128-row) MFMA items take
 // the first n_mfma_wide * Hkv work-groups, the 64-row MFMA items the next
 // n_mfma * Hkv (dispatched first: the longest), the VALU items the rest, so
@@ -1493,22 +1886,28 @@ __global__ __launch_bounds__(512) void partial_attention(PartialArgs a) {
   constexpr int VB = ValuShape<T, D, R>::LDS_B;
   constexpr int MB4 = sizeof(T) == 2 ? MfmaShape<D, 4>::LDS_B : 0;
   constexpr int MB2 = sizeof(T) == 2 ? MfmaShape<D, 2>::LDS_B : 0;
-  constexpr int MB = MB4 > MB2 ? MB4 : MB2;
+  constexpr int MBG = sizeof(T) == 2 ? MfmaGroupShape<D>::LDS_B : 0;
+  constexpr int MB = MB4 > MB2 ? (MB4 > MBG ? MB4 : MBG) : (MB2 > MBG ? MB2 : MBG);
   __shared__ __attribute__((aligned(1024))) char lds[VB > MB ? VB : MB];
+  const int ng = a.plan.n_mfma_group * a.hkv;
   const int nw = a.plan.n_mfma_wide * a.hkv;
   const int nm = a.plan.n_mfma * a.hkv;
   const int b = static_cast<int>(blockIdx.x);
   if constexpr (sizeof(T) == 2) {
-    if (b < nw) {
-      mfma_body<D, FUSED, 2>(a, lds, b, 0);
+    if (b < ng) {
+      mfma_group_body<D, FUSED>(a, lds, b, 0);
       return;
     }
-    if (b < nw + nm) {
-      mfma_body<D, FUSED, 4>(a, lds, b - nw, a.plan.n_mfma_wide);
+    if (b < ng + nw) {
+      mfma_body<D, FUSED, 2>(a, lds, b - ng, a.plan.n_mfma_group);
+      return;
+    }
+    if (b < ng + nw + nm) {
+      mfma_body<D, FUSED, 4>(a, lds, b - ng - nw, a.plan.n_mfma_group + a.plan.n_mfma_wide);
       return;
     }
   }
-  valu_body<T, D, R, FUSED>(a, lds, b - nw - nm);
+  valu_body<T, D, R, FUSED>(a, lds, b - ng - nw - nm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1556,6 +1955,7 @@ static DevPlan make_dev_plan(const deft_plan* p) {
   d.tickets = const_cast<int32_t*>(b) + L.tickets;
   d.merge_slots = b + L.merge_slots;
   d.merge_stride = L.merge_stride;
+  d.n_mfma_group = L.n_mfma_group;
   d.n_mfma_wide = L.n_mfma_wide;
   d.n_mfma = L.n_mfma;
   d.n_valu = L.n_valu;
@@ -1612,9 +2012,9 @@ static int validate_block_table(const deft_plan* p, const deft_attn_desc* d, con
 template <typename T, int D>
 static int launch_partials(const PartialArgs& pa, hipStream_t st) {
   const int hkv = pa.hkv;
-  if (sizeof(T) != 2 && pa.plan.n_mfma + pa.plan.n_mfma_wide > 0)
+  if (sizeof(T) != 2 && pa.plan.n_mfma_group + pa.plan.n_mfma + pa.plan.n_mfma_wide > 0)
     return fail(DEFT_ERR_UNSUPPORTED, "MFMA work for fp32 inputs");
-  const dim3 grid((pa.plan.n_mfma_wide + pa.plan.n_mfma + pa.plan.n_valu) * hkv), block(512);
+  const dim3 grid((pa.plan.n_mfma_group + pa.plan.n_mfma_wide + pa.plan.n_mfma + pa.plan.n_valu) * hkv), block(512);
   if (grid.x == 0) return DEFT_OK;
   // the VALU body's row capacity: 4 when every VALU item fits, else 8
   static_assert(kValuRows == 8, "VALU row capacities are 4 and 8");

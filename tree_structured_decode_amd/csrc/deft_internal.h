@@ -20,6 +20,7 @@ constexpr int kPageSize = 16;
 // the hh-th query head of the KV head being processed (G = Hq / Hkv).
 constexpr int kMfmaRows = 64;      // rows per MFMA work item (4 tiles of 16)
 constexpr int kMfmaWideRows = 128; // rows per wide MFMA work item (groups of more than kMfmaRows rows)
+constexpr int kMfmaGroupRows = 256; // rows per whole-group MFMA work item (no token split)
 constexpr int kMfmaMinRows = 16;   // a chunk needs this many rows to use MFMA
 constexpr int kValuRows = 8;       // rows per VALU work item
 constexpr int64_t kMaxQueryRows = int64_t{1} << 28;       // num_queries * num_q_heads < this
@@ -43,7 +44,7 @@ static_assert(sizeof(WorkItem) == 32, "work items are read as two int4");
 struct ImageLayout {
   size_t chunk_start, group_offsets, chunk_full, slot_query, slot_mask, flat_to_logical,
       query_slot_offsets, query_slots, mfma_items, valu_items, tickets, merge_slots, total_words;
-  int32_t n_mfma_wide, n_mfma, n_valu;   // mfma_items holds the wide items, then the 64-row ones
+  int32_t n_mfma_group, n_mfma_wide, n_mfma, n_valu;   // mfma_items: group, wide, then 64-row items
   // Merge lists at a fixed stride (each query's slots, padded with -1), so
   // the merge reads a query's slot ids without first reading its offsets;
   // 0 when the plan's slot counts are too uneven for that (CSR lists only).

@@ -336,7 +336,7 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   int rc = check_desc(p, d);
   if (rc) return rc;
   const int32_t G = d->num_q_heads / d->num_kv_heads;
-  std::vector<WorkItem> wide, mfma, valu;
+  std::vector<WorkItem> group, wide, mfma, valu;
   // Items of kMfmaWideRows rows (groups of more than kMfmaRows rows) halve
   // the KV traffic of a group, since each chunk is streamed by half as many
   // work-groups, but also halve the number of work-groups: worth it only
@@ -352,24 +352,31 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   const bool wide_on = force && (force[0] == '0' || force[0] == '1')
                            ? force[0] == '1'
                            : n64 * d->num_kv_heads >= 2 * static_cast<int64_t>(device_cu_count());
+  // Whole-group items (up to kMfmaGroupRows rows, no token split): each
+  // chunk enters a compute unit once per KV head for its whole group.
+  // DEFT_MFMA_GROUP=1 or 0 forces them on or off.
+  const char* gforce = std::getenv("DEFT_MFMA_GROUP");
+  const bool group_on = gforce && (gforce[0] == '0' || gforce[0] == '1') ? gforce[0] == '1' : false;
   for (int32_t k = 0; k < p->num_chunks; ++k) {
     const int32_t rows = (p->group_offsets[k + 1] - p->group_offsets[k]) * G;
     if (rows == 0) continue;
     // MFMA when the group fills a tile; the query-centric baseline (groups of
     // one query) takes MFMA for every bf16 group, its faster kernel
     const bool use_mfma = d->dtype == DEFT_DTYPE_BF16 && (rows >= kMfmaMinRows || p->query_centric);
-    const bool use_wide = use_mfma && wide_on && rows > kMfmaRows;
-    const int32_t blk = use_wide ? kMfmaWideRows : use_mfma ? kMfmaRows : kValuRows;
+    const bool use_group = use_mfma && group_on;
+    const bool use_wide = use_mfma && !use_group && wide_on && rows > kMfmaRows;
+    const int32_t blk = use_group ? kMfmaGroupRows : use_wide ? kMfmaWideRows : use_mfma ? kMfmaRows : kValuRows;
     const int32_t cs = p->chunk_start[k], len = p->chunk_start[k + 1] - cs;
     int32_t lstart = p->flat_to_logical[cs];
     for (int32_t t = 1; t < len && lstart >= 0; ++t)
       if (p->flat_to_logical[cs + t] != lstart + t) lstart = -1;
     for (int32_t r = 0; r < rows; r += blk)
-      (use_wide ? wide : use_mfma ? mfma : valu)
+      (use_group ? group : use_wide ? wide : use_mfma ? mfma : valu)
           .push_back({k, r, std::min(blk, rows - r), cs, len, p->group_offsets[k], p->chunk_full[k] ? 1 : 0, lstart});
   }
   // one launch of 512-thread work-groups covers every item for every KV head
-  if (static_cast<int64_t>(wide.size() + mfma.size() + valu.size()) * d->num_kv_heads > kMaxPartialBlocks)
+  if (static_cast<int64_t>(group.size() + wide.size() + mfma.size() + valu.size()) * d->num_kv_heads >
+      kMaxPartialBlocks)
     return fail(DEFT_ERR_UNSUPPORTED,
                 "work items x num_kv_heads above 2^23 - 1, the partial kernel's grid limit (raise chunk_tokens)");
   size_t w = 0;
@@ -383,7 +390,7 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   L->flat_to_logical = take(p->total_tokens);
   L->query_slot_offsets = take(p->num_queries + 1);
   L->query_slots = take(S);
-  L->mfma_items = take(8 * (wide.size() + mfma.size()));
+  L->mfma_items = take(8 * (group.size() + wide.size() + mfma.size()));
   L->valu_items = take(8 * valu.size());
   // fused-merge tickets, one per (query, query head); zero in the uploaded
   // image and reset to zero by the kernels after use
@@ -396,6 +403,7 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   L->merge_stride = (max_slots > 0 && padded <= 4 * static_cast<int64_t>(S) + 4096) ? max_slots : 0;
   L->merge_slots = take(L->merge_stride ? static_cast<size_t>(padded) : 0);
   L->total_words = w;
+  L->n_mfma_group = static_cast<int32_t>(group.size());
   L->n_mfma_wide = static_cast<int32_t>(wide.size());
   L->n_mfma = static_cast<int32_t>(mfma.size());
   L->n_valu = static_cast<int32_t>(valu.size());
@@ -416,8 +424,9 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   std::copy(p->flat_to_logical.begin(), p->flat_to_logical.end(), im + L->flat_to_logical);
   std::copy(p->query_slot_offsets.begin(), p->query_slot_offsets.end(), im + L->query_slot_offsets);
   std::copy(p->query_slots.begin(), p->query_slots.end(), im + L->query_slots);
-  std::memcpy(im + L->mfma_items, wide.data(), sizeof(WorkItem) * wide.size());
-  std::memcpy(im + L->mfma_items + 8 * wide.size(), mfma.data(), sizeof(WorkItem) * mfma.size());
+  std::memcpy(im + L->mfma_items, group.data(), sizeof(WorkItem) * group.size());
+  std::memcpy(im + L->mfma_items + 8 * group.size(), wide.data(), sizeof(WorkItem) * wide.size());
+  std::memcpy(im + L->mfma_items + 8 * (group.size() + wide.size()), mfma.data(), sizeof(WorkItem) * mfma.size());
   std::memcpy(im + L->valu_items, valu.data(), sizeof(WorkItem) * valu.size());
   if (L->merge_stride) {
     int32_t* ms = im + L->merge_slots;
