@@ -14,6 +14,15 @@ copy, and consecutive steps cycle through the copies (and through R copies of
 Q and of the output), so R * KV bytes (>= 512 MB) evicts the 256 MB Infinity
 Cache and the L2s between reuses of a copy.
 
+The chunk size is the library's rule (deft_plan_auto_chunk_tokens) unless
+--chunk-tokens gives one; the workload's hand-tuned size is timed beside it
+when they differ.  Besides the graph-timed steps: per-step latency
+distributions (median, p10, p90) cold (after a 1 GiB write that evicts the
+Infinity Cache and the L2s) and warm; a 1 GiB streaming-read calibration
+(libdeft_bench) giving the achievable HBM bandwidth, the second roofline
+fraction; the oracle on the host cores (all threads, and one thread for the
+three smallest workloads).
+
 Prints ONE JSON line.  `value` is the step latency in microseconds.
 """
 from __future__ import annotations
@@ -69,14 +78,25 @@ def placements(wl, copies, rng):
     return span * copies, [(base + r * span).astype(np.int32) for r in range(copies)]
 
 
-def cpu_baseline(wl, budget_s: float):
+def cpu_baseline(wl, budget_s: float, threads=None):
     """The fp64 oracle on the host cores: whole workload or a query sample,
-    repeated for about `budget_s` seconds; returns per-step microseconds."""
+    repeated for about `budget_s` seconds; returns per-step microseconds.
+    threads=1 limits the BLAS pools to one thread for the run."""
+    import contextlib
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:  # noqa: BLE001
+        threadpool_info = threadpool_limits = None
+    ctx = threadpool_limits(limits=threads) if (threads and threadpool_limits) else contextlib.nullcontext()
+    with ctx:
+        return _cpu_baseline(wl, budget_s, threadpool_info)
+
+
+def _cpu_baseline(wl, budget_s, threadpool_info):
     import numpy as np
     from oracle import attention as OA
     from tree_structured_decode_amd import workloads as W
     try:
-        from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas = 1
@@ -115,10 +135,13 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--chunk-tokens", type=int, default=None)
+    ap.add_argument("--chunk-tokens", type=int, default=0,
+                    help="chunk size; 0 (default) takes the library's rule (deft_plan_auto_chunk_tokens)")
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--dist-iters", type=int, default=100,
+                    help="timed iterations of the per-step latency distributions (cold and warm)")
     ap.add_argument("--profile-run", action="store_true",
                     help="eager steps only (for rocprofv3 kernel traces and counters)")
     ap.add_argument("--profile-graph", action="store_true",
@@ -151,7 +174,15 @@ def main():
     pool_pages = None
     if args.workload == 5:
         pool_pages = W.hbm_pool_pages(torch.cuda.get_device_properties(0).total_memory)
-    wl = W.standard_workload(args.workload, chunk_tokens=args.chunk_tokens, pool_pages=pool_pages)
+    wl = W.standard_workload(args.workload, pool_pages=pool_pages)
+    hand_chunk = wl.chunk_tokens            # the size tuned by hand for this workload
+    if args.chunk_tokens:
+        wl.chunk_tokens, chunk_rule = args.chunk_tokens, "given"
+    else:
+        ad = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+        wl.chunk_tokens = D.deft_plan_auto_chunk_tokens(wl.parents, wl.seg_lens, wl.query_nodes, ad,
+                                                        query_lens=wl.query_lens)
+        chunk_rule = "auto"
     eb = wl.k_tokens.element_size()
     T, hq, hkv, d, nq = wl.total_tokens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_queries
     kv_bytes = T * 2 * hkv * d * eb
@@ -347,6 +378,69 @@ def main():
     _, warm_ms = timed(g_warm)
     copies = copies_saved
     del g_step, g_part, g_merge, g_warm
+
+    # The workload's hand-tuned chunk size, timed the same way, when the
+    # library's rule chose another one.
+    hand_us = None
+    if hand_chunk != wl.chunk_tokens:
+        def hand_plan(p, s_, q_, c_):
+            if wl.query_lens is None:
+                return D.deft_plan_create(p, s_, q_, hand_chunk)
+            return D.deft_plan_create_multi_token(p, s_, q_, wl.query_lens, hand_chunk)
+        hand_us, _, _ = alt_plan_leg(hand_plan)
+
+    # Per-step latency distributions: each step bracketed by events on the
+    # launch stream, eagerly launched behind GPU work that lets the host run
+    # ahead: cold = after a 1 GiB write that evicts the Infinity Cache and the
+    # L2s (and the step cycles through the cold copies), warm = the same copy
+    # every step behind an idle spin.
+    def step_distribution(cold, n_iter, n_warm=10):
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if cold else None
+        pairs = []
+        for i in range(n_warm + n_iter):
+            if cold:
+                flush.fill_(i & 255)
+            else:
+                torch.cuda._sleep(200000)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(i if cold else 0)
+            e1.record()
+            if i >= n_warm:
+                pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+        del flush
+        return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
+                "p90": float(np.percentile(t, 90)), "iters": n_iter}
+
+    lat_cold = step_distribution(True, args.dist_iters)
+    lat_warm = step_distribution(False, args.dist_iters)
+
+    # Achievable HBM read bandwidth on this device: a plain 1 GiB streaming
+    # read (libdeft_bench), median of 10 timed launches.
+    import ctypes
+    blib = ctypes.CDLL(os.path.join(ROOT, "tree_structured_decode_amd", "libdeft_bench.so"))
+    blib.deft_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    blib.deft_bench_stream_read_sink_floats.restype = ctypes.c_size_t
+    cal_bytes = 1 << 30
+    cal_src = torch.ones(cal_bytes // 4, dtype=torch.float32, device=dev)
+    cal_sink = torch.empty(int(blib.deft_bench_stream_read_sink_floats()), dtype=torch.float32, device=dev)
+    cal_stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cal_t = []
+    for i in range(13):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = blib.deft_bench_stream_read(ctypes.c_void_p(cal_src.data_ptr()), cal_bytes,
+                                         ctypes.c_void_p(cal_sink.data_ptr()), cal_stream)
+        e1.record()
+        assert rc == 0, "stream-read calibration launch failed"
+        if i >= 3:
+            cal_t.append((e0, e1))
+    torch.cuda.synchronize()
+    assert abs(float(cal_sink.double().sum()) - cal_bytes // 4) < 1.0, "stream read checksum"
+    cal_gbs = cal_bytes / (float(np.median([a.elapsed_time(b) for a, b in cal_t])) * 1e-3) / 1e9
+    del cal_src, cal_sink
     assert torch.isfinite(outs[0].float()).all(), "non-finite output"
 
     ms_per_step = wall / args.steps * 1e3
@@ -375,6 +469,8 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "kernel": "lse_merge", "algorithmic_bytes_per_launch": part_bytes + q_bytes}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if roof["unit"] == "GB/s":
+        roof["frac_of_achievable"] = roof["achieved"] / cal_gbs
     roof["launch_us_mean"] = mean_part if dominant == "partial" else mean_merge
     roof["traffic"] = None
     counters = os.path.join(ROOT, "profiles", "hbm_counters.json")
@@ -426,6 +522,16 @@ def main():
             "max_abs_diff_vs_deft": nc_err,
         },
         "warm_step_us": warm_ms * 1e3 / args.steps,
+        "chunk_rule": chunk_rule,
+        "hand_picked_chunk_tokens": hand_chunk,
+        "hand_picked_step_us": hand_us,
+        "step_latency_us": {
+            "cold": lat_cold, "warm": lat_warm,
+            "method": ("each step bracketed by HIP events on the launch stream, eager launches; cold: after a "
+                       "1 GiB write evicting the Infinity Cache and the L2s; warm: the same inputs every step"),
+        },
+        "hbm_calibration": {"stream_read_gbs": cal_gbs, "bytes": cal_bytes, "launches": 10,
+                            "kernel": "deft_bench_stream_read (libdeft_bench.so)"},
         "planner_host_us_median": float(np.median(plan_times) * 1e6),
         "plan_upload_us": upload_us,
         "plan_device_bytes": plan_bytes,
@@ -440,6 +546,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        if args.workload in (1, 2, 3):
+            line["cpu_baseline_1thread"] = cpu_baseline(wl, args.cpu_budget * 0.75, threads=1)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -207,6 +207,27 @@ int deft_plan_create_multi_token(const int32_t* parents, const int32_t* seg_lens
                                  const int32_t* query_nodes, const int32_t* query_lens,
                                  int32_t num_queries, int32_t chunk_tokens, deft_plan** out_plan);
 
+/*
+ * Chunk size for deft_plan_create (or deft_plan_create_multi_token, with
+ * query_lens; NULL means whole nodes) chosen by one rule: the smallest
+ * multiple of 32 tokens, up to 4096, for which the partial-attention kernel
+ * of this tree under `desc` has at most `num_cus` work-groups, so every chunk
+ * of every KV head runs in one round on a device of num_cus compute units
+ * (one work-group per compute unit); 4096 when even that needs more rounds
+ * (long chunks then amortise each work-group's fixed cost).  Work-groups are
+ * counted as items of 64 rows for bf16 groups of 16 or more rows and of 8
+ * rows otherwise, times num_kv_heads, from each chunk's group size ("2.
+ * Flattened Tree KV Splitting" cuts the flat token space into equal chunks;
+ * "1. KV-Guided Grouping" gives each chunk one group).  num_cus = 0 takes the
+ * current device's count (256 when it cannot be queried).
+ * *out_chunk_tokens is set on success.  Errors: those of deft_plan_create for
+ * the tree arrays, INVALID_ARGUMENT for a NULL out pointer or num_cus < 0,
+ * and the desc errors of deft_plan_device_bytes.
+ */
+int deft_plan_auto_chunk_tokens(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                                const int32_t* query_nodes, const int32_t* query_lens, int32_t num_queries,
+                                const deft_attn_desc* desc, int32_t num_cus, int32_t* out_chunk_tokens);
+
 /* Free a plan (NULL is ignored); waits for its last upload's copy to have
  * run.  The caller must first let every stream that consumes its device
  * image get past that work (the image is caller memory and stays). */
@@ -295,6 +316,21 @@ int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_
                               const int32_t* block_table, deft_plan* plan, void* out,
                               const deft_attn_desc* desc, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * Whether the attention calls on this plan since the last check ran
+ * correctly.  The matrix-core partial kernels synchronise the waves that
+ * share an LDS ring through flags with a bounded wait (2^20 checks, about
+ * 30 ms; DEFT_SPIN_LIMIT in the environment lowers it, for tests); a wait
+ * that runs out never hangs the GPU but leaves that work-group's results
+ * invalid, and sets a status word in the plan's device image.  This call
+ * copies that word to the host on `stream`, synchronises the stream, and
+ * returns DEFT_ERR_HIP (with a message) if it was set, clearing it; else
+ * DEFT_OK.  INVALID_ARGUMENT if the plan is NULL or has no device image.
+ * It synchronises, so it is meant for periodic checks and tests, not for
+ * every step or for graph capture.
+ */
+int deft_plan_status(deft_plan* plan, void* stream);
 
 /*
  * Size of the device scratch that deft_tree_attention_noalloc uses for the

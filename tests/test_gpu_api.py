@@ -10,7 +10,7 @@ from tree_structured_decode_amd import deft as D
 from tree_structured_decode_amd import workloads as W
 from tree_structured_decode_amd.runner import TreeAttention
 
-from gpu_helpers import DEV, gpu_inputs, say
+from gpu_helpers import DEV, check_close, gpu_inputs, oracle_out, say
 
 pytestmark = pytest.mark.gpu
 
@@ -92,3 +92,32 @@ def test_back_to_back_uploads_keep_each_image():
     from gpu_helpers import check_close, oracle_out, TOL
     check_close(got, oracle_out(wl, queries=sel), TOL[torch.bfloat16], "after back-to-back uploads")
     D.deft_plan_destroy(plan)
+
+
+def test_bounded_wait_give_up_is_reported(monkeypatch):
+    """A partial kernel whose inter-wave waits may make no second check
+    (DEFT_SPIN_LIMIT=0, forced from the host; every kernel still exits)
+    reports through deft_plan_status; the status is cleared by the check,
+    and normal calls leave it clear."""
+    wl = W.standard_workload(2)
+    q, kc, vc, bt = gpu_inputs(wl)
+    desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens, desc, device=DEV)
+    out = torch.empty_like(q)
+    say("spin limit default")
+    ta(q, kc, vc, bt, out)
+    D.deft_plan_status(ta.plan)                 # no give-up
+    say("spin limit 0")
+    monkeypatch.setenv("DEFT_SPIN_LIMIT", "0")
+    for _ in range(3):
+        ta(q, kc, vc, bt, out)
+    with pytest.raises(D.DeftError) as err:
+        D.deft_plan_status(ta.plan)
+    assert err.value.code == D.DEFT_ERR_HIP
+    assert "bounded wait" in str(err.value)
+    D.deft_plan_status(ta.plan)                 # cleared by the check
+    monkeypatch.delenv("DEFT_SPIN_LIMIT")
+    ta(q, kc, vc, bt, out)
+    D.deft_plan_status(ta.plan)
+    got = out.double().cpu().numpy()
+    check_close(got, oracle_out(wl), 2e-2, "after the forced give-up")

@@ -305,3 +305,74 @@ def test_binding_checks_tensor_shapes():
         with pytest.raises(D.DeftError) as e:
             D.deft_lse_merge(plan, desc, po, pm, pm, good["out"], D.DEFT_PARTIAL_BF16_NORM)
         assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT and "part_o" in str(e.value)
+
+
+def _rule_by_brute_force(parents, seg_lens, query_nodes, hq, hkv, bf16, cus, query_lens=None):
+    """The documented chunk-size rule, evaluated by building the reference
+    planner's plan at every candidate size: the smallest multiple of 32 up to
+    4096 whose work-groups (items of 64 rows for bf16 groups of >= 16 rows,
+    8 rows otherwise, times the KV heads) number at most `cus`; else 4096."""
+    g = hq // hkv
+    for c in range(32, 4097, 32):
+        plan = ref_plan(parents, seg_lens, query_nodes, c, query_lens=query_lens)
+        go = plan["group_offsets"].astype(np.int64)
+        rows = (go[1:] - go[:-1]) * g
+        blk = np.where(bf16 & (rows >= 16), 64, 8)
+        if int(np.sum(-(-rows // blk))) * hkv <= cus:
+            return c
+    return 4096
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 6])
+def test_auto_chunk_tokens_matches_the_rule(cfg):
+    wl = W.standard_workload(cfg)
+    bf16 = wl.dtype == torch.bfloat16
+    for cus in (256, 80, 1024):
+        desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+        got = D.deft_plan_auto_chunk_tokens(wl.parents, wl.seg_lens, wl.query_nodes, desc, cus,
+                                            query_lens=wl.query_lens)
+        want = _rule_by_brute_force(wl.parents, wl.seg_lens, wl.query_nodes, wl.num_q_heads, wl.num_kv_heads,
+                                    bf16, cus, query_lens=wl.query_lens)
+        assert got == want, (cfg, cus, got, want)
+
+
+def test_auto_chunk_tokens_known_choices():
+    """On 256 compute units the rule gives 544 for the 4K-prefix tree (eight
+    chunks x four 64-row items x eight KV heads = 256 work-groups; 520 would
+    do too but is not a multiple of 32) and 4096 for the 32K-prefix tree
+    (no size fits one round)."""
+    wl = W.standard_workload(2)
+    desc = D.make_desc(wl.dtype, 32, 8, 128, wl.num_pages)
+    assert D.deft_plan_auto_chunk_tokens(wl.parents, wl.seg_lens, wl.query_nodes, desc, 256) == 544
+    tree, _ = W.medusa_token_tree(np.random.default_rng(0), (8, 4, 2, 2, 1), 256)
+    p, s, qn = W.prefix_plus_token_tree(32768, tree)
+    desc5 = D.make_desc(torch.bfloat16, 64, 8, 128, 1)
+    assert D.deft_plan_auto_chunk_tokens(p, s, qn, desc5, 256) == 4096
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_auto_chunk_tokens_random_trees(seed):
+    rng = np.random.default_rng(9100 + seed)
+    n = int(rng.integers(1, 40))
+    p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([5, 60, 300])), int(rng.integers(1, 30)),
+                             forest_prob=float(rng.choice([0.0, 0.2])))
+    hkv = int(rng.choice([1, 2, 8]))
+    hq = hkv * int(rng.choice([1, 4, 8]))
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    cus = int(rng.choice([4, 32, 256]))
+    desc = D.make_desc(dtype, hq, hkv, 128, 10)
+    got = D.deft_plan_auto_chunk_tokens(p, s, qn, desc, cus)
+    assert got == _rule_by_brute_force(p, s, qn, hq, hkv, dtype == torch.bfloat16, cus)
+
+
+def test_auto_chunk_tokens_errors():
+    desc = D.make_desc(torch.bfloat16, 8, 2, 128, 10)
+    with pytest.raises(D.DeftError) as e:
+        D.deft_plan_auto_chunk_tokens([-1, 5], [3, 3], [0], desc)
+    assert e.value.code == D.DEFT_ERR_INVALID_TREE
+    with pytest.raises(D.DeftError) as e:
+        D.deft_plan_auto_chunk_tokens([-1], [3], [0], D.make_desc(torch.bfloat16, 8, 2, 96, 10))
+    assert e.value.code == D.DEFT_ERR_UNSUPPORTED
+    with pytest.raises(D.DeftError) as e:
+        D.deft_plan_auto_chunk_tokens([-1], [3], [0], desc, num_cus=-1)
+    assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT

@@ -19,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdeft.so")
+SANITIZED_LIB = os.path.join(BUILD, "libdeft_host_sanitized.so")
+BENCH_LIB = os.path.join(PKG, "libdeft_bench.so")
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -54,7 +56,27 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", "--offload-arch=gfx950", att_o, plan_o, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # the streaming-read calibration kernel the benchmark times
+    bench_o = os.path.join(BUILD, "deft_bench.o")
+    _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "deft_bench.hip"), "-o", bench_o], verbose)
+    tmp = BENCH_LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", "--offload-arch=gfx950", bench_o, "-o", tmp], verbose)
+    os.replace(tmp, BENCH_LIB)
     return LIB
+
+
+def build_planner_sanitized(verbose: bool = False) -> str:
+    """The host planner alone (deft_plan.cpp plus host-only stand-ins for the
+    HIP entry points), built with AddressSanitizer and UndefinedBehavior-
+    Sanitizer for the CPU test suite; load it with libasan preloaded."""
+    os.makedirs(BUILD, exist_ok=True)
+    inc = ["-I", INCLUDE, "-I", CSRC]
+    tmp = SANITIZED_LIB + ".tmp"
+    _run(["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+          "-fno-sanitize-recover=undefined", "-fPIC", "-shared", "-Wall", *inc,
+          os.path.join(CSRC, "deft_plan.cpp"), os.path.join(CSRC, "deft_host_only.cpp"), "-o", tmp], verbose)
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
 
 
 if __name__ == "__main__":

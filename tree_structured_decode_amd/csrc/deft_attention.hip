@@ -73,6 +73,7 @@ struct DevPlan {
   const int4* mfma_items;
   const int4* valu_items;
   int32_t* tickets;          // [Nq * Hq], zero between calls (fused merge)
+  int32_t* status;           // 1 once a bounded wait gave up (deft_plan_status reads and clears it)
   const int32_t* merge_slots;   // [Nq][merge_stride] slot ids padded with -1, or unused
   int32_t n_mfma_group, n_mfma_wide, n_mfma, n_valu, mask_words, num_queries, merge_stride;   // mfma_items: group, wide, 64-row
 };
@@ -102,6 +103,7 @@ struct PartialArgs {
   int32_t hq, hkv, grp;
   int32_t po_bf16;   // 1: store O / l rounded to bf16 (internal workspace format)
   float scale_log2;  // log2(e) / sqrt(d)
+  int32_t spin_limit;   // checks of a bounded inter-wave wait before it gives up
   int32_t fused;     // 1: launch the kernels' fused variants (fused_merge_tail)
   int32_t max_valu_rows;   // host only: picks the VALU kernel's row capacity
   MergeArgs merge;   // used when fused
@@ -518,31 +520,42 @@ __device__ inline float rowsum4(float x) {
 
 // Two-wave rendezvous through LDS: publish `i` in *mine, then wait until
 // *theirs reaches `i`.  Both waves of a pair run the same iteration count,
-// so every wait ends; the spin is also bounded so that a broken pairing can
-// only produce wrong values, never a wave that does not finish.
-__device__ inline void pair_sync(int32_t* mine, int32_t* theirs, int32_t i, int lane) {
+// so every wait ends; the spin is also bounded (`spins` checks, the kernel
+// argument spin_limit) so that a broken pairing can never leave a wave that
+// does not finish.  A wait that runs out of checks sets *status (device
+// memory of the plan image) to 1: the work-group's results are then invalid,
+// and deft_plan_status reports it to the host.
+__device__ inline void report_give_up(int32_t* status, int lane) {
+  if (lane == 0) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void pair_sync(int32_t* mine, int32_t* theirs, int32_t i, int lane, int32_t spins,
+                                 int32_t* status) {
   if (lane == 0) __hip_atomic_store(mine, i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  for (int spin = 0; spin < (1 << 20); ++spin) {
-    if (__hip_atomic_load(theirs, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= i) break;
+  for (int spin = 0;; ++spin) {
+    if (__hip_atomic_load(theirs, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= i) return;
+    if (spin >= spins) break;
     __builtin_amdgcn_s_sleep(1);
   }
+  report_give_up(status, lane);
 }
 // The same for N waves: wave `me` publishes `i` in flags[me], then waits
-// until every other flag reaches `i` (bounded like pair_sync).
+// until every other flag reaches `i` (bounded and reported like pair_sync).
 template <int N>
-__device__ inline void group_sync(int32_t* flags, int me, int32_t i, int lane) {
+__device__ inline void group_sync(int32_t* flags, int me, int32_t i, int lane, int32_t spins, int32_t* status) {
   if constexpr (N == 2) {
-    pair_sync(&flags[me], &flags[me ^ 1], i, lane);
+    pair_sync(&flags[me], &flags[me ^ 1], i, lane, spins, status);
   } else {
     if (lane == 0) __hip_atomic_store(&flags[me], i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    for (int spin = 0; spin < (1 << 20); ++spin) {
+    for (int spin = 0;; ++spin) {
       bool done = true;
 #pragma unroll
       for (int k = 0; k < N; ++k)
         if (k != me) done &= __hip_atomic_load(&flags[k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= i;
-      if (done) break;
+      if (done) return;
+      if (spin >= spins) break;
       __builtin_amdgcn_s_sleep(1);
     }
+    report_give_up(status, lane);
   }
 }
 
@@ -1206,7 +1219,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     // have finished iteration i-1", then waits for the others to say the
     // same, after which the other stage can be refilled with step i+1.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    group_sync<NGRP>(grp_ready[sp], gr, i, lane);
+    group_sync<NGRP>(grp_ready[sp], gr, i, lane, a.spin_limit, P.status);
     if (step >= nsteps) return;
     const bool next = step + NSPLIT < nsteps;
     const int base = step * 32;
@@ -1280,8 +1293,13 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
       for (int e = 0; e < 8; ++e) z[rt][e] = e < 4 ? sacc[0][rt][e] : sacc[1][rt][e - 4];
       if (!all_visible) {
         const uint32_t bits = row_ok ? (mb[rl] >> (8 * lj)) & 0xffu : 0u;
+        // a step of a partly masked chunk whose tokens every row of the tile
+        // sees (the prefix part of a chunk that also holds tree tokens) needs
+        // no selects
+        if (!__all(bits == 0xffu && valid_e >= 8)) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) z[rt][e] = (((bits >> e) & 1u) && e < valid_e) ? z[rt][e] : kNegInf;
+          for (int e = 0; e < 8; ++e) z[rt][e] = (((bits >> e) & 1u) && e < valid_e) ? z[rt][e] : kNegInf;
+        }
       } else if (!row_ok) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[rt][e] = kNegInf;
@@ -1369,7 +1387,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     }
   }
   if constexpr (NSPLIT == 4) {
-    group_sync<NGRP>(grp_ready[sp], gr, iters, lane);   // the split is past its last step
+    group_sync<NGRP>(grp_ready[sp], gr, iters, lane, a.spin_limit, P.status);   // the split is past its last step
     {
       f32x4* mine = reinterpret_cast<f32x4*>(smem + sp * 2 * STAGE_B + gr * RED_W);
 #pragma unroll
@@ -1429,7 +1447,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
       return reinterpret_cast<f32x4*>(smem + (grp < 2 ? Shape::QOFF + grp * RED_W : 2 * STAGE_B + (grp - 2) * RED_W));
     };
     if (sp == 1) {
-      group_sync<NGRP>(grp_ready[1], gr, iters, lane);
+      group_sync<NGRP>(grp_ready[1], gr, iters, lane, a.spin_limit, P.status);
       f32x4* mine = red_of(gr);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -1765,8 +1783,13 @@ __device__ __forceinline__ void mfma_group_body(const PartialArgs& a, char* lds,
       for (int e = 0; e < 8; ++e) z[rt][e] = e < 4 ? sacc[0][rt][e] : sacc[1][rt][e - 4];
       if (!all_visible) {
         const uint32_t bits = row_ok ? (mb[rl] >> (8 * lj)) & 0xffu : 0u;
+        // a step of a partly masked chunk whose tokens every row of the tile
+        // sees (the prefix part of a chunk that also holds tree tokens) needs
+        // no selects
+        if (!__all(bits == 0xffu && valid_e >= 8)) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) z[rt][e] = (((bits >> e) & 1u) && e < valid_e) ? z[rt][e] : kNegInf;
+          for (int e = 0; e < 8; ++e) z[rt][e] = (((bits >> e) & 1u) && e < valid_e) ? z[rt][e] : kNegInf;
+        }
       } else if (!row_ok) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[rt][e] = kNegInf;
@@ -1953,6 +1976,7 @@ static DevPlan make_dev_plan(const deft_plan* p) {
   d.mfma_items = reinterpret_cast<const int4*>(b + L.mfma_items);
   d.valu_items = reinterpret_cast<const int4*>(b + L.valu_items);
   d.tickets = const_cast<int32_t*>(b) + L.tickets;
+  d.status = const_cast<int32_t*>(b) + L.status;
   d.merge_slots = b + L.merge_slots;
   d.merge_stride = L.merge_stride;
   d.n_mfma_group = L.n_mfma_group;
@@ -1962,6 +1986,20 @@ static DevPlan make_dev_plan(const deft_plan* p) {
   d.mask_words = p->mask_words;
   d.num_queries = p->num_queries;
   return d;
+}
+
+// Checks a bounded inter-wave wait makes before it gives up: 2^20 (each
+// check sleeps ~64 cycles, so about 30 ms), or DEFT_SPIN_LIMIT from the
+// environment when it lies in [0, 2^20] (tests force a give-up with a tiny
+// limit).
+static int32_t spin_limit() {
+  constexpr long kDefault = 1L << 20;
+  const char* env = std::getenv("DEFT_SPIN_LIMIT");
+  if (env && env[0]) {
+    const long v = std::strtol(env, nullptr, 10);
+    if (v >= 0 && v <= kDefault) return static_cast<int32_t>(v);
+  }
+  return static_cast<int32_t>(kDefault);
 }
 
 static int hip_check(hipError_t e, const char* what) {
@@ -2048,6 +2086,7 @@ static int run_partials(const void* q, const void* k, const void* v, const int32
   pa.grp = d->num_q_heads / d->num_kv_heads;
   pa.po_bf16 = po_bf16 ? 1 : 0;
   pa.scale_log2 = kLog2e / std::sqrt(static_cast<float>(d->head_dim));
+  pa.spin_limit = spin_limit();
   pa.fused = fused_out != nullptr;
   pa.max_valu_rows = p->layout.max_valu_rows;
   pa.merge.po = po;
@@ -2249,6 +2288,29 @@ int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_
   // (query, head) row merges it (fused_merge_tail).
   return deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, po, pm, pl, po_bf16,
                             static_cast<hipStream_t>(stream), out);
+}
+
+int deft_plan_status(deft_plan* plan, void* stream) {
+  if (!plan) return fail(DEFT_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!plan->uploaded) return fail(DEFT_ERR_INVALID_ARGUMENT, "plan has no device image: call deft_plan_upload");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* word = static_cast<int32_t*>(plan->dev) + plan->layout.status;
+  int32_t flag = 0;
+  int rc = deft::hip_check(hipMemcpyAsync(&flag, word, sizeof(flag), hipMemcpyDeviceToHost, st),
+                           "copy of the plan's status word");
+  if (rc) return rc;
+  rc = deft::hip_check(hipStreamSynchronize(st), "hipStreamSynchronize for the status word");
+  if (rc) return rc;
+  if (flag == 0) return DEFT_OK;
+  const int32_t zero = 0;
+  rc = deft::hip_check(hipMemcpyAsync(word, &zero, sizeof(zero), hipMemcpyHostToDevice, st),
+                       "reset of the plan's status word");
+  if (rc) return rc;
+  rc = deft::hip_check(hipStreamSynchronize(st), "hipStreamSynchronize after the status reset");
+  if (rc) return rc;
+  return fail(DEFT_ERR_HIP, "a partial-attention work-group ran out of its bounded wait for a partner wave "
+                            "(DEFT_SPIN_LIMIT checks); the outputs of the attention calls on this plan since "
+                            "the last status check are not valid");
 }
 
 int deft_tree_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,

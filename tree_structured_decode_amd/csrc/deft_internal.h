@@ -43,7 +43,7 @@ static_assert(sizeof(WorkItem) == 32, "work items are read as two int4");
 // Offsets (in 4-byte words) of each array inside the device image.
 struct ImageLayout {
   size_t chunk_start, group_offsets, chunk_full, slot_query, slot_mask, flat_to_logical,
-      query_slot_offsets, query_slots, mfma_items, valu_items, tickets, merge_slots, total_words;
+      query_slot_offsets, query_slots, mfma_items, valu_items, tickets, status, merge_slots, total_words;
   int32_t n_mfma_group, n_mfma_wide, n_mfma, n_valu;   // mfma_items: group, wide, then 64-row items
   // Merge lists at a fixed stride (each query's slots, padded with -1), so
   // the merge reads a query's slot ids without first reading its offsets;

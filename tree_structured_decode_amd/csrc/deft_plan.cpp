@@ -40,6 +40,66 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
+// Depth-first pre-order of the nodes (roots, then each node's children, in
+// ascending id) and the flat index of each node's first token.
+static void flatten(const int32_t* parents, const int32_t* seg_lens, int32_t n, std::vector<int32_t>* order,
+                    std::vector<int32_t>* flat_start) {
+  // Children in CSR form; filling in ascending i keeps each list ascending.
+  std::vector<int32_t> child_off(n + 1, 0), child(n), roots;
+  for (int32_t i = 0; i < n; ++i) {
+    if (parents[i] < 0) roots.push_back(i); else child_off[parents[i] + 1]++;
+  }
+  for (int32_t i = 0; i < n; ++i) child_off[i + 1] += child_off[i];
+  {
+    std::vector<int32_t> fill(child_off.begin(), child_off.end() - 1);
+    for (int32_t i = 0; i < n; ++i)
+      if (parents[i] >= 0) child[fill[parents[i]]++] = i;
+  }
+  // Explicit stack (push in reverse to pop ascending).
+  order->clear();
+  order->reserve(n);
+  std::vector<int32_t> stack(roots.rbegin(), roots.rend());
+  while (!stack.empty()) {
+    int32_t x = stack.back();
+    stack.pop_back();
+    order->push_back(x);
+    for (int32_t k = child_off[x + 1] - 1; k >= child_off[x]; --k) stack.push_back(child[k]);
+  }
+  flat_start->resize(n);
+  int64_t f = 0;
+  for (int32_t x : *order) {
+    (*flat_start)[x] = static_cast<int32_t>(f);
+    f += seg_lens[x];
+  }
+}
+
+// The tree encoding's checks shared by every entry point that takes a tree.
+static int validate_tree(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                         const int32_t* query_nodes, int32_t num_queries, const int32_t* query_lens) {
+  if (num_nodes < 1 || num_queries < 1)
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "need at least one node and one query");
+  if (!parents || !seg_lens || !query_nodes)
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "tree arrays must not be NULL");
+  for (int32_t i = 0; i < num_nodes; ++i) {
+    if (parents[i] < -1 || parents[i] >= i)
+      return fail(DEFT_ERR_INVALID_TREE,
+                  "parents[" + std::to_string(i) + "] must be -1 or in [0, " + std::to_string(i) + ")");
+    if (seg_lens[i] < 1)
+      return fail(DEFT_ERR_INVALID_TREE, "seg_lens[" + std::to_string(i) + "] must be >= 1");
+  }
+  for (int32_t q = 0; q < num_queries; ++q)
+    if (query_nodes[q] < 0 || query_nodes[q] >= num_nodes)
+      return fail(DEFT_ERR_INVALID_TREE, "query_nodes[" + std::to_string(q) + "] out of range");
+  if (query_lens)
+    for (int32_t q = 0; q < num_queries; ++q)
+      if (query_lens[q] < 1 || query_lens[q] > seg_lens[query_nodes[q]])
+        return fail(DEFT_ERR_INVALID_TREE, "query_lens[" + std::to_string(q) + "] must be in [1, seg_lens[node]]");
+  int64_t total = 0;
+  for (int32_t i = 0; i < num_nodes; ++i) total += seg_lens[i];
+  if (total > INT32_MAX) return fail(DEFT_ERR_INVALID_TREE, "total tokens exceed 2^31 - 1");
+  return DEFT_OK;
+}
+
 // query_lens (may be null): leading tokens of its own node each query sees.
 static int build_plan(deft_plan* p, const int32_t* parents, const int32_t* seg_lens,
                       int32_t n, const int32_t* query_nodes, int32_t nq, int32_t c,
@@ -53,36 +113,10 @@ static int build_plan(deft_plan* p, const int32_t* parents, const int32_t* seg_l
   }
   const int32_t total = static_cast<int32_t>(run);
 
-  // Children in CSR form; filling in ascending i keeps each list ascending.
-  std::vector<int32_t> child_off(n + 1, 0), child(n), roots;
-  for (int32_t i = 0; i < n; ++i) {
-    if (parents[i] < 0) roots.push_back(i); else child_off[parents[i] + 1]++;
-  }
-  for (int32_t i = 0; i < n; ++i) child_off[i + 1] += child_off[i];
-  {
-    std::vector<int32_t> fill(child_off.begin(), child_off.end() - 1);
-    for (int32_t i = 0; i < n; ++i)
-      if (parents[i] >= 0) child[fill[parents[i]]++] = i;
-  }
-
-  // Depth-first pre-order with an explicit stack (push in reverse to pop ascending).
-  p->flat_node_order.clear();
-  p->flat_node_order.reserve(n);
-  std::vector<int32_t> stack(roots.rbegin(), roots.rend());
-  while (!stack.empty()) {
-    int32_t x = stack.back();
-    stack.pop_back();
-    p->flat_node_order.push_back(x);
-    for (int32_t k = child_off[x + 1] - 1; k >= child_off[x]; --k) stack.push_back(child[k]);
-  }
-  p->node_flat_start.resize(n);
+  flatten(parents, seg_lens, n, &p->flat_node_order, &p->node_flat_start);
   p->flat_to_logical.resize(total);
-  int32_t f = 0;
-  for (int32_t x : p->flat_node_order) {
-    p->node_flat_start[x] = f;
-    for (int32_t i = 0; i < seg_lens[x]; ++i) p->flat_to_logical[f + i] = p->node_start[x] + i;
-    f += seg_lens[x];
-  }
+  for (int32_t x : p->flat_node_order)
+    for (int32_t i = 0; i < seg_lens[x]; ++i) p->flat_to_logical[p->node_flat_start[x] + i] = p->node_start[x] + i;
 
   // Equal chunks from flat index 0.
   const int32_t nc = static_cast<int32_t>((static_cast<int64_t>(total) + c - 1) / c);
@@ -331,41 +365,68 @@ size_t workspace_bytes_for(const deft_plan* p, const deft_attn_desc* d) {
   return 4 * (align_words(partial_o_words(p, d)) + 2 * align_words(sh));
 }
 
+// Which work items a chunk's group of `rows` (slot, query head) rows takes.
+// MFMA when the group fills a tile (the query-centric baseline, groups of one
+// query, takes MFMA for every bf16 group, its faster kernel).  Items of
+// kMfmaWideRows rows (groups of more than kMfmaRows rows) halve the KV
+// traffic of a group, since each chunk is streamed by half as many
+// work-groups, but also halve the number of work-groups: worth it only when
+// the 64-row items would fill the device at least twice over.  Whole-group
+// items (kMfmaGroupRows, no token split) are taken only on request.
+// DEFT_MFMA_WIDE / DEFT_MFMA_GROUP = 1 or 0 in the environment force either
+// choice (tests).
+struct ItemPolicy {
+  bool bf16, query_centric, wide_on, group_on;
+  bool mfma(int32_t rows) const { return bf16 && (rows >= kMfmaMinRows || query_centric); }
+  int32_t block(int32_t rows) const {
+    if (!mfma(rows)) return kValuRows;
+    if (group_on) return kMfmaGroupRows;
+    if (wide_on && rows > kMfmaRows) return kMfmaWideRows;
+    return kMfmaRows;
+  }
+};
+
+static ItemPolicy item_policy(const std::vector<int32_t>& chunk_rows, const deft_attn_desc* d, bool query_centric,
+                              int cus) {
+  ItemPolicy pol{d->dtype == DEFT_DTYPE_BF16, query_centric, false, false};
+  int64_t n64 = 0;
+  for (int32_t rows : chunk_rows) {
+    const int32_t b = pol.mfma(rows) ? kMfmaRows : kValuRows;
+    n64 += (rows + b - 1) / b;
+  }
+  const char* force = std::getenv("DEFT_MFMA_WIDE");
+  pol.wide_on = force && (force[0] == '0' || force[0] == '1') ? force[0] == '1'
+                                                              : n64 * d->num_kv_heads >= 2 * static_cast<int64_t>(cus);
+  const char* gforce = std::getenv("DEFT_MFMA_GROUP");
+  pol.group_on = gforce && (gforce[0] == '0' || gforce[0] == '1') ? gforce[0] == '1' : false;
+  return pol;
+}
+
+// Partial-kernel work-groups for chunks with these group row counts.
+static int64_t work_groups(const std::vector<int32_t>& chunk_rows, const ItemPolicy& pol, int32_t hkv) {
+  int64_t items = 0;
+  for (int32_t rows : chunk_rows) {
+    const int32_t b = pol.block(rows);
+    items += (rows + b - 1) / b;
+  }
+  return items * hkv;
+}
+
 int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* image,
                 ImageLayout* L) {
   int rc = check_desc(p, d);
   if (rc) return rc;
   const int32_t G = d->num_q_heads / d->num_kv_heads;
   std::vector<WorkItem> group, wide, mfma, valu;
-  // Items of kMfmaWideRows rows (groups of more than kMfmaRows rows) halve
-  // the KV traffic of a group, since each chunk is streamed by half as many
-  // work-groups, but also halve the number of work-groups: worth it only
-  // when the 64-row items would fill the device at least twice over.
-  int64_t n64 = 0;
-  for (int32_t k = 0; k < p->num_chunks; ++k) {
-    const int32_t rows = (p->group_offsets[k + 1] - p->group_offsets[k]) * G;
-    const bool m = d->dtype == DEFT_DTYPE_BF16 && (rows >= kMfmaMinRows || p->query_centric);
-    n64 += (rows + (m ? kMfmaRows : kValuRows) - 1) / (m ? kMfmaRows : kValuRows);
-  }
-  // (DEFT_MFMA_WIDE=1 or 0 in the environment forces the choice, for tests.)
-  const char* force = std::getenv("DEFT_MFMA_WIDE");
-  const bool wide_on = force && (force[0] == '0' || force[0] == '1')
-                           ? force[0] == '1'
-                           : n64 * d->num_kv_heads >= 2 * static_cast<int64_t>(device_cu_count());
-  // Whole-group items (up to kMfmaGroupRows rows, no token split): each
-  // chunk enters a compute unit once per KV head for its whole group.
-  // DEFT_MFMA_GROUP=1 or 0 forces them on or off.
-  const char* gforce = std::getenv("DEFT_MFMA_GROUP");
-  const bool group_on = gforce && (gforce[0] == '0' || gforce[0] == '1') ? gforce[0] == '1' : false;
+  std::vector<int32_t> chunk_rows(p->num_chunks);
+  for (int32_t k = 0; k < p->num_chunks; ++k) chunk_rows[k] = (p->group_offsets[k + 1] - p->group_offsets[k]) * G;
+  const ItemPolicy pol = item_policy(chunk_rows, d, p->query_centric, device_cu_count());
   for (int32_t k = 0; k < p->num_chunks; ++k) {
     const int32_t rows = (p->group_offsets[k + 1] - p->group_offsets[k]) * G;
     if (rows == 0) continue;
-    // MFMA when the group fills a tile; the query-centric baseline (groups of
-    // one query) takes MFMA for every bf16 group, its faster kernel
-    const bool use_mfma = d->dtype == DEFT_DTYPE_BF16 && (rows >= kMfmaMinRows || p->query_centric);
-    const bool use_group = use_mfma && group_on;
-    const bool use_wide = use_mfma && !use_group && wide_on && rows > kMfmaRows;
-    const int32_t blk = use_group ? kMfmaGroupRows : use_wide ? kMfmaWideRows : use_mfma ? kMfmaRows : kValuRows;
+    const bool use_mfma = pol.mfma(rows);
+    const int32_t blk = pol.block(rows);
+    const bool use_group = blk == kMfmaGroupRows, use_wide = blk == kMfmaWideRows;
     const int32_t cs = p->chunk_start[k], len = p->chunk_start[k + 1] - cs;
     int32_t lstart = p->flat_to_logical[cs];
     for (int32_t t = 1; t < len && lstart >= 0; ++t)
@@ -395,6 +456,9 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   // fused-merge tickets, one per (query, query head); zero in the uploaded
   // image and reset to zero by the kernels after use
   L->tickets = take(static_cast<size_t>(p->num_queries) * d->num_q_heads);
+  // status word: 1 once a kernel's bounded inter-wave wait gave up (zero in
+  // the uploaded image; deft_plan_status reads and clears it)
+  L->status = take(1);
   // fixed-stride merge lists when padding costs at most about 4x the slots
   int32_t max_slots = 0;
   for (int32_t q = 0; q < p->num_queries; ++q)
@@ -440,6 +504,59 @@ int build_image(deft_plan* p, const deft_attn_desc* d, std::vector<int32_t>* ima
   return DEFT_OK;
 }
 
+// Chunk-size rule: the smallest multiple of kAutoChunkStep tokens (up to
+// kMaxChunkTokens) whose partial-kernel work-groups number at most `cus` (one
+// round on the device), counting items of kMfmaRows rows for matrix-core
+// groups and kValuRows rows otherwise; kMaxChunkTokens when none does.  (The
+// wider items halve a chunk's work-groups but are taken for workloads that
+// run several rounds anyway; a one-round size found by counting them gives
+// more, shorter chunks, so more merge operands per query, and measured
+// slower.)  A chunk's group size is counted from each
+// query's visible flat intervals (its path's segments, in pre-order), as the
+// planner's first pass does, without building the plan.
+constexpr int32_t kAutoChunkStep = 32;
+
+static int32_t auto_chunk_tokens(const int32_t* parents, const int32_t* seg_lens, int32_t n,
+                                 const int32_t* query_nodes, const int32_t* query_lens, int32_t nq,
+                                 const deft_attn_desc* d, int cus) {
+  std::vector<int32_t> order, fstart;
+  flatten(parents, seg_lens, n, &order, &fstart);
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) total += seg_lens[i];
+  std::vector<int64_t> ia, ib;
+  std::vector<int32_t> qoff(nq + 1, 0), path;
+  for (int32_t q = 0; q < nq; ++q) {
+    path.clear();
+    for (int32_t x = query_nodes[q]; x >= 0; x = parents[x]) path.push_back(x);
+    for (auto it = path.rbegin(); it != path.rend(); ++it) {
+      const int64_t a = fstart[*it];
+      ia.push_back(a);
+      ib.push_back(a + (query_lens && *it == query_nodes[q] ? query_lens[q] : seg_lens[*it]));
+    }
+    qoff[q + 1] = static_cast<int32_t>(ia.size());
+  }
+  const int32_t G = d->num_q_heads / d->num_kv_heads;
+  std::vector<int32_t> rows;
+  for (int32_t c = kAutoChunkStep; c <= kMaxChunkTokens; c += kAutoChunkStep) {
+    const int64_t nc = (total + c - 1) / c;
+    rows.assign(static_cast<size_t>(nc), 0);
+    for (int32_t q = 0; q < nq; ++q) {
+      int64_t last = -1;
+      for (int32_t t = qoff[q]; t < qoff[q + 1]; ++t)
+        for (int64_t k = ia[t] / c; k <= (ib[t] - 1) / c; ++k)
+          if (k != last) {
+            rows[k] += G;
+            last = k;
+          }
+    }
+    ItemPolicy pol = item_policy(rows, d, false, cus);
+    pol.wide_on = false;     // a one-round size is counted in 64-row items
+    pol.group_on = false;
+    if (work_groups(rows, pol, d->num_kv_heads) <= cus) return c;
+  }
+  return kMaxChunkTokens;
+}
+
 }  // namespace deft
 
 using deft::fail;
@@ -455,30 +572,10 @@ static int plan_create(const int32_t* parents, const int32_t* seg_lens, int32_t 
   if (!out_plan) return fail(DEFT_ERR_INVALID_ARGUMENT, "out_plan is NULL");
   *out_plan = nullptr;
   if (chunk_tokens < 1) return fail(DEFT_ERR_INVALID_ARGUMENT, "chunk_tokens must be >= 1");
-  if (num_nodes < 1 || num_queries < 1)
-    return fail(DEFT_ERR_INVALID_ARGUMENT, "need at least one node and one query");
-  if (!parents || !seg_lens || !query_nodes)
-    return fail(DEFT_ERR_INVALID_ARGUMENT, "tree arrays must not be NULL");
-  for (int32_t i = 0; i < num_nodes; ++i) {
-    if (parents[i] < -1 || parents[i] >= i)
-      return fail(DEFT_ERR_INVALID_TREE,
-                  "parents[" + std::to_string(i) + "] must be -1 or in [0, " + std::to_string(i) + ")");
-    if (seg_lens[i] < 1)
-      return fail(DEFT_ERR_INVALID_TREE, "seg_lens[" + std::to_string(i) + "] must be >= 1");
-  }
-  for (int32_t q = 0; q < num_queries; ++q)
-    if (query_nodes[q] < 0 || query_nodes[q] >= num_nodes)
-      return fail(DEFT_ERR_INVALID_TREE, "query_nodes[" + std::to_string(q) + "] out of range");
-  if (query_lens)
-    for (int32_t q = 0; q < num_queries; ++q)
-      if (query_lens[q] < 1 || query_lens[q] > seg_lens[query_nodes[q]])
-        return fail(DEFT_ERR_INVALID_TREE, "query_lens[" + std::to_string(q) + "] must be in [1, seg_lens[node]]");
-  int64_t total = 0;
-  for (int32_t i = 0; i < num_nodes; ++i) total += seg_lens[i];
-  if (total > INT32_MAX) return fail(DEFT_ERR_INVALID_TREE, "total tokens exceed 2^31 - 1");
+  int rc = deft::validate_tree(parents, seg_lens, num_nodes, query_nodes, num_queries, query_lens);
+  if (rc) return rc;
   deft_plan* p = new (std::nothrow) deft_plan();
   if (!p) return fail(DEFT_ERR_NO_MEMORY, "host allocation failed");
-  int rc;
   try {
     if (kind == PlanKind::kQueryCentric)
       rc = deft::build_query_centric(p, parents, seg_lens, num_nodes, query_nodes, num_queries, chunk_tokens);
@@ -563,6 +660,25 @@ int deft_plan_device_bytes(deft_plan* p, const deft_attn_desc* d, size_t* plan_b
   if (rc) return rc;
   if (plan_bytes) *plan_bytes = 4 * L.total_words;
   if (workspace_bytes) *workspace_bytes = deft::workspace_bytes_for(p, d);
+  return DEFT_OK;
+}
+
+int deft_plan_auto_chunk_tokens(const int32_t* parents, const int32_t* seg_lens, int32_t num_nodes,
+                                const int32_t* query_nodes, const int32_t* query_lens, int32_t num_queries,
+                                const deft_attn_desc* desc, int32_t num_cus, int32_t* out_chunk_tokens) {
+  deft::set_error("");
+  if (!out_chunk_tokens) return fail(DEFT_ERR_INVALID_ARGUMENT, "out_chunk_tokens is NULL");
+  if (num_cus < 0) return fail(DEFT_ERR_INVALID_ARGUMENT, "num_cus must be >= 0");
+  int rc = deft::validate_tree(parents, seg_lens, num_nodes, query_nodes, num_queries, query_lens);
+  if (rc) return rc;
+  rc = deft::check_desc(nullptr, desc);
+  if (rc) return rc;
+  try {
+    *out_chunk_tokens = deft::auto_chunk_tokens(parents, seg_lens, num_nodes, query_nodes, query_lens, num_queries,
+                                                desc, num_cus > 0 ? num_cus : deft::device_cu_count());
+  } catch (const std::bad_alloc&) {
+    return fail(DEFT_ERR_NO_MEMORY, "host allocation failed while choosing the chunk size");
+  }
   return DEFT_OK;
 }
 

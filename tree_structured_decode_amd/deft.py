@@ -21,7 +21,10 @@ from typing import Optional
 import numpy as np
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdeft.so")
+# DEFT_LIB_PATH names another build of the library (the host-only sanitizer
+# build of the planner, in the CPU tests).
+LIB_PATH = os.environ.get("DEFT_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libdeft.so")
 
 DEFT_OK = 0
 DEFT_ERR_INVALID_ARGUMENT = -1
@@ -38,7 +41,8 @@ EXPORTED_SYMBOLS = (
     "deft_plan_create", "deft_plan_create_query_centric", "deft_plan_create_node_chunks",
     "deft_plan_create_multi_token", "deft_plan_destroy", "deft_plan_export", "deft_plan_device_bytes",
     "deft_plan_upload", "deft_tree_attention", "deft_tree_attention_fused", "deft_partial_attention",
-    "deft_lse_merge", "deft_last_error", "deft_tree_attention_noalloc",
+    "deft_lse_merge", "deft_last_error", "deft_tree_attention_noalloc", "deft_plan_status",
+    "deft_plan_auto_chunk_tokens",
 )
 DEFT_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -98,6 +102,9 @@ def lib() -> ctypes.CDLL:
                                       _P, ctypes.c_size_t, _P]
     L.deft_tree_attention_fused.argtypes = L.deft_tree_attention.argtypes
     L.deft_tree_attention_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.POINTER(deft_attn_desc), _P]
+    L.deft_plan_status.argtypes = [_P, _P]
+    L.deft_plan_auto_chunk_tokens.argtypes = [_I32P, _I32P, ctypes.c_int32, _I32P, _I32P, ctypes.c_int32,
+                                              ctypes.POINTER(deft_attn_desc), ctypes.c_int32, _I32P]
     L.deft_partial_attention.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(deft_attn_desc),
                                          _P, _P, _P, ctypes.c_int32, _P]
     L.deft_lse_merge.argtypes = [_P, ctypes.POINTER(deft_attn_desc), _P, _P, _P, ctypes.c_int32,
@@ -107,7 +114,8 @@ def lib() -> ctypes.CDLL:
                  "deft_plan_create_multi_token", "deft_plan_export",
                  "deft_plan_device_bytes", "deft_plan_upload",
                  "deft_tree_attention", "deft_tree_attention_fused", "deft_tree_attention_noalloc",
-                 "deft_partial_attention", "deft_lse_merge"):
+                 "deft_partial_attention", "deft_lse_merge", "deft_plan_status",
+                 "deft_plan_auto_chunk_tokens"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -198,6 +206,20 @@ def deft_plan_create_multi_token(parents, seg_lens, query_nodes, query_lens, chu
     return Plan(h, int(s.sum(dtype=np.int64)))
 
 
+def deft_plan_auto_chunk_tokens(parents, seg_lens, query_nodes, desc, num_cus: int = 0,
+                                query_lens=None) -> int:
+    """The library's chunk size for this tree and attention shape (see deft.h)."""
+    p, s, q = _i32(parents), _i32(seg_lens), _i32(query_nodes)
+    ql = None if query_lens is None else _i32(query_lens)
+    if ql is not None and ql.shape[0] != q.shape[0]:
+        raise ValueError("query_lens needs one entry per query")
+    out = ctypes.c_int32()
+    _check(lib().deft_plan_auto_chunk_tokens(_ptr_i32(p), _ptr_i32(s), int(p.shape[0]), _ptr_i32(q),
+                                             None if ql is None else _ptr_i32(ql), int(q.shape[0]),
+                                             ctypes.byref(desc), int(num_cus), ctypes.byref(out)))
+    return int(out.value)
+
+
 def deft_plan_destroy(plan: Plan):
     if plan.handle:
         lib().deft_plan_destroy(plan.handle)
@@ -248,6 +270,12 @@ def deft_plan_upload(plan: Plan, desc: deft_attn_desc, dev_plan: torch.Tensor, s
     _check(lib().deft_plan_upload(plan.handle, ctypes.byref(desc), _dev(dev_plan),
                                   dev_plan.numel() * dev_plan.element_size(), _stream(stream)))
     plan.dev_plan = dev_plan          # keep the device image alive with the plan
+
+
+def deft_plan_status(plan: Plan, stream=None):
+    """Raises DeftError(DEFT_ERR_HIP) if a kernel's bounded wait gave up since
+    the last check (synchronises the stream)."""
+    _check(lib().deft_plan_status(plan.handle, _stream(stream)))
 
 
 _DTYPES = {DEFT_DTYPE_F32: torch.float32, DEFT_DTYPE_BF16: torch.bfloat16}

@@ -15,12 +15,20 @@ class TreeAttention:
 
     desc: a deft_attn_desc (see deft.make_desc).  Device buffers are torch
     tensors on `device`; the plan image is uploaded on `stream`.
+    chunk_tokens 0 takes the library's rule (deft_plan_auto_chunk_tokens) for
+    the tree plan; the chosen size is kept in self.chunk_tokens.
     """
 
     def __init__(self, parents, seg_lens, query_nodes, chunk_tokens: int, desc, device="cuda",
                  stream=None, query_centric: bool = False, node_chunks: bool = False,
                  query_lens=None):
         self.desc = desc
+        if chunk_tokens == 0:
+            if query_centric or node_chunks:
+                raise ValueError("the chunk-size rule is for the tree plan")
+            chunk_tokens = D.deft_plan_auto_chunk_tokens(parents, seg_lens, query_nodes, desc,
+                                                         query_lens=query_lens)
+        self.chunk_tokens = chunk_tokens
         if query_lens is not None:
             if query_centric or node_chunks:
                 raise ValueError("query_lens is supported by the tree plan only")
