@@ -500,3 +500,45 @@ def test_group_items_standard_tree_and_fused(monkeypatch):
     D.deft_tree_attention_fused(q, kc, vc, bt, ta.plan, out2, ta.desc, ta.workspace)
     torch.cuda.synchronize()
     assert np.array_equal(out2.double().cpu().numpy(), got)
+
+
+@pytest.mark.parametrize("cfg,force", [(2, None), (4, None), (3, None), (2, FORCE_WIDE), (2, FORCE_GROUP),
+                                       (1, None)])
+def test_fused_path_reads_fresh_partials(monkeypatch, cfg, force):
+    """The single-dispatch path hands partials between work-groups (possibly
+    on different XCDs) through device-coherent stores and loads and relaxed
+    tickets.  Stale data would show here: calls alternate between two input
+    sets (the second with Q negated and V permuted across the tree's tokens), the
+    workspace is filled with NaN before each call, and every call's output is
+    compared with the two-dispatch path's on the same inputs bit for bit (the
+    first input set's also with the oracle)."""
+    if force is not None:
+        monkeypatch.setenv(*force)
+    wl = W.standard_workload(cfg)
+    say("fused fresh", cfg, force)
+    q, kc, vc, bt = gpu_inputs(wl)
+    q2 = (-q).contiguous()
+    # V permuted across the tree's tokens (pages of the pool that hold none
+    # stay poisoned, so the permutation stays among written rows)
+    t = torch.arange(wl.total_tokens)
+    pi, ri = bt.cpu().long()[t // 16].to(vc.device), (t % 16).to(vc.device)
+    perm = torch.randperm(wl.total_tokens, generator=torch.Generator().manual_seed(cfg)).to(vc.device)
+    vc2 = vc.clone()
+    vc2[pi, ri] = vc[pi[perm], ri[perm]]
+    desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens, desc, device=DEV)
+    refs = []
+    for qq, vv in ((q, vc), (q2, vc2)):
+        o = torch.full_like(q, float("nan"))
+        D.deft_tree_attention(qq, kc, vv, bt, ta.plan, o, desc, ta.workspace)
+        refs.append(o)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        k = rep % 2
+        qq, vv = ((q, vc), (q2, vc2))[k]
+        ta.workspace.view(torch.float32).fill_(float("nan"))
+        o = torch.full_like(q, float("nan"))
+        D.deft_tree_attention_fused(qq, kc, vv, bt, ta.plan, o, desc, ta.workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(o, refs[k]), f"rep {rep}: fused output differs from the two-dispatch path"
+    check_close(refs[0].double().cpu().numpy(), oracle_out(wl), TOL[wl.dtype], "fused fresh, inputs 1")

@@ -41,6 +41,7 @@
 #include <cstdint>
 #include <mutex>
 #include <type_traits>
+#include <utility>
 #include <vector>
 
 #include "deft_internal.h"
@@ -226,7 +227,7 @@ __device__ inline void stage_token_rows(int32_t* tok_row, const DevPlan& P, cons
 
 // ---------------------------------------------------------------------------
 // Merge kernel: four (query, query head) rows per wave, one per 16-lane row
-// of lanes (merge_rows4 below).
+// of lanes (merge_rows below).
 // ---------------------------------------------------------------------------
 
 // Whole-wave reductions without the LDS crossbar: DPP within each row of 16
@@ -288,126 +289,256 @@ __device__ inline float row_reduce16(float x, Op op) {
   return op(x, dpp(x, std::integral_constant<int, 0x140>{}));   // row_mirror
 }
 
+// Accesses of partial results.  COHERENT (the single-dispatch path, whose
+// last work-group of a (query, head) row reads partials other work-groups
+// wrote, possibly on other XCDs with their own L2): relaxed device-scope
+// atomic stores and loads, which the compiler emits as ordinary vector
+// memory instructions with device coherence scope (sc1 on gfx950: stores
+// written through to the device's coherence point, loads served from it), so
+// no write-back or invalidation of a whole L2 is needed to hand partials
+// from one work-group to another; ordering comes from each wave's wait for
+// its own stores and a work-group barrier before the relaxed ticket.  The
+// two-dispatch path (kernel boundary in between) uses plain accesses.
+template <bool COHERENT>
+__device__ inline void st_u32(void* p, uint32_t v) {
+  if constexpr (COHERENT) __hip_atomic_store(static_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *static_cast<uint32_t*>(p) = v;
+}
+template <bool COHERENT>
+__device__ inline void st_f32(float* p, float v) { st_u32<COHERENT>(p, __float_as_uint(v)); }
+template <bool COHERENT>
+__device__ inline void st_u32x2(void* p, uint32_t lo, uint32_t hi) {
+  if constexpr (COHERENT)
+    __hip_atomic_store(static_cast<uint64_t*>(p), (static_cast<uint64_t>(hi) << 32) | lo, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else *static_cast<u32x2*>(p) = u32x2{lo, hi};
+}
+template <bool COHERENT>
+__device__ inline void st_f32x4(float* p, f32x4 v) {
+  if constexpr (COHERENT) {
+    st_u32x2<true>(p, __float_as_uint(v[0]), __float_as_uint(v[1]));
+    st_u32x2<true>(p + 2, __float_as_uint(v[2]), __float_as_uint(v[3]));
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+template <bool COHERENT>
+__device__ inline float ld_f32(const float* p) {
+  if constexpr (COHERENT)
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+  else return *p;
+}
+template <bool COHERENT>
+__device__ inline u32x2 ld_u32x2(const void* p) {
+  if constexpr (COHERENT) {
+    const uint64_t v = __hip_atomic_load(static_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return u32x2{static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32)};
+  } else {
+    return *static_cast<const u32x2*>(p);
+  }
+}
+template <bool COHERENT>
+__device__ inline u32x4 ld_u32x4(const void* p) {
+  if constexpr (COHERENT) {
+    const u32x2 a = ld_u32x2<true>(p), b = ld_u32x2<true>(static_cast<const char*>(p) + 8);
+    return u32x4{a[0], a[1], b[0], b[1]};
+  } else {
+    return *static_cast<const u32x4*>(p);
+  }
+}
+
+// Partial-result format of a merge: read from MergeArgs at run time, or
+// fixed by a caller that knows it.
+constexpr int kFmtRuntime = -1, kFmtF32 = 0, kFmtBf16 = 1;
+
 // EPL consecutive elements of one partial O row (slot-head sh) as raw words:
 // bf16 (O / l) or fp32 (unnormalised O).
-template <int D, int EPL>
+template <int EPL, int FMT>
 struct PartialRow {
-  static constexpr int WORDS = EPL;   // enough for fp32; bf16 uses the first EPL / 2
+  static constexpr int WORDS = FMT == kFmtBf16 ? EPL / 2 : EPL;
   uint32_t w[WORDS];
 };
-template <int D, int EPL>
-__device__ inline void load_partial_row(const MergeArgs& a, int64_t sh, int sub, PartialRow<D, EPL>& r) {
-  if (a.po_bf16) {
+template <int FMT>
+__device__ inline bool fmt_bf16(const MergeArgs& a) {
+  if constexpr (FMT == kFmtRuntime) return a.po_bf16 != 0;
+  else return FMT == kFmtBf16;
+}
+template <int D, int EPL, int FMT, bool COHERENT>
+__device__ inline void load_partial_row(const MergeArgs& a, int64_t sh, int sub, PartialRow<EPL, FMT>& r) {
+  if (fmt_bf16<FMT>(a)) {
     const uint16_t* src = reinterpret_cast<const uint16_t*>(a.po) + sh * D + sub * EPL;
     if constexpr (EPL == 8) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+      const u32x4 v = ld_u32x4<COHERENT>(src);
 #pragma unroll
       for (int e = 0; e < 4; ++e) r.w[e] = v[e];
     } else {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+      const u32x2 v = ld_u32x2<COHERENT>(src);
       r.w[0] = v[0];
       r.w[1] = v[1];
     }
-  } else {
+    // with the format chosen at run time, every word is defined on both
+    // branches, which keeps the row in registers
+    if constexpr (FMT == kFmtRuntime) {
+#pragma unroll
+      for (int e = EPL / 2; e < EPL; ++e) r.w[e] = 0u;
+    }
+  } else if constexpr (FMT != kFmtBf16) {
     const float* src = a.po + sh * D + sub * EPL;
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + e);
+      const u32x4 v = ld_u32x4<COHERENT>(src + e);
 #pragma unroll
       for (int k = 0; k < 4; ++k) r.w[e + k] = v[k];
     }
   }
 }
-template <int D, int EPL>
-__device__ inline float partial_elem(const MergeArgs& a, const PartialRow<D, EPL>& r, int e) {
-  if (a.po_bf16) return __uint_as_float(e & 1 ? (r.w[e >> 1] & 0xffff0000u) : (r.w[e >> 1] << 16));
-  return __uint_as_float(r.w[e]);
+template <int EPL, int FMT>
+__device__ inline float partial_elem(const MergeArgs& a, const PartialRow<EPL, FMT>& r, int e) {
+  if (fmt_bf16<FMT>(a)) return __uint_as_float(e & 1 ? (r.w[e >> 1] & 0xffff0000u) : (r.w[e >> 1] << 16));
+  if constexpr (FMT != kFmtBf16) return __uint_as_float(r.w[e]);
+  else return 0.f;
+}
+// Lane J's value of each 16-lane row, J = 0..15, in every lane of the row.
+template <typename X, int... J>
+__device__ inline void row_bcast_all(X x, X (&out)[16], std::integer_sequence<int, J...>) {
+  ((out[J] = row_bcast<J>(x)), ...);
 }
 
-// Merge of up to four (query, query head) rows per wave, one per 16-lane
-// row of lanes; `code` = qi * Hq + h for this lane's row, or -1 for none.
-// Lane sub of a row reads the metadata (slot id, m, l) of the row's slots
-// sub, sub + 16, ... and D/16 consecutive elements of every slot's partial O
-// row, so a row costs two rounds of dependent loads (the slot ids, then m, l
-// and the O rows together).  With M = max_s m_s and w_s = exp(m_s - M):
+// Merge of (query, query head) rows: NC rows per 16-lane row of lanes, so
+// 4 * NC per wave; codes[c] = qi * Hq + h of this lane's c-th row, or -1 for
+// none.  Lane sub of a row reads the metadata (slot id, m, l) of the row's
+// slots sub, sub + 16, ... and D/16 consecutive elements of every slot's
+// partial O row.  A round of up to 16 slots costs two rounds of dependent
+// loads (the slot ids, then m, l and the O rows together), and the loads of
+// all NC rows are issued before any of them is reduced, so NC rows cost the
+// latency of one.  With M = max_s m_s and w_s = exp(m_s - M):
 //   fp32 unnormalised partials   out = sum_s w_s O_s / sum_s w_s l_s
 //   bf16 partials holding O_s/l_s out = sum_s w_s l_s (O_s/l_s) / sum_s w_s l_s
 // Rows with more than 16 slots take several rounds, rescaled online.
-template <typename T, int D>
-__device__ void merge_rows4(const MergeArgs& a, int code) {
+// PRE: the caller has already read each row's slot count and its first 16
+// slot ids into LDS (pre.ids[u * 16 + s], pre.cnt[u] for the row's query
+// index us[c]), so the first round starts with the partials' own loads.
+struct PrefetchedSlots {
+  const int32_t* ids;
+  const int32_t* cnt;
+};
+template <typename T, int D, bool COHERENT, int NC, int FMT, bool PRE = false>
+__device__ __attribute__((always_inline)) void merge_rows(const MergeArgs& a, const int (&codes)[NC],
+                                                          PrefetchedSlots pre = {}, const int* us = nullptr) {
   constexpr int EPL = D / 16;      // elements per lane
   const int lane = threadIdx.x & 63, sub = lane & 15;
-  const bool live = code >= 0;
-  const int qi = live ? code / a.hq : 0, h = live ? code % a.hq : 0;
-  // The row's slot list: fixed stride (padded with -1, read without a
-  // dependent offset lookup) or CSR.
-  const int32_t* list;
-  int cnt;
-  if (a.merge_stride > 0) {
-    list = a.merge_slots + static_cast<size_t>(qi) * a.merge_stride;
-    cnt = live ? a.merge_stride : 0;
-  } else {
-    const int s0 = a.query_slot_offsets[qi];
-    list = a.query_slots + s0;
-    cnt = live ? a.query_slot_offsets[qi + 1] - s0 : 0;
-  }
-  const int cmax = static_cast<int>(wave_max(static_cast<float>(cnt)));
-  float acc[EPL];
+  bool live[NC];
+  int qi[NC], h[NC], cnt[NC];
+  const int32_t* list[NC];
+  int cmx = 0;
+  // the row's slot list: fixed stride (padded with -1, read without a
+  // dependent offset lookup) or CSR
+  auto slot_list = [&](int q, int& n) {
+    if (a.merge_stride > 0) {
+      n = a.merge_stride;
+      return a.merge_slots + static_cast<size_t>(q) * a.merge_stride;
+    }
+    const int s0 = a.query_slot_offsets[q];
+    n = a.query_slot_offsets[q + 1] - s0;
+    return a.query_slots + s0;
+  };
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  float mrun = kNegInf, wsum = 0.f;
+  for (int c = 0; c < NC; ++c) {
+    live[c] = codes[c] >= 0;
+    qi[c] = live[c] ? codes[c] / a.hq : 0;
+    h[c] = live[c] ? codes[c] % a.hq : 0;
+    if constexpr (PRE) {
+      list[c] = nullptr;               // looked up only for rows of more than 16 slots
+      cnt[c] = live[c] ? pre.cnt[us[c]] : 0;
+    } else {
+      int n;
+      list[c] = slot_list(qi[c], n);
+      cnt[c] = live[c] ? n : 0;
+    }
+    cmx = cnt[c] > cmx ? cnt[c] : cmx;
+  }
+  const int cmax = static_cast<int>(wave_max(static_cast<float>(cmx)));
+  float acc[NC][EPL], mrun[NC], wsum[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    mrun[c] = kNegInf;
+    wsum[c] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[c][e] = 0.f;
+  }
   for (int i0 = 0; i0 < cmax; i0 += 16) {
-    const int raw = i0 + sub < cnt ? list[i0 + sub] : -1;
-    const bool ok = raw >= 0;                   // padding entries are -1
-    const int64_t sh = static_cast<int64_t>(ok ? raw : 0) * a.hq + h;
-    const float mv = ok ? a.pm[sh] : kNegInf;
-    const float lv = ok ? a.pl[sh] : 0.f;
-    // every slot's O row of this round, issued before any reduction
-    PartialRow<D, EPL> rows[16];
-    int sj[16];
-    sj[0] = row_bcast<0>(raw); sj[1] = row_bcast<1>(raw); sj[2] = row_bcast<2>(raw); sj[3] = row_bcast<3>(raw);
-    sj[4] = row_bcast<4>(raw); sj[5] = row_bcast<5>(raw); sj[6] = row_bcast<6>(raw); sj[7] = row_bcast<7>(raw);
-    sj[8] = row_bcast<8>(raw); sj[9] = row_bcast<9>(raw); sj[10] = row_bcast<10>(raw); sj[11] = row_bcast<11>(raw);
-    sj[12] = row_bcast<12>(raw); sj[13] = row_bcast<13>(raw); sj[14] = row_bcast<14>(raw); sj[15] = row_bcast<15>(raw);
+    int raw[NC];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (sj[j] >= 0) load_partial_row<D, EPL>(a, static_cast<int64_t>(sj[j]) * a.hq + h, sub, rows[j]);
-    const float mnew = fmaxf(mrun, row_reduce16(mv, [](float x, float y) { return fmaxf(x, y); }));
-    const float w = mv == kNegInf ? 0.f : __expf(mv - mnew);
-    const float wl = w * lv;
-    const float wt = a.po_bf16 ? wl : w;      // weight of the stored O row
-    const float rescale = mrun == kNegInf ? 0.f : __expf(mrun - mnew);
-    mrun = mnew;
-    wsum = wsum * rescale + row_reduce16(wl, [](float x, float y) { return x + y; });
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] *= rescale;
-    float wj[16];
-    wj[0] = row_bcast<0>(wt); wj[1] = row_bcast<1>(wt); wj[2] = row_bcast<2>(wt); wj[3] = row_bcast<3>(wt);
-    wj[4] = row_bcast<4>(wt); wj[5] = row_bcast<5>(wt); wj[6] = row_bcast<6>(wt); wj[7] = row_bcast<7>(wt);
-    wj[8] = row_bcast<8>(wt); wj[9] = row_bcast<9>(wt); wj[10] = row_bcast<10>(wt); wj[11] = row_bcast<11>(wt);
-    wj[12] = row_bcast<12>(wt); wj[13] = row_bcast<13>(wt); wj[14] = row_bcast<14>(wt); wj[15] = row_bcast<15>(wt);
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (sj[j] >= 0) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wj[j], partial_elem<D, EPL>(a, rows[j], e), acc[e]);
+    for (int c = 0; c < NC; ++c) {
+      if constexpr (PRE) {
+        if (i0 == 0) {
+          raw[c] = live[c] ? pre.ids[us[c] * 16 + sub] : -1;
+          continue;
+        }
+        if (i0 == 16 && live[c]) {
+          int n;
+          list[c] = slot_list(qi[c], n);
+        }
       }
+      raw[c] = i0 + sub < cnt[c] ? list[c][i0 + sub] : -1;
+    }
+    // every slot's m, l and O row of this round, for all NC rows, issued
+    // before any reduction
+    float mv[NC], lv[NC];
+    int sj[NC][16];
+    PartialRow<EPL, FMT> rows[NC][16];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const bool ok = raw[c] >= 0;                   // padding entries are -1
+      const int64_t sh = static_cast<int64_t>(ok ? raw[c] : 0) * a.hq + h[c];
+      mv[c] = ok ? ld_f32<COHERENT>(a.pm + sh) : kNegInf;
+      lv[c] = ok ? ld_f32<COHERENT>(a.pl + sh) : 0.f;
+      row_bcast_all(raw[c], sj[c], std::make_integer_sequence<int, 16>{});
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (sj[c][j] >= 0)
+          load_partial_row<D, EPL, FMT, COHERENT>(a, static_cast<int64_t>(sj[c][j]) * a.hq + h[c], sub, rows[c][j]);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float mnew = fmaxf(mrun[c], row_reduce16(mv[c], [](float x, float y) { return fmaxf(x, y); }));
+      const float w = mv[c] == kNegInf ? 0.f : __expf(mv[c] - mnew);
+      const float wl = w * lv[c];
+      const float wt = fmt_bf16<FMT>(a) ? wl : w;      // weight of the stored O row
+      const float rescale = mrun[c] == kNegInf ? 0.f : __expf(mrun[c] - mnew);
+      mrun[c] = mnew;
+      wsum[c] = wsum[c] * rescale + row_reduce16(wl, [](float x, float y) { return x + y; });
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[c][e] *= rescale;
+      float wj[16];
+      row_bcast_all(wt, wj, std::make_integer_sequence<int, 16>{});
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (sj[c][j] >= 0) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[c][e] = fmaf(wj[j], partial_elem<EPL, FMT>(a, rows[c][j], e), acc[c][e]);
+        }
+    }
   }
-  if (!live) return;
-  const float inv = 1.f / wsum;
-  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + sub * EPL;
-  if constexpr (sizeof(T) == 2) {
-    uint32_t pk[EPL / 2];
 #pragma unroll
-    for (int e = 0; e < EPL / 2; ++e)
-      pk[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-    if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ob) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-    else *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = u32x2{pk[0], pk[1]};
-  } else {
+  for (int c = 0; c < NC; ++c) {
+    if (!live[c]) continue;
+    const float inv = 1.f / wsum[c];
+    const size_t ob = (static_cast<size_t>(qi[c]) * a.hq + h[c]) * D + sub * EPL;
+    if constexpr (sizeof(T) == 2) {
+      uint32_t pk[EPL / 2];
 #pragma unroll
-    for (int e = 0; e < EPL; e += 4)
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob + e) =
-          f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+      for (int e = 0; e < EPL / 2; ++e)
+        pk[e] = pack_bf16x2(acc[c][2 * e] * inv, acc[c][2 * e + 1] * inv);
+      if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ob) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      else *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = u32x2{pk[0], pk[1]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob + e) =
+            f32x4{acc[c][e] * inv, acc[c][e + 1] * inv, acc[c][e + 2] * inv, acc[c][e + 3] * inv};
+    }
   }
 }
 
@@ -416,7 +547,8 @@ __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
   const int wave0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
   if (wave0 >= a.nq * a.hq) return;          // whole waves leave together
   const int code = wave0 + ((threadIdx.x & 63) >> 4);
-  merge_rows4<T, D>(a, code < a.nq * a.hq ? code : -1);
+  const int codes[1] = {code < a.nq * a.hq ? code : -1};
+  merge_rows<T, D, false, 1, kFmtRuntime>(a, codes);
 }
 
 // ---------------------------------------------------------------------------
@@ -425,49 +557,134 @@ __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
 // work-group that takes a row's last ticket (every slot of that query has
 // then written its partial) merges the row itself, through the same
 // per-(query, head) merge as the merge kernel, and resets the ticket to zero
-// for the next call.  Tickets are acquire-release atomics at device scope:
-// the release publishes the work-group's partials to the other L2s, the
-// acquire makes the merging work-group read everyone's.  Calls that share a
+// for the next call.  The partials of this path are stored and read with
+// device-coherent accesses (st_* / ld_* with COHERENT); every wave waits for
+// its own stores to complete and the work-group meets at a barrier before
+// the tickets are taken, so a row's last ticket is only taken once every
+// partial of that row has reached the device's coherence point, where the
+// merging work-group reads it.  The tickets are relaxed device-scope
+// atomics: no write-back or invalidation of a whole L2 cache, which would
+// also throw other work-groups' KV out of their XCD's L2.  Calls that share a
 // plan (and so its tickets) must not overlap.
+//
+// Everything the tail needs that no other work-group writes (each row's
+// query, slot count and ticket address, and the first 16 slot ids of each
+// of the work-group's queries) is read before the wait for the partial
+// stores, so those plan lookups overlap it, and a merge starts with the
+// partials' own loads.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__device__ void fused_merge_tail(const MergeArgs& m, const DevPlan& P, int32_t* tickets, int grp,
-                                 int32_t rb, int32_t nr, int32_t gofs, int g, int32_t* last_list,
-                                 int32_t* n_last) {
+constexpr int kPartialThreads = 512;   // threads of a partial-kernel work-group
+
+// LDS of the tail, in the body's (then dead) buffers: prefetched slot ids and
+// counts of up to ROWS + 1 queries, and the query index of each merged row.
+template <int ROWS>
+struct TailLds {
+  static constexpr int MAX_Q = ROWS + 1;
+  static constexpr int IDS = 0;
+  static constexpr int CNT = IDS + 4 * 16 * MAX_Q;
+  static constexpr int ROW_Q = CNT + 4 * MAX_Q;
+  static constexpr int BYTES = ROW_Q + 4 * ROWS;
+  static constexpr int PER_THREAD = (16 * MAX_Q + kPartialThreads - 1) / kPartialThreads;
+};
+
+template <typename T, int D, int ROWS>
+__device__ __attribute__((always_inline)) void fused_merge_tail(const MergeArgs& m, const DevPlan& P,
+                                                                int32_t* tickets, int grp, int32_t rb,
+                                                                int32_t nr, int32_t gofs, int g, char* lds,
+                                                                int32_t* last_list, int32_t* n_last) {
+  static_assert(ROWS <= kPartialThreads, "one ticket lane per row");
+  using TL = TailLds<ROWS>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int nwave = blockDim.x >> 6;
-  // every wave's partial stores have completed before any ticket is taken
+  int32_t* pre_ids = reinterpret_cast<int32_t*>(lds + TL::IDS);
+  int32_t* pre_cnt = reinterpret_cast<int32_t*>(lds + TL::CNT);
+  int32_t* row_q = reinterpret_cast<int32_t*>(lds + TL::ROW_Q);
+  // queries of this work-group's rows: slot_query[gofs + u0 + u], u < nu
+  const int u0 = rb / grp;
+  const int nu = nr > 0 ? (rb + nr - 1) / grp - u0 + 1 : 0;
+  // this lane's row for the tickets
+  const int r = w * 64 + lane;
+  const bool has_row = r < nr;
+  int need = 0, code = -1, u = 0;
+  int32_t* t = tickets;
+  if (has_row) {
+    const int row = rb + r;
+    const int qi = P.slot_query[gofs + row / grp];
+    const int head = g * grp + row % grp;
+    need = P.query_slot_offsets[qi + 1] - P.query_slot_offsets[qi];
+    t = tickets + static_cast<size_t>(qi) * m.hq + head;
+    code = qi * m.hq + head;
+    u = row / grp - u0;
+  }
+  // first 16 slot ids and the slot count of each query (plan data)
+  int32_t pid[TL::PER_THREAD], pcnt[TL::PER_THREAD];
+#pragma unroll
+  for (int k = 0; k < TL::PER_THREAD; ++k) {
+    const int e = static_cast<int>(threadIdx.x) + k * kPartialThreads;
+    pid[k] = -1;
+    pcnt[k] = 0;
+    if (e < nu * 16) {
+      const int qi = P.slot_query[gofs + u0 + (e >> 4)];
+      int n;
+      const int32_t* list;
+      if (m.merge_stride > 0) {
+        n = m.merge_stride;
+        list = m.merge_slots + static_cast<size_t>(qi) * m.merge_stride;
+      } else {
+        const int s0 = m.query_slot_offsets[qi];
+        n = m.query_slot_offsets[qi + 1] - s0;
+        list = m.query_slots + s0;
+      }
+      pcnt[k] = n;
+      if ((e & 15) < n) pid[k] = list[e & 15];
+    }
+  }
+  // every wave's partial stores (and the lookups above) have completed
+  // before any ticket is taken; the body's LDS is free after the barrier
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int r0 = w * 64; r0 < nr; r0 += nwave * 64) {
-    int32_t code = -1;
-    const int r = r0 + lane;
-    if (r < nr) {
-      const int row = rb + r;
-      const int qi = P.slot_query[gofs + row / grp];
-      const int head = g * grp + row % grp;
-      const int need = P.query_slot_offsets[qi + 1] - P.query_slot_offsets[qi];
-      int32_t* t = tickets + static_cast<size_t>(qi) * m.hq + head;
-      const int old = __hip_atomic_fetch_add(t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == need - 1) {
-        __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        code = qi * m.hq + head;
-      }
+#pragma unroll
+  for (int k = 0; k < TL::PER_THREAD; ++k) {
+    const int e = static_cast<int>(threadIdx.x) + k * kPartialThreads;
+    if (e < nu * 16) {
+      pre_ids[e] = pid[k];
+      if ((e & 15) == 0) pre_cnt[e >> 4] = pcnt[k];
+    }
+  }
+  if (w * 64 < nr) {
+    if (has_row) {
+      const int old = __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == need - 1) __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else code = -1;
     }
     const uint64_t bal = __ballot(code >= 0);
     const int pos = __popcll(bal & ((1ull << lane) - 1ull));
-    // rows are taken in blocks of 64 by one wave each, so list slots never collide
-    if (code >= 0) last_list[r0 + pos] = code;
-    if (lane == 0) n_last[r0 / 64] = __popcll(bal);
+    // each wave lists the rows of its own block of 64
+    if (code >= 0) {
+      last_list[w * 64 + pos] = code;
+      row_q[w * 64 + pos] = u;
+    }
+    if (lane == 0) n_last[w] = __popcll(bal);
   }
   __syncthreads();
-  // merge the rows this work-group completed, four per wave
+  // merge the rows this work-group completed, 4 * NC per wave at a time;
+  // the partials of this path are bf16 (O / l) for bf16 attention and fp32
+  // for fp32, so the format is fixed here (two rows per lane row for bf16,
+  // whose rows take half the registers)
+  constexpr int NC = sizeof(T) == 2 ? 2 : 1;
+  constexpr int FMT = sizeof(T) == 2 ? kFmtBf16 : kFmtF32;
+  const int nwave = kPartialThreads / 64;
   const int nblk = (nr + 63) / 64;
   for (int b = 0; b < nblk; ++b) {
     const int cnt = n_last[b];
-    for (int k = 4 * w; k < cnt; k += 4 * nwave) {
-      const int j = k + (lane >> 4);
-      merge_rows4<T, D>(m, j < cnt ? last_list[b * 64 + j] : -1);
+    for (int k = 4 * NC * w; k < cnt; k += 4 * NC * nwave) {
+      int codes[NC], us[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int j = k + (lane >> 4) + 4 * c;
+        codes[c] = j < cnt ? last_list[b * 64 + j] : -1;
+        us[c] = j < cnt ? row_q[b * 64 + j] : 0;
+      }
+      merge_rows<T, D, true, NC, FMT, true>(m, codes, PrefetchedSlots{pre_ids, pre_cnt}, us);
     }
   }
 }
@@ -934,19 +1151,20 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
     const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
     if (a.po_bf16) {
       const float inv = 1.f / lsum;
-      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.po) + sh * D + e) =
-          pack_bf16x2(o0 * inv, o1 * inv);
+      st_u32<FUSED>(reinterpret_cast<uint16_t*>(a.po) + sh * D + e, pack_bf16x2(o0 * inv, o1 * inv));
     } else {
-      *reinterpret_cast<u32x2*>(a.po + sh * D + e) = u32x2{__float_as_uint(o0), __float_as_uint(o1)};
+      st_u32x2<FUSED>(a.po + sh * D + e, __float_as_uint(o0), __float_as_uint(o1));
     }
     if (e == 0) {
-      a.pm[sh] = mx == kNegInf ? kNegInf : mx * kLn2;
-      a.pl[sh] = lsum;
+      st_f32<FUSED>(a.pm + sh, mx == kNegInf ? kNegInf : mx * kLn2);
+      st_f32<FUSED>(a.pl + sh, lsum);
     }
   }
   if constexpr (FUSED) {
+    static_assert(TailLds<kValuRows>::BYTES <= Shape::LIST_OFF, "tail LDS fits the body's buffers");
     int32_t* last_list = reinterpret_cast<int32_t*>(lds + Shape::LIST_OFF);
-    fused_merge_tail<T, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, last_list + kValuRows);
+    fused_merge_tail<T, D, kValuRows>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, lds, last_list,
+                                      last_list + kValuRows);
   }
 }
 
@@ -1415,8 +1633,8 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
         const int row = rb + r;
         const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
         if (ln < 16 && dq == 0) {
-          a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
-          a.pl[sh] = ls;
+          st_f32<FUSED>(a.pm + sh, mx == kNegInf ? kNegInf : mx * cl2 * kLn2);
+          st_f32<FUSED>(a.pl + sh, ls);
         }
         const float inv = 1.f / ls;
 #pragma unroll
@@ -1430,9 +1648,9 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
           if (a.po_bf16) {
             const uint32_t lo = pack_bf16x2(acc[0] * inv, acc[1] * inv);
             const uint32_t hi = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + at) = u32x2{lo, hi};
+            st_u32x2<FUSED>(reinterpret_cast<uint16_t*>(a.po) + at, lo, hi);
           } else {
-            *reinterpret_cast<f32x4*>(a.po + at) = acc;
+            st_f32x4<FUSED>(a.po + at, acc);
           }
         }
       }
@@ -1470,8 +1688,8 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
           const int row = rb + r;
           const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
           if (lj == 0) {
-            a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
-            a.pl[sh] = ls;
+            st_f32<FUSED>(a.pm + sh, mx == kNegInf ? kNegInf : mx * cl2 * kLn2);
+            st_f32<FUSED>(a.pl + sh, ls);
           }
           const float inv = 1.f / ls;
 #pragma unroll
@@ -1481,9 +1699,9 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
             if (a.po_bf16) {
               const uint32_t lo = pack_bf16x2(acc[0] * inv, acc[1] * inv);
               const uint32_t hi = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-              *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + at) = u32x2{lo, hi};
+              st_u32x2<FUSED>(reinterpret_cast<uint16_t*>(a.po) + at, lo, hi);
             } else {
-              *reinterpret_cast<f32x4*>(a.po + at) = acc;
+              st_f32x4<FUSED>(a.po + at, acc);
             }
           }
         }
@@ -1491,8 +1709,10 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     }
   }
   if constexpr (FUSED) {
+    static_assert(TailLds<ROWS>::BYTES <= Shape::LIST_OFF, "tail LDS fits the body's buffers");
     int32_t* last_list = reinterpret_cast<int32_t*>(lds + Shape::LIST_OFF);
-    fused_merge_tail<uint16_t, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, last_list + ROWS);
+    fused_merge_tail<uint16_t, D, ROWS>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, lds, last_list,
+                                        last_list + ROWS);
   }
 }
 
@@ -1868,8 +2088,8 @@ __device__ __forceinline__ void mfma_group_body(const PartialArgs& a, char* lds,
         const int row = rb + r;
         const int64_t sh = static_cast<int64_t>(gofs + row / a.grp) * a.hq + g * a.grp + row % a.grp;
         if (lj == 0) {
-          a.pm[sh] = mx == kNegInf ? kNegInf : mx * cl2 * kLn2;
-          a.pl[sh] = ls;
+          st_f32<FUSED>(a.pm + sh, mx == kNegInf ? kNegInf : mx * cl2 * kLn2);
+          st_f32<FUSED>(a.pl + sh, ls);
         }
         if (a.po_bf16) {
           const float inv = 1.f / lacc[rt][0];    // O / l, independent of the offset
@@ -1878,19 +2098,20 @@ __device__ __forceinline__ void mfma_group_body(const PartialArgs& a, char* lds,
             const f32x4 acc = o[dt][rt];
             const uint32_t lo = pack_bf16x2(acc[0] * inv, acc[1] * inv);
             const uint32_t hi = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.po) + sh * D + dt * 16 + lj * 4) = u32x2{lo, hi};
+            st_u32x2<FUSED>(reinterpret_cast<uint16_t*>(a.po) + sh * D + dt * 16 + lj * 4, lo, hi);
           }
         } else {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            *reinterpret_cast<f32x4*>(a.po + sh * D + dt * 16 + lj * 4) = f * o[dt][rt];
+          for (int dt = 0; dt < DT; ++dt) st_f32x4<FUSED>(a.po + sh * D + dt * 16 + lj * 4, f * o[dt][rt]);
         }
       }
     }
   }
   if constexpr (FUSED) {
+    static_assert(TailLds<ROWS>::BYTES <= Shape::LIST_OFF, "tail LDS fits the body's buffers");
     int32_t* last_list = reinterpret_cast<int32_t*>(lds + Shape::LIST_OFF);
-    fused_merge_tail<uint16_t, D>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, last_list, last_list + ROWS);
+    fused_merge_tail<uint16_t, D, ROWS>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, lds, last_list,
+                                        last_list + ROWS);
   }
 }
 
@@ -1904,8 +2125,8 @@ __device__ __forceinline__ void mfma_group_body(const PartialArgs& a, char* lds,
 // runs.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int R, bool FUSED>
-__global__ __launch_bounds__(512) void partial_attention(PartialArgs a) {
-  static_assert(64 * valu_waves<R>() == 512, "both bodies run 8 waves");
+__global__ __launch_bounds__(kPartialThreads) void partial_attention(PartialArgs a) {
+  static_assert(64 * valu_waves<R>() == kPartialThreads, "both bodies run 8 waves");
   constexpr int VB = ValuShape<T, D, R>::LDS_B;
   constexpr int MB4 = sizeof(T) == 2 ? MfmaShape<D, 4>::LDS_B : 0;
   constexpr int MB2 = sizeof(T) == 2 ? MfmaShape<D, 2>::LDS_B : 0;
@@ -2052,7 +2273,7 @@ static int launch_partials(const PartialArgs& pa, hipStream_t st) {
   const int hkv = pa.hkv;
   if (sizeof(T) != 2 && pa.plan.n_mfma_group + pa.plan.n_mfma + pa.plan.n_mfma_wide > 0)
     return fail(DEFT_ERR_UNSUPPORTED, "MFMA work for fp32 inputs");
-  const dim3 grid((pa.plan.n_mfma_group + pa.plan.n_mfma_wide + pa.plan.n_mfma + pa.plan.n_valu) * hkv), block(512);
+  const dim3 grid((pa.plan.n_mfma_group + pa.plan.n_mfma_wide + pa.plan.n_mfma + pa.plan.n_valu) * hkv), block(kPartialThreads);
   if (grid.x == 0) return DEFT_OK;
   // the VALU body's row capacity: 4 when every VALU item fits, else 8
   static_assert(kValuRows == 8, "VALU row capacities are 4 and 8");
