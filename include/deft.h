@@ -303,14 +303,19 @@ int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
  * Accumulation" gives the rule).  Unlike that description, partials still
  * pass through memory: the workspace holds them as for deft_tree_attention
  * (4.46 MB written and read back on the 4K-prefix / 64-node tree), because
- * the chunks of one query run on different compute units.  Every
- * work-group, after writing its partials, takes a device-scope
- * acquire-release ticket for each (query, head) row it wrote; the one that
- * takes a row's last ticket merges that row and writes `out`, then resets the
- * ticket.  The tickets live in the plan's device image (zero after upload and
- * after every completed call), so calls that share a plan must not overlap
- * and the plan is not const here.  Arguments, layouts, workspace and errors
- * as for deft_tree_attention; results are bitwise equal to it.
+ * the chunks of one query run on different compute units.  The one grid
+ * holds the partial work-groups followed by merge work-groups (16 (query,
+ * head) rows each while that needs at most 128 of them, else 32).  A
+ * partial work-group writes its partials with
+ * device-coherent stores, waits for them, and adds one to a device-scope
+ * ticket per (query, head) row it wrote; a merge work-group waits until its
+ * rows' tickets count every slot of their query, resets them, merges the
+ * rows and writes `out`.  Its wait is bounded (as deft_plan_status
+ * describes): past the limit it reports a give-up and merges what it finds.
+ * The tickets live in the plan's device image (zero after upload and after
+ * every completed call), so calls that share a plan must not overlap and the
+ * plan is not const here.  Arguments, layouts, workspace and errors as for
+ * deft_tree_attention; results are bitwise equal to it.
  */
 int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_table, deft_plan* plan, void* out,
@@ -321,9 +326,12 @@ int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_
  * Whether the attention calls on this plan since the last check ran
  * correctly.  The matrix-core partial kernels synchronise the waves that
  * share an LDS ring through flags with a bounded wait (2^20 checks, about
- * 30 ms; DEFT_SPIN_LIMIT in the environment lowers it, for tests); a wait
- * that runs out never hangs the GPU but leaves that work-group's results
- * invalid, and sets a status word in the plan's device image.  This call
+ * 30 ms; DEFT_SPIN_LIMIT in the environment lowers it, for tests), and the
+ * merge work-groups of deft_tree_attention_fused wait for their rows'
+ * tickets with the same number of checks (each a device-scope load, so
+ * about a second); a wait that runs out never hangs the GPU but leaves that
+ * work-group's results invalid, and sets a status word in the plan's device
+ * image.  This call
  * copies that word to the host on `stream`, synchronises the stream, and
  * returns DEFT_ERR_HIP (with a message) if it was set, clearing it; else
  * DEFT_OK.  INVALID_ARGUMENT if the plan is NULL or has no device image.

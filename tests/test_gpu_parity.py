@@ -377,6 +377,30 @@ def test_single_node_single_query_and_duplicates():
             check_close(got, oracle_out(wl), TOL[dtype], "edge")
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 64), (torch.bfloat16, 64), (torch.float32, 128)])
+def test_fused_merge_work_groups_many_rows(dtype, d):
+    """161 queries x 16 heads = 2576 (query, head) rows: the single-dispatch
+    path's merge work-groups take 32 rows, the last one ragged (16 rows).
+    Output equals the two-dispatch path bit for bit, twice in a row (the
+    tickets return to zero), and the oracle within tolerance."""
+    p, s, qn = W.shared_prompt_branches(48, 161, 3)
+    wl = W.make_workload("many-rows", p, s, qn, chunk_tokens=32, hq=16, hkv=4, d=d, dtype=dtype, seed=5,
+                         placement="permuted")
+    say("fused many rows", str(dtype), d)
+    q, kc, vc, bt = gpu_inputs(wl)
+    desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens, desc, device=DEV)
+    ref = torch.full_like(q, float("nan"))
+    D.deft_tree_attention(q, kc, vc, bt, ta.plan, ref, desc, ta.workspace)
+    for rep in range(2):
+        ta.workspace.view(torch.float32).fill_(float("nan"))
+        o = torch.full_like(q, float("nan"))
+        D.deft_tree_attention_fused(q, kc, vc, bt, ta.plan, o, desc, ta.workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref), f"rep {rep}: fused output differs from the two-dispatch path"
+    check_close(ref.double().cpu().numpy(), oracle_out(wl), TOL[dtype], "many rows")
+
+
 @pytest.mark.timeout(900)
 def test_long_context_spec_tree_all_queries():
     """The 32K-prefix / 256-node tree in a pool filling ~60% of HBM, pages at
@@ -502,8 +526,8 @@ def test_group_items_standard_tree_and_fused(monkeypatch):
     assert np.array_equal(out2.double().cpu().numpy(), got)
 
 
-@pytest.mark.parametrize("cfg,force", [(2, None), (4, None), (3, None), (2, FORCE_WIDE), (2, FORCE_GROUP),
-                                       (1, None)])
+@pytest.mark.parametrize("cfg,force", [(2, None), (4, None), (3, None), (6, None), (2, FORCE_WIDE),
+                                       (2, FORCE_GROUP), (1, None)])
 def test_fused_path_reads_fresh_partials(monkeypatch, cfg, force):
     """The single-dispatch path hands partials between work-groups (possibly
     on different XCDs) through device-coherent stores and loads and relaxed
@@ -526,7 +550,8 @@ def test_fused_path_reads_fresh_partials(monkeypatch, cfg, force):
     vc2 = vc.clone()
     vc2[pi, ri] = vc[pi[perm], ri[perm]]
     desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
-    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens, desc, device=DEV)
+    ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens, desc, device=DEV,
+                       query_lens=wl.query_lens)
     refs = []
     for qq, vv in ((q, vc), (q2, vc2)):
         o = torch.full_like(q, float("nan"))

@@ -105,7 +105,8 @@ struct PartialArgs {
   int32_t po_bf16;   // 1: store O / l rounded to bf16 (internal workspace format)
   float scale_log2;  // log2(e) / sqrt(d)
   int32_t spin_limit;   // checks of a bounded inter-wave wait before it gives up
-  int32_t fused;     // 1: launch the kernels' fused variants (fused_merge_tail)
+  int32_t fused;     // 1: single-dispatch launch (fused_publish, merge_worker)
+  int32_t merge_wg_rows;   // (query, head) rows per merge work-group when fused
   int32_t max_valu_rows;   // host only: picks the VALU kernel's row capacity
   MergeArgs merge;   // used when fused
 };
@@ -416,16 +417,12 @@ __device__ inline void row_bcast_all(X x, X (&out)[16], std::integer_sequence<in
 //   fp32 unnormalised partials   out = sum_s w_s O_s / sum_s w_s l_s
 //   bf16 partials holding O_s/l_s out = sum_s w_s l_s (O_s/l_s) / sum_s w_s l_s
 // Rows with more than 16 slots take several rounds, rescaled online.
-// PRE: the caller has already read each row's slot count and its first 16
-// slot ids into LDS (pre.ids[u * 16 + s], pre.cnt[u] for the row's query
-// index us[c]), so the first round starts with the partials' own loads.
-struct PrefetchedSlots {
-  const int32_t* ids;
-  const int32_t* cnt;
-};
+// PRE: the caller has already read each row's slot count (cnt0[c], 0 for no
+// row) and this lane's first slot id (raw0[c]: slot sub of the row's list,
+// or -1), so the first round starts with the partials' own loads.
 template <typename T, int D, bool COHERENT, int NC, int FMT, bool PRE = false>
 __device__ __attribute__((always_inline)) void merge_rows(const MergeArgs& a, const int (&codes)[NC],
-                                                          PrefetchedSlots pre = {}, const int* us = nullptr) {
+                                                          const int* raw0 = nullptr, const int* cnt0 = nullptr) {
   constexpr int EPL = D / 16;      // elements per lane
   const int lane = threadIdx.x & 63, sub = lane & 15;
   bool live[NC];
@@ -450,7 +447,7 @@ __device__ __attribute__((always_inline)) void merge_rows(const MergeArgs& a, co
     h[c] = live[c] ? codes[c] % a.hq : 0;
     if constexpr (PRE) {
       list[c] = nullptr;               // looked up only for rows of more than 16 slots
-      cnt[c] = live[c] ? pre.cnt[us[c]] : 0;
+      cnt[c] = live[c] ? cnt0[c] : 0;
     } else {
       int n;
       list[c] = slot_list(qi[c], n);
@@ -473,7 +470,7 @@ __device__ __attribute__((always_inline)) void merge_rows(const MergeArgs& a, co
     for (int c = 0; c < NC; ++c) {
       if constexpr (PRE) {
         if (i0 == 0) {
-          raw[c] = live[c] ? pre.ids[us[c] * 16 + sub] : -1;
+          raw[c] = live[c] ? raw0[c] : -1;
           continue;
         }
         if (i0 == 16 && live[c]) {
@@ -552,141 +549,105 @@ __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Fused merge (one dispatch for the whole step).  After its partial stores a
-// work-group takes one ticket per (query, query head) row it wrote; the
-// work-group that takes a row's last ticket (every slot of that query has
-// then written its partial) merges the row itself, through the same
-// per-(query, head) merge as the merge kernel, and resets the ticket to zero
-// for the next call.  The partials of this path are stored and read with
-// device-coherent accesses (st_* / ld_* with COHERENT); every wave waits for
-// its own stores to complete and the work-group meets at a barrier before
-// the tickets are taken, so a row's last ticket is only taken once every
-// partial of that row has reached the device's coherence point, where the
-// merging work-group reads it.  The tickets are relaxed device-scope
-// atomics: no write-back or invalidation of a whole L2 cache, which would
-// also throw other work-groups' KV out of their XCD's L2.  Calls that share a
-// plan (and so its tickets) must not overlap.
+// Single-dispatch step.  The grid holds the partial work-groups followed by
+// merge work-groups of 16 or 32 (query, query head) rows each.  A
+// partial work-group stores its partials with device-coherent accesses
+// (st_* with COHERENT), every wave waits for its own stores to complete, the
+// work-group meets at a barrier, and it adds one to a ticket per (query,
+// head) row it wrote (a relaxed device-scope atomic whose old value is not
+// returned), then leaves.  A merge work-group reads its rows' slot counts
+// and first slot ids, polls the rows' tickets until each has counted every
+// slot of its query (a bounded wait: past the spin limit it reports a
+// give-up through the plan's status word and merges what is there), resets
+// them to zero for the next call, and merges the rows through the same
+// per-(query, head) merge as the merge kernel, with device-coherent loads.
 //
-// Everything the tail needs that no other work-group writes (each row's
-// query, slot count and ticket address, and the first 16 slot ids of each
-// of the work-group's queries) is read before the wait for the partial
-// stores, so those plan lookups overlap it, and a merge starts with the
-// partials' own loads.
+// The dispatcher places work-groups in index order, so a merge work-group
+// only takes a compute unit once every partial work-group has been placed,
+// and no partial work-group waits for anything.  The merge reads spread over
+// many work-groups (a merge by the work-group that completes a row would
+// gather them on the few that finish last), and no
+// write-back or invalidation of a whole L2 is needed (which would also throw
+// other work-groups' KV out of their XCD's L2).  Calls that share a plan
+// (and so its tickets) must not overlap.
 // ---------------------------------------------------------------------------
-constexpr int kPartialThreads = 512;   // threads of a partial-kernel work-group
+// A bounded wait that ran out of checks: the work-group's results are
+// invalid; the plan's status word (device memory) records it for
+// deft_plan_status.
+__device__ inline void report_give_up(int32_t* status, int lane) {
+  if (lane == 0) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr int kPartialThreads = 512;    // threads of a partial-kernel work-group
+// Rows per merge work-group: 16 (four waves of 4 rows) while that keeps the
+// merge work-groups within kMergeWorkGroups, else 32 (eight waves), so that
+// the merge reads spread over many compute units without the merge
+// work-groups outnumbering them by far (measured on the 4K-prefix, parallel
+// sampling, reasoning and multi-token trees: 8 rows, or 64 rows at two per
+// lane row, were slower).
+constexpr int kMergeWorkGroups = 128;
+inline int merge_worker_rows(int nrows) { return (nrows + 15) / 16 <= kMergeWorkGroups ? 16 : 32; }
 
-// LDS of the tail, in the body's (then dead) buffers: prefetched slot ids and
-// counts of up to ROWS + 1 queries, and the query index of each merged row.
+// End of a partial work-group on the single-dispatch path: tickets of rows
+// [rb, rb + nr) of its item, once its partial stores have completed.
 template <int ROWS>
-struct TailLds {
-  static constexpr int MAX_Q = ROWS + 1;
-  static constexpr int IDS = 0;
-  static constexpr int CNT = IDS + 4 * 16 * MAX_Q;
-  static constexpr int ROW_Q = CNT + 4 * MAX_Q;
-  static constexpr int BYTES = ROW_Q + 4 * ROWS;
-  static constexpr int PER_THREAD = (16 * MAX_Q + kPartialThreads - 1) / kPartialThreads;
-};
-
-template <typename T, int D, int ROWS>
-__device__ __attribute__((always_inline)) void fused_merge_tail(const MergeArgs& m, const DevPlan& P,
-                                                                int32_t* tickets, int grp, int32_t rb,
-                                                                int32_t nr, int32_t gofs, int g, char* lds,
-                                                                int32_t* last_list, int32_t* n_last) {
+__device__ __attribute__((always_inline)) void fused_publish(const DevPlan& P, int hq, int grp, int32_t rb,
+                                                             int32_t nr, int32_t gofs, int g) {
   static_assert(ROWS <= kPartialThreads, "one ticket lane per row");
-  using TL = TailLds<ROWS>;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int32_t* pre_ids = reinterpret_cast<int32_t*>(lds + TL::IDS);
-  int32_t* pre_cnt = reinterpret_cast<int32_t*>(lds + TL::CNT);
-  int32_t* row_q = reinterpret_cast<int32_t*>(lds + TL::ROW_Q);
-  // queries of this work-group's rows: slot_query[gofs + u0 + u], u < nu
-  const int u0 = rb / grp;
-  const int nu = nr > 0 ? (rb + nr - 1) / grp - u0 + 1 : 0;
-  // this lane's row for the tickets
-  const int r = w * 64 + lane;
-  const bool has_row = r < nr;
-  int need = 0, code = -1, u = 0;
-  int32_t* t = tickets;
-  if (has_row) {
+  const int r = static_cast<int>(threadIdx.x);
+  int32_t* t = nullptr;
+  if (r < nr) {      // the ticket's address is looked up while the stores drain
     const int row = rb + r;
     const int qi = P.slot_query[gofs + row / grp];
-    const int head = g * grp + row % grp;
-    need = P.query_slot_offsets[qi + 1] - P.query_slot_offsets[qi];
-    t = tickets + static_cast<size_t>(qi) * m.hq + head;
-    code = qi * m.hq + head;
-    u = row / grp - u0;
+    t = P.tickets + static_cast<size_t>(qi) * hq + g * grp + row % grp;
   }
-  // first 16 slot ids and the slot count of each query (plan data)
-  int32_t pid[TL::PER_THREAD], pcnt[TL::PER_THREAD];
-#pragma unroll
-  for (int k = 0; k < TL::PER_THREAD; ++k) {
-    const int e = static_cast<int>(threadIdx.x) + k * kPartialThreads;
-    pid[k] = -1;
-    pcnt[k] = 0;
-    if (e < nu * 16) {
-      const int qi = P.slot_query[gofs + u0 + (e >> 4)];
-      int n;
-      const int32_t* list;
-      if (m.merge_stride > 0) {
-        n = m.merge_stride;
-        list = m.merge_slots + static_cast<size_t>(qi) * m.merge_stride;
-      } else {
-        const int s0 = m.query_slot_offsets[qi];
-        n = m.query_slot_offsets[qi + 1] - s0;
-        list = m.query_slots + s0;
-      }
-      pcnt[k] = n;
-      if ((e & 15) < n) pid[k] = list[e & 15];
-    }
-  }
-  // every wave's partial stores (and the lookups above) have completed
-  // before any ticket is taken; the body's LDS is free after the barrier
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-#pragma unroll
-  for (int k = 0; k < TL::PER_THREAD; ++k) {
-    const int e = static_cast<int>(threadIdx.x) + k * kPartialThreads;
-    if (e < nu * 16) {
-      pre_ids[e] = pid[k];
-      if ((e & 15) == 0) pre_cnt[e >> 4] = pcnt[k];
-    }
+  if (r < nr) __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge work-group mw of `rows` (query, head) rows (16 or 32): wave w
+// merges rows mw * rows + 4 * w + (lane / 16).
+template <typename T, int D>
+__device__ __attribute__((always_inline)) void merge_worker(const MergeArgs& m, const DevPlan& P,
+                                                            int32_t spin_limit, int mw, int rows) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, sub = lane & 15;
+  const int nrows = m.nq * m.hq;
+  const int code0 = mw * rows + w * 4;
+  if (w * 4 >= rows || code0 >= nrows) return;     // whole waves leave together
+  const int code = code0 + (lane >> 4);
+  const bool live = code < nrows;
+  const int qi = live ? code / m.hq : 0;
+  // everything but the partials themselves, read before the wait
+  const int need = live ? P.query_slot_offsets[qi + 1] - P.query_slot_offsets[qi] : 0;
+  int n;
+  const int32_t* list;
+  if (m.merge_stride > 0) {
+    n = m.merge_stride;
+    list = m.merge_slots + static_cast<size_t>(qi) * m.merge_stride;
+  } else {
+    const int s0 = m.query_slot_offsets[qi];
+    n = m.query_slot_offsets[qi + 1] - s0;
+    list = m.query_slots + s0;
   }
-  if (w * 64 < nr) {
-    if (has_row) {
-      const int old = __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == need - 1) __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else code = -1;
+  const int raw = live && sub < n ? list[sub] : -1;
+  int32_t* t = P.tickets + (live ? code : 0);
+  for (int spin = 0;; ++spin) {
+    const int got = live ? __hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : need;
+    if (__all(got >= need)) break;
+    if (spin >= spin_limit) {
+      report_give_up(P.status, lane);
+      break;
     }
-    const uint64_t bal = __ballot(code >= 0);
-    const int pos = __popcll(bal & ((1ull << lane) - 1ull));
-    // each wave lists the rows of its own block of 64
-    if (code >= 0) {
-      last_list[w * 64 + pos] = code;
-      row_q[w * 64 + pos] = u;
-    }
-    if (lane == 0) n_last[w] = __popcll(bal);
+    __builtin_amdgcn_s_sleep(1);
   }
-  __syncthreads();
-  // merge the rows this work-group completed, 4 * NC per wave at a time;
+  if (live && sub == 0) __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // the partials of this path are bf16 (O / l) for bf16 attention and fp32
-  // for fp32, so the format is fixed here (two rows per lane row for bf16,
-  // whose rows take half the registers)
-  constexpr int NC = sizeof(T) == 2 ? 2 : 1;
+  // for fp32, so the format is fixed here
   constexpr int FMT = sizeof(T) == 2 ? kFmtBf16 : kFmtF32;
-  const int nwave = kPartialThreads / 64;
-  const int nblk = (nr + 63) / 64;
-  for (int b = 0; b < nblk; ++b) {
-    const int cnt = n_last[b];
-    for (int k = 4 * NC * w; k < cnt; k += 4 * NC * nwave) {
-      int codes[NC], us[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int j = k + (lane >> 4) + 4 * c;
-        codes[c] = j < cnt ? last_list[b * 64 + j] : -1;
-        us[c] = j < cnt ? row_q[b * 64 + j] : 0;
-      }
-      merge_rows<T, D, true, NC, FMT, true>(m, codes, PrefetchedSlots{pre_ids, pre_cnt}, us);
-    }
-  }
+  const int codes[1] = {live ? code : -1};
+  const int raws[1] = {raw};
+  const int cnts[1] = {live ? n : 0};
+  merge_rows<T, D, true, 1, FMT, true>(m, codes, raws, cnts);
 }
 
 // ---------------------------------------------------------------------------
@@ -742,9 +703,6 @@ __device__ inline float rowsum4(float x) {
 // does not finish.  A wait that runs out of checks sets *status (device
 // memory of the plan image) to 1: the work-group's results are then invalid,
 // and deft_plan_status reports it to the host.
-__device__ inline void report_give_up(int32_t* status, int lane) {
-  if (lane == 0) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ inline void pair_sync(int32_t* mine, int32_t* theirs, int32_t i, int lane, int32_t spins,
                                  int32_t* status) {
   if (lane == 0) __hip_atomic_store(mine, i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -806,8 +764,7 @@ struct ValuShape {
   static constexpr int SMEM_B = RING_B > RED_B ? RING_B : RED_B;
   // LDS carve-out: ring / reduction buffer, staged token rows, fused-merge lists
   static constexpr int TOK_OFF = SMEM_B;
-  static constexpr int LIST_OFF = TOK_OFF + 4 * kMaxChunkTokens;
-  static constexpr int LDS_B = LIST_OFF + 4 * (kValuRows + 4);
+  static constexpr int LDS_B = TOK_OFF + 4 * kMaxChunkTokens;
 };
 
 template <typename T, int D, int R, bool FUSED>
@@ -1161,10 +1118,7 @@ __device__ __forceinline__ void valu_body(const PartialArgs& a, char* lds, int b
     }
   }
   if constexpr (FUSED) {
-    static_assert(TailLds<kValuRows>::BYTES <= Shape::LIST_OFF, "tail LDS fits the body's buffers");
-    int32_t* last_list = reinterpret_cast<int32_t*>(lds + Shape::LIST_OFF);
-    fused_merge_tail<T, D, kValuRows>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, lds, last_list,
-                                      last_list + kValuRows);
+    fused_publish<kValuRows>(P, a.hq, a.grp, rb, nr, gofs, g);
   }
 }
 
@@ -1207,8 +1161,7 @@ struct MfmaShape {
   static constexpr int TOK_OFF = NSPLIT == 4 ? RING_B : RING_B + ROWS * ROWB;
   static constexpr int STATS_OFF = TOK_OFF + 4 * kMaxChunkTokens;
   static constexpr int FLAGS_OFF = STATS_OFF + 8 * 32 * 3 * 4;
-  static constexpr int LIST_OFF = FLAGS_OFF + 4 * 8;
-  static constexpr int LDS_B = LIST_OFF + 4 * (ROWS + 4);
+  static constexpr int LDS_B = FLAGS_OFF + 4 * 8;
 };
 
 template <int D, bool FUSED, int NSPLIT>
@@ -1709,10 +1662,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     }
   }
   if constexpr (FUSED) {
-    static_assert(TailLds<ROWS>::BYTES <= Shape::LIST_OFF, "tail LDS fits the body's buffers");
-    int32_t* last_list = reinterpret_cast<int32_t*>(lds + Shape::LIST_OFF);
-    fused_merge_tail<uint16_t, D, ROWS>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, lds, last_list,
-                                        last_list + ROWS);
+    fused_publish<ROWS>(P, a.hq, a.grp, rb, nr, gofs, g);
   }
 }
 
@@ -1744,8 +1694,7 @@ struct MfmaGroupShape {
   // LDS carve-out: ring, the block's Q rows, staged token rows, fused-merge lists
   static constexpr int QOFF = RING_B;
   static constexpr int TOK_OFF = QOFF + ROWS * ROWB;
-  static constexpr int LIST_OFF = TOK_OFF + 4 * kMaxChunkTokens;
-  static constexpr int LDS_B = LIST_OFF + 4 * (ROWS + 4);
+  static constexpr int LDS_B = TOK_OFF + 4 * kMaxChunkTokens;
 };
 
 template <int D, bool FUSED>
@@ -2108,10 +2057,7 @@ __device__ __forceinline__ void mfma_group_body(const PartialArgs& a, char* lds,
     }
   }
   if constexpr (FUSED) {
-    static_assert(TailLds<ROWS>::BYTES <= Shape::LIST_OFF, "tail LDS fits the body's buffers");
-    int32_t* last_list = reinterpret_cast<int32_t*>(lds + Shape::LIST_OFF);
-    fused_merge_tail<uint16_t, D, ROWS>(a.merge, P, P.tickets, a.grp, rb, nr, gofs, g, lds, last_list,
-                                        last_list + ROWS);
+    fused_publish<ROWS>(P, a.hq, a.grp, rb, nr, gofs, g);
   }
 }
 
@@ -2137,6 +2083,13 @@ __global__ __launch_bounds__(kPartialThreads) void partial_attention(PartialArgs
   const int nw = a.plan.n_mfma_wide * a.hkv;
   const int nm = a.plan.n_mfma * a.hkv;
   const int b = static_cast<int>(blockIdx.x);
+  if constexpr (FUSED) {
+    const int np = ng + nw + nm + a.plan.n_valu * a.hkv;
+    if (b >= np) {
+      merge_worker<T, D>(a.merge, a.plan, a.spin_limit, b - np, a.merge_wg_rows);
+      return;
+    }
+  }
   if constexpr (sizeof(T) == 2) {
     if (b < ng) {
       mfma_group_body<D, FUSED>(a, lds, b, 0);
@@ -2273,8 +2226,11 @@ static int launch_partials(const PartialArgs& pa, hipStream_t st) {
   const int hkv = pa.hkv;
   if (sizeof(T) != 2 && pa.plan.n_mfma_group + pa.plan.n_mfma + pa.plan.n_mfma_wide > 0)
     return fail(DEFT_ERR_UNSUPPORTED, "MFMA work for fp32 inputs");
-  const dim3 grid((pa.plan.n_mfma_group + pa.plan.n_mfma_wide + pa.plan.n_mfma + pa.plan.n_valu) * hkv), block(kPartialThreads);
-  if (grid.x == 0) return DEFT_OK;
+  const int n_partial = (pa.plan.n_mfma_group + pa.plan.n_mfma_wide + pa.plan.n_mfma + pa.plan.n_valu) * hkv;
+  if (n_partial == 0) return DEFT_OK;
+  // the single-dispatch path appends its merge work-groups
+  const int n_merge = pa.fused ? (pa.merge.nq * pa.merge.hq + pa.merge_wg_rows - 1) / pa.merge_wg_rows : 0;
+  const dim3 grid(n_partial + n_merge), block(kPartialThreads);
   // the VALU body's row capacity: 4 when every VALU item fits, else 8
   static_assert(kValuRows == 8, "VALU row capacities are 4 and 8");
   const bool r4 = pa.max_valu_rows <= 4;
@@ -2309,6 +2265,7 @@ static int run_partials(const void* q, const void* k, const void* v, const int32
   pa.scale_log2 = kLog2e / std::sqrt(static_cast<float>(d->head_dim));
   pa.spin_limit = spin_limit();
   pa.fused = fused_out != nullptr;
+  pa.merge_wg_rows = merge_worker_rows(p->num_queries * d->num_q_heads);
   pa.max_valu_rows = p->layout.max_valu_rows;
   pa.merge.po = po;
   pa.merge.pm = pm;
@@ -2505,8 +2462,8 @@ int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_
   float* po = static_cast<float*>(workspace);
   float* pm = po + align(deft::partial_o_words(plan, desc));
   float* pl = pm + align(sh);
-  // One dispatch per partial kernel: the last work-group to finish a
-  // (query, head) row merges it (fused_merge_tail).
+  // One dispatch: partial work-groups, then merge work-groups that wait for
+  // their rows' tickets (fused_publish, merge_worker).
   return deft::run_partials(q, k_cache, v_cache, block_table, plan, desc, po, pm, pl, po_bf16,
                             static_cast<hipStream_t>(stream), out);
 }
