@@ -2,11 +2,16 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--chunk-tokens C]
 
-A step is one pass of the hot path over one synthetic batch: the partial-
-attention kernel (every KV chunk streamed once per KV head for its query
-group) and the log-sum-exp merge, with the plan's device image, Q and the
-paged KV pool already resident in HBM.  The host planner and the plan upload
-(a PCIe copy) are timed separately and reported as extra fields.
+A step is one pass of the hot path over one synthetic batch: partial
+attention (every KV chunk streamed once per KV head for its query group) and
+the log-sum-exp merge, as the library's default call runs them, in one
+launch (deft_tree_attention_fused: the partial work-groups and then merge
+work-groups that take each (query, head) row once its partials are in),
+with the plan's device image, Q and the paged KV pool already resident in
+HBM.  The same step as two launches (partial kernel, then merge kernel;
+deft_tree_attention, bitwise the same output) is timed beside it.  The host
+planner and the plan upload (a PCIe copy) are timed separately and reported
+as extra fields.
 
 Cold caches without flushes in the timed region: the tree's KV pages are
 placed R times at disjoint positions of one pool, with one block table per
@@ -145,7 +150,7 @@ def main():
     ap.add_argument("--profile-run", action="store_true",
                     help="eager steps only (for rocprofv3 kernel traces and counters)")
     ap.add_argument("--profile-graph", action="store_true",
-                    help="with --profile-run: replay the partial kernel's timed graph instead")
+                    help="with --profile-run: replay the timed graph of K steps instead")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain elementwise copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -238,12 +243,14 @@ def main():
     torch.cuda.synchronize()
     upload_us = up0.elapsed_time(up1) * 1e3
 
-    def step(i, what="both"):
+    def step(i, what="step"):
+        """One step: the library's default call (a single dispatch: partial
+        and merge work-groups in one grid), or one of its legs."""
         r = i % copies
-        if what == "both":
-            D.deft_tree_attention(qs[r], kc, vc, bts[r], plan, outs[r], desc, workspace)
-        elif what == "fused":
+        if what == "step":
             D.deft_tree_attention_fused(qs[r], kc, vc, bts[r], plan, outs[r], desc, workspace)
+        elif what == "two":
+            D.deft_tree_attention(qs[r], kc, vc, bts[r], plan, outs[r], desc, workspace)
         elif what == "partial":
             D.deft_partial_attention(qs[r], kc, vc, bts[r], plan, desc, part_o, part_m, part_l, fmt)
         else:
@@ -254,14 +261,14 @@ def main():
     torch.cuda.synchronize()
     if args.profile_run:
         if args.profile_graph:
-            # the partial kernel's timed leg as bench.py runs it: a graph of
-            # K partial-only launches over the cold copies, replayed 1 + 5 times
+            # the timed leg as bench.py runs it: a graph of K steps over the
+            # cold copies, replayed 1 + 5 times
             g = torch.cuda.CUDAGraph()
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
             with torch.cuda.graph(g, stream=s):
                 for i in range(args.steps):
-                    step(i, "partial")
+                    step(i)
             torch.cuda.synchronize()
             for _ in range(6):
                 g.replay()
@@ -291,8 +298,10 @@ def main():
         return g
 
     def timed(g):
-        """Replay once to warm, then time one replay: (wall s, event ms)."""
-        g.replay()
+        """Replay three times to warm (caches, and the clocks after the host-side
+        checks left the GPU idle), then time one replay: (wall s, event ms)."""
+        for _ in range(3):
+            g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -303,7 +312,7 @@ def main():
         torch.cuda.synchronize()
         return time.perf_counter() - t0, e0.elapsed_time(e1)
 
-    g_step = capture("both", 0, args.steps)
+    g_step = capture("step", 0, args.steps)
     # every replay must reproduce the eager result (eager work between replays)
     for _ in range(2):
         for o in outs:
@@ -320,19 +329,20 @@ def main():
         """Per-kernel legs: median event time of `reps` timed replays."""
         return sorted(timed(g)[1] for _ in range(reps))[reps // 2]
 
+    step_ms_median = timed_median(g_step)
     g_part = capture("partial", 0, args.steps)
     part_ms = timed_median(g_part)
     g_merge = capture("merge", 0, args.steps)
     merge_ms = timed_median(g_merge)
-    # single-dispatch variant (last work-group of each row merges it): same
+    # the partial kernel then the merge kernel (deft_tree_attention): same
     # results bit for bit, timed the same way
-    g_fused = capture("fused", 0, args.steps)
+    g_two = capture("two", 0, args.steps)
     for o in outs:
         o.fill_(float("nan"))
-    _, fused_ms = timed(g_fused)
+    two_ms = timed_median(g_two)
     for r in range(min(copies, args.steps)):
-        assert torch.equal(outs[r], eager[r]), f"fused variant differs from the two-dispatch path (copy {r})"
-    del g_fused
+        assert torch.equal(outs[r], eager[r]), f"two-dispatch path differs from the single dispatch (copy {r})"
+    del g_two
     # the merge graph leaves outs[] holding merge-only results; restore the reference state
     for i in range(copies):
         step(i)
@@ -349,7 +359,7 @@ def main():
 
         def step2(i):
             r = i % copies
-            D.deft_tree_attention(qs[r], kc, vc, bts[r], plan2, outs2[r], desc, ws2)
+            D.deft_tree_attention_fused(qs[r], kc, vc, bts[r], plan2, outs2[r], desc, ws2)
 
         for i in range(copies):
             step2(i)
@@ -374,7 +384,7 @@ def main():
     nc_us, nc_err, nc_info = alt_plan_leg(D.deft_plan_create_node_chunks) if alt else (None, None, None)
     copies_saved = copies
     copies = 1                        # warm: the same copy every step, labelled as such
-    g_warm = capture("both", 0, args.steps)
+    g_warm = capture("step", 0, args.steps)
     _, warm_ms = timed(g_warm)
     copies = copies_saved
     del g_step, g_part, g_merge, g_warm
@@ -450,28 +460,31 @@ def main():
     naive_kv = float(sum(paths)) * 2 * hkv * d * eb
     part_bytes = S * hq * (d * (2 if wl.dtype == torch.bfloat16 else 4) + 8)
     algo_step = kv_bytes + 2 * q_bytes
+    mean_step = step_ms_median * 1e3 / args.steps     # a step is one launch
     mean_part = part_ms * 1e3 / args.steps
     mean_merge = merge_ms * 1e3 / args.steps
-    dominant = "partial" if mean_part >= mean_merge else "merge"
-    # the bound whose time floor is larger: matrix-core flops or HBM bytes
-    mfma_bound = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > (kv_bytes + q_bytes) / (HBM_PEAK_GBS * 1e9)
-    if dominant == "partial":
-        if mfma_bound:
-            achieved = flops / (mean_part * 1e-6) / 1e12
-            roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
-        else:
-            achieved = (kv_bytes + q_bytes) / (mean_part * 1e-6) / 1e9
-            roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-        roof["kernel"] = "partial_attention"
-        roof["algorithmic_bytes_per_launch"] = kv_bytes + q_bytes
+    # The step's one kernel (partial_attention with its merge work-groups):
+    # KV and Q read, out written.  The bound whose time floor is larger:
+    # matrix-core flops or HBM bytes.
+    algo_launch = kv_bytes + 2 * q_bytes
+    mfma_bound = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > algo_launch / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": flops / (mean_step * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
     else:
-        achieved = (part_bytes + q_bytes) / (mean_merge * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "kernel": "lse_merge", "algorithmic_bytes_per_launch": part_bytes + q_bytes}
+        roof = {"bound": "hbm", "achieved": algo_launch / (mean_step * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["kernel"] = "partial_attention (single dispatch: partial and merge work-groups)"
+    roof["algorithmic_bytes_per_launch"] = algo_launch
     roof["frac"] = roof["achieved"] / roof["peak"]
     if roof["unit"] == "GB/s":
         roof["frac_of_achievable"] = roof["achieved"] / cal_gbs
-    roof["launch_us_mean"] = mean_part if dominant == "partial" else mean_merge
+    roof["launch_us_mean"] = mean_step
+    # the partial kernel alone, as the two-dispatch path launches it
+    roof_partial = {"kernel": "partial_attention (partials only)", "launch_us_mean": mean_part,
+                    "algorithmic_bytes_per_launch": kv_bytes + q_bytes,
+                    "achieved_gbs": (kv_bytes + q_bytes) / (mean_part * 1e-6) / 1e9}
+    roof_partial["frac"] = roof_partial["achieved_gbs"] / HBM_PEAK_GBS
     roof["traffic"] = None
     counters = os.path.join(ROOT, "profiles", "hbm_counters.json")
     if os.path.exists(counters):
@@ -504,11 +517,16 @@ def main():
         "achieved_hbm_gbs": algo_step / (latency_us * 1e-6) / 1e9,
         "achieved_hbm_frac": algo_step / (latency_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "queries_per_s": nq / (latency_us * 1e-6),
-        "timing": "hipGraph of the K steps, replayed once untimed then once timed; the per-kernel legs (partial, merge) are the median of 5 timed replays of K launches of that kernel alone",
+        "timing": ("a step is the library's default call, one launch (deft_tree_attention_fused: partial and "
+                   "merge work-groups in one grid); hipGraph of the K steps, replayed three times untimed then "
+                   "once timed (value, step_us_events); the legs (the single dispatch again, the partial kernel, "
+                   "the merge kernel, the two-dispatch deft_tree_attention) are the median of 5 timed "
+                   "replays of K launches"),
         "step_us_events": ev_ms * 1e3 / args.steps,
+        "single_dispatch_step_us_median": mean_step,
+        "two_dispatch_step_us": two_ms * 1e3 / args.steps,
         "partial_kernel_us_mean": mean_part,
         "merge_kernel_us_mean": mean_merge,
-        "fused_single_dispatch_step_us": fused_ms * 1e3 / args.steps,
         "query_centric_baseline": None if qc_us is None else {
             "step_us": qc_us,
             "kv_bytes_read_ideal": naive_kv,
@@ -542,6 +560,7 @@ def main():
         "flops": flops,
         "partial_mfma_tflops": flops / (mean_part * 1e-6) / 1e12,
         "roofline": roof,
+        "roofline_partial_kernel": roof_partial,
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -309,8 +309,8 @@ int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
  * partial work-group writes its partials with
  * device-coherent stores, waits for them, and adds one to a device-scope
  * ticket per (query, head) row it wrote; a merge work-group waits until its
- * rows' tickets count every slot of their query, resets them, merges the
- * rows and writes `out`.  Its wait is bounded (as deft_plan_status
+ * rows' tickets count every slot of their query, subtracts that count,
+ * merges the rows and writes `out`.  Its wait is bounded (as deft_plan_status
  * describes): past the limit it reports a give-up and merges what it finds.
  * The tickets live in the plan's device image (zero after upload and after
  * every completed call), so calls that share a plan must not overlap and the

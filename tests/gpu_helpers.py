@@ -25,13 +25,14 @@ def gpu_inputs(wl):
     return q, kc, vc, bt
 
 
-def run_gpu(wl, chunk_tokens=None, poison_workspace=True, inputs=None):
-    """Tree attention through libdeft; returns (out on CPU as float64, runner)."""
+def run_gpu(wl, chunk_tokens=None, poison_workspace=True, inputs=None, single_dispatch=True):
+    """Tree attention through libdeft (the runner's single-dispatch call, or
+    the partial and merge kernels); returns (out on CPU as float64, runner)."""
     c = chunk_tokens or wl.chunk_tokens
     desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
     q, kc, vc, bt = inputs if inputs is not None else gpu_inputs(wl)
     ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, c, desc, device=DEV,
-                       query_lens=wl.query_lens)
+                       query_lens=wl.query_lens, single_dispatch=single_dispatch)
     if poison_workspace:
         ta.workspace.view(torch.float32).fill_(float("nan"))
     out = torch.full_like(q, float("nan"))

@@ -39,11 +39,12 @@ def _rms_check(got, want, what):
     assert err.mean() <= 2 ** -8 * mean, f"{what}: mean err {err.mean():.3e} above 2^-8 * {mean:.3e}"
 
 
+@pytest.mark.parametrize("single_dispatch", [True, False])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_standard_workload_matches_oracle(cfg):
+def test_standard_workload_matches_oracle(cfg, single_dispatch):
     wl = W.standard_workload(cfg)
-    say("standard", cfg, "C", wl.chunk_tokens)
-    got, _ = run_gpu(wl)
+    say("standard", cfg, "C", wl.chunk_tokens, "single dispatch", single_dispatch)
+    got, _ = run_gpu(wl, single_dispatch=single_dispatch)
     want = oracle_out(wl)
     check_close(got, want, TOL[wl.dtype], f"workload {cfg}")
     if wl.dtype == torch.bfloat16:
@@ -68,9 +69,10 @@ def test_tiny_tree_shuffled_pages_and_chunk_sizes():
         check_close(got, oracle_out(wl), 1e-5, f"C={c}")
 
 
+@pytest.mark.parametrize("single_dispatch", [True, False])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("seed", range(6))
-def test_random_trees(seed, dtype):
+def test_random_trees(seed, dtype, single_dispatch):
     rng = np.random.default_rng(5000 + seed)
     n = int(rng.integers(1, 50))
     p, s, qn = W.random_tree(rng, n, 1, int(rng.choice([1, 9, 80, 300])), int(rng.integers(1, 40)),
@@ -82,8 +84,8 @@ def test_random_trees(seed, dtype):
     wl = W.make_workload("rand", p, s, qn, chunk_tokens=c, hq=hq, hkv=hkv, d=d, dtype=dtype,
                          seed=seed, placement="scattered",
                          pool_pages=2 * (-(-int(s.sum()) // 16)) + 3)
-    say("random", seed, str(dtype), f"N={n} Nq={len(qn)} Hq={hq} Hkv={hkv} d={d} C={c}")
-    got, _ = run_gpu(wl)
+    say("random", seed, str(dtype), f"N={n} Nq={len(qn)} Hq={hq} Hkv={hkv} d={d} C={c}", single_dispatch)
+    got, _ = run_gpu(wl, single_dispatch=single_dispatch)
     want = oracle_out(wl)
     check_close(got, want, TOL[dtype], f"seed {seed}")
     if dtype == torch.bfloat16:

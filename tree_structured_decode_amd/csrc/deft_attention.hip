@@ -558,8 +558,9 @@ __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
 // returned), then leaves.  A merge work-group reads its rows' slot counts
 // and first slot ids, polls the rows' tickets until each has counted every
 // slot of its query (a bounded wait: past the spin limit it reports a
-// give-up through the plan's status word and merges what is there), resets
-// them to zero for the next call, and merges the rows through the same
+// give-up through the plan's status word and merges what is there), takes
+// that count back out of them (so that every ticket is zero again once the
+// call has ended, give-up or not), and merges the rows through the same
 // per-(query, head) merge as the merge kernel, with device-coherent loads.
 //
 // The dispatcher places work-groups in index order, so a merge work-group
@@ -640,7 +641,10 @@ __device__ __attribute__((always_inline)) void merge_worker(const MergeArgs& m, 
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  if (live && sub == 0) __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // take this call's count back out rather than storing zero: after a
+  // give-up, increments that arrive later still bring the ticket back to
+  // zero by the end of the call
+  if (live && sub == 0) __hip_atomic_fetch_add(t, -need, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // the partials of this path are bf16 (O / l) for bf16 attention and fp32
   // for fp32, so the format is fixed here
   constexpr int FMT = sizeof(T) == 2 ? kFmtBf16 : kFmtF32;

@@ -17,12 +17,19 @@ class TreeAttention:
     tensors on `device`; the plan image is uploaded on `stream`.
     chunk_tokens 0 takes the library's rule (deft_plan_auto_chunk_tokens) for
     the tree plan; the chosen size is kept in self.chunk_tokens.
+
+    single_dispatch (default True): a call is one launch
+    (deft_tree_attention_fused: partial and merge work-groups in one grid,
+    handing rows over through tickets in the plan's device image), so calls
+    on one runner must not overlap; False runs the partial kernel and the
+    merge kernel (deft_tree_attention).  Both give the same bits.
     """
 
     def __init__(self, parents, seg_lens, query_nodes, chunk_tokens: int, desc, device="cuda",
                  stream=None, query_centric: bool = False, node_chunks: bool = False,
-                 query_lens=None):
+                 query_lens=None, single_dispatch: bool = True):
         self.desc = desc
+        self.single_dispatch = single_dispatch
         if chunk_tokens == 0:
             if query_centric or node_chunks:
                 raise ValueError("the chunk-size rule is for the tree plan")
@@ -50,8 +57,8 @@ class TreeAttention:
     def __call__(self, q, k_cache, v_cache, block_table, out=None, stream=None):
         if out is None:
             out = torch.empty_like(q)
-        D.deft_tree_attention(q, k_cache, v_cache, block_table, self.plan, out, self.desc,
-                              self.workspace, stream)
+        run = D.deft_tree_attention_fused if self.single_dispatch else D.deft_tree_attention
+        run(q, k_cache, v_cache, block_table, self.plan, out, self.desc, self.workspace, stream)
         return out
 
     def partials(self, q, k_cache, v_cache, block_table, partial_format=D.DEFT_PARTIAL_F32, stream=None):
