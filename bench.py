@@ -151,6 +151,8 @@ def main():
                     help="eager steps only (for rocprofv3 kernel traces and counters)")
     ap.add_argument("--profile-graph", action="store_true",
                     help="with --profile-run: replay the timed graph of K steps instead")
+    ap.add_argument("--profile-two-dispatch", action="store_true",
+                    help="with --profile-run: eager steps as two launches (partial kernel, merge kernel)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain elementwise copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -275,7 +277,7 @@ def main():
                 torch.cuda.synchronize()
         else:
             for i in range(args.steps):
-                step(i)
+                step(i, "two" if args.profile_two_dispatch else "step")
         torch.cuda.synchronize()
         print(json.dumps({"profile_run": wl.name, "chunk_tokens": wl.chunk_tokens, "steps": args.steps,
                           "copies": copies, "kv_bytes": kv_bytes, "q_bytes": q_bytes,
