@@ -92,15 +92,20 @@ def test_random_trees(seed, dtype, single_dispatch):
         _rms_check(got, want, f"seed {seed}")
 
 
+@pytest.mark.parametrize("min_rows", ["1", "16"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("branches", [1, 2, 20])
-def test_kernel_paths(branches, d, dtype):
+def test_kernel_paths(monkeypatch, branches, d, dtype, min_rows):
     """Each body and row capacity on purpose: a 300-token prompt shared by
     `branches` queries, each on its own 90-token branch, 4 query heads per KV
-    head.  The prompt's group has 4 * branches rows (1 -> the 4-row VALU body,
-    whose bf16 d=128 lanes hold 32 bytes; 2 -> the 8-row VALU body; 20 -> the
-    MFMA body for bf16) and every branch chunk has 4 rows."""
+    head.  The prompt's group has 4 * branches rows and every branch chunk 4.
+    fp32 runs the VALU body (1 branch -> 4-row items, 2 -> 8-row items).  For
+    bf16 the matrix-core body takes every chunk by default (few rows padded);
+    with DEFT_MFMA_MIN_ROWS=16 chunks of fewer than 16 rows take the VALU body
+    (4 rows: bf16 d=128 lanes hold 32 bytes; 8 rows) and 20 branches' prompt
+    the matrix-core body."""
+    monkeypatch.setenv("DEFT_MFMA_MIN_ROWS", min_rows)
     p, s, qn = W.shared_prompt_branches(300, branches, 90)
     wl = W.make_workload("paths", p, s, qn, chunk_tokens=96, hq=8, hkv=2, d=d, dtype=dtype,
                          seed=branches * 7 + d, placement="scattered",
@@ -168,10 +173,11 @@ def test_constant_values_bf16():
 
 FORCE_WIDE = ("DEFT_MFMA_WIDE", "1")
 FORCE_GROUP = ("DEFT_MFMA_GROUP", "1")
+FORCE_VALU = ("DEFT_MFMA_MIN_ROWS", "16")    # bf16 chunks of < 16 rows on the VALU body
 
 
-@pytest.mark.parametrize("cfg,c,force", [(1, 64, None), (3, 512, None), (2, 256, None), (2, 256, FORCE_WIDE),
-                                         (2, 96, FORCE_GROUP)])
+@pytest.mark.parametrize("cfg,c,force", [(1, 64, None), (3, 512, None), (3, 512, FORCE_VALU), (2, 256, None),
+                                         (2, 256, FORCE_WIDE), (2, 96, FORCE_GROUP)])
 def test_partials_match_oracle(monkeypatch, cfg, c, force):
     """Per-slot fp32 partials (m, l, unnormalised O) against the oracle's;
     `force` selects 128-row MFMA items or whole-group items (each with its
@@ -203,8 +209,8 @@ def test_partials_match_oracle(monkeypatch, cfg, c, force):
     check_close(po / scale, o / scale, tol, "O / l")
 
 
-@pytest.mark.parametrize("cfg,c,force", [(3, 512, None), (2, 520, None), (2, 520, FORCE_WIDE),
-                                         (2, 136, FORCE_GROUP)])
+@pytest.mark.parametrize("cfg,c,force", [(3, 512, None), (3, 512, FORCE_VALU), (2, 520, None),
+                                         (2, 520, FORCE_WIDE), (2, 136, FORCE_GROUP)])
 def test_bf16_normalised_partials_match_oracle(monkeypatch, cfg, c, force):
     """The internal partial format of bf16 inputs: O / l rounded to bf16."""
     if force is not None:
@@ -529,7 +535,7 @@ def test_group_items_standard_tree_and_fused(monkeypatch):
 
 
 @pytest.mark.parametrize("cfg,force", [(2, None), (4, None), (3, None), (6, None), (2, FORCE_WIDE),
-                                       (2, FORCE_GROUP), (1, None)])
+                                       (2, FORCE_GROUP), (3, FORCE_VALU), (4, FORCE_VALU), (1, None)])
 def test_fused_path_reads_fresh_partials(monkeypatch, cfg, force):
     """The single-dispatch path hands partials between work-groups (possibly
     on different XCDs) through device-coherent stores and loads and relaxed

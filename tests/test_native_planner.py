@@ -307,17 +307,18 @@ def test_binding_checks_tensor_shapes():
         assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT and "part_o" in str(e.value)
 
 
-def _rule_by_brute_force(parents, seg_lens, query_nodes, hq, hkv, bf16, cus, query_lens=None):
+def _rule_by_brute_force(parents, seg_lens, query_nodes, hq, hkv, bf16, cus, query_lens=None, min_rows=1):
     """The documented chunk-size rule, evaluated by building the reference
     planner's plan at every candidate size: the smallest multiple of 32 up to
-    4096 whose work-groups (items of 64 rows for bf16 groups of >= 16 rows,
-    8 rows otherwise, times the KV heads) number at most `cus`; else 4096."""
+    4096 whose work-groups (items of 64 rows for bf16 groups of >= min_rows
+    rows, by default every bf16 group, 8 rows otherwise, times the KV heads)
+    number at most `cus`; else 4096."""
     g = hq // hkv
     for c in range(32, 4097, 32):
         plan = ref_plan(parents, seg_lens, query_nodes, c, query_lens=query_lens)
         go = plan["group_offsets"].astype(np.int64)
         rows = (go[1:] - go[:-1]) * g
-        blk = np.where(bf16 & (rows >= 16), 64, 8)
+        blk = np.where(bf16 & (rows >= min_rows), 64, 8)
         if int(np.sum(-(-rows // blk))) * hkv <= cus:
             return c
     return 4096
@@ -334,6 +335,19 @@ def test_auto_chunk_tokens_matches_the_rule(cfg):
         want = _rule_by_brute_force(wl.parents, wl.seg_lens, wl.query_nodes, wl.num_q_heads, wl.num_kv_heads,
                                     bf16, cus, query_lens=wl.query_lens)
         assert got == want, (cfg, cus, got, want)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_auto_chunk_tokens_follows_the_matrix_core_threshold(monkeypatch, cfg):
+    """DEFT_MFMA_MIN_ROWS=16 sends bf16 groups of fewer than 16 rows to the
+    VALU body (8-row items), and the rule counts them that way."""
+    monkeypatch.setenv("DEFT_MFMA_MIN_ROWS", "16")
+    wl = W.standard_workload(cfg)
+    desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    got = D.deft_plan_auto_chunk_tokens(wl.parents, wl.seg_lens, wl.query_nodes, desc, 256)
+    want = _rule_by_brute_force(wl.parents, wl.seg_lens, wl.query_nodes, wl.num_q_heads, wl.num_kv_heads,
+                                True, 256, min_rows=16)
+    assert got == want, (cfg, got, want)
 
 
 def test_auto_chunk_tokens_known_choices():

@@ -21,7 +21,7 @@ constexpr int kPageSize = 16;
 constexpr int kMfmaRows = 64;      // rows per MFMA work item (4 tiles of 16)
 constexpr int kMfmaWideRows = 128; // rows per wide MFMA work item (groups of more than kMfmaRows rows)
 constexpr int kMfmaGroupRows = 256; // rows per whole-group MFMA work item (no token split)
-constexpr int kMfmaMinRows = 16;   // a chunk needs this many rows to use MFMA
+constexpr int kMfmaMinRows = 1;    // default rows a bf16 chunk needs to use MFMA (every chunk)
 constexpr int kValuRows = 8;       // rows per VALU work item
 constexpr int64_t kMaxQueryRows = int64_t{1} << 28;       // num_queries * num_q_heads < this
 constexpr int64_t kMaxPartialBlocks = (int64_t{1} << 23) - 1; // grid x 512 threads < 2^32

@@ -375,9 +375,26 @@ size_t workspace_bytes_for(const deft_plan* p, const deft_attn_desc* d) {
 // items (kMfmaGroupRows, no token split) are taken only on request.
 // DEFT_MFMA_WIDE / DEFT_MFMA_GROUP = 1 or 0 in the environment force either
 // choice (tests).
+// Rows a bf16 chunk needs to run on the matrix-core bodies: kMfmaMinRows
+// (every chunk: a few-row item pads its rows on the matrix cores, which the
+// latency-bound step loop has time for, where the VALU body spends its
+// instruction stream on the same rows and ran about twice as long on the
+// parallel-sampling tree's 512-token branches), or DEFT_MFMA_MIN_ROWS from
+// the environment when it lies in [1, 4096] (tests send small chunks to the
+// VALU body with it).
+static int32_t mfma_min_rows() {
+  const char* env = std::getenv("DEFT_MFMA_MIN_ROWS");
+  if (env && env[0]) {
+    const long v = std::strtol(env, nullptr, 10);
+    if (v >= 1 && v <= 4096) return static_cast<int32_t>(v);
+  }
+  return kMfmaMinRows;
+}
+
 struct ItemPolicy {
   bool bf16, query_centric, wide_on, group_on;
-  bool mfma(int32_t rows) const { return bf16 && (rows >= kMfmaMinRows || query_centric); }
+  int32_t min_rows;
+  bool mfma(int32_t rows) const { return bf16 && (rows >= min_rows || query_centric); }
   int32_t block(int32_t rows) const {
     if (!mfma(rows)) return kValuRows;
     if (group_on) return kMfmaGroupRows;
@@ -388,7 +405,7 @@ struct ItemPolicy {
 
 static ItemPolicy item_policy(const std::vector<int32_t>& chunk_rows, const deft_attn_desc* d, bool query_centric,
                               int cus) {
-  ItemPolicy pol{d->dtype == DEFT_DTYPE_BF16, query_centric, false, false};
+  ItemPolicy pol{d->dtype == DEFT_DTYPE_BF16, query_centric, false, false, mfma_min_rows()};
   int64_t n64 = 0;
   for (int32_t rows : chunk_rows) {
     const int32_t b = pol.mfma(rows) ? kMfmaRows : kValuRows;
