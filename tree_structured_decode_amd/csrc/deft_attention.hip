@@ -291,15 +291,17 @@ __device__ inline float row_reduce16(float x, Op op) {
 }
 
 // Accesses of partial results.  COHERENT (the single-dispatch path, whose
-// last work-group of a (query, head) row reads partials other work-groups
-// wrote, possibly on other XCDs with their own L2): relaxed device-scope
-// atomic stores and loads, which the compiler emits as ordinary vector
-// memory instructions with device coherence scope (sc1 on gfx950: stores
-// written through to the device's coherence point, loads served from it), so
-// no write-back or invalidation of a whole L2 is needed to hand partials
-// from one work-group to another; ordering comes from each wave's wait for
-// its own stores and a work-group barrier before the relaxed ticket.  The
-// two-dispatch path (kernel boundary in between) uses plain accesses.
+// merge work-groups read partials that partial work-groups of the same
+// launch wrote, possibly on other XCDs with their own L2): relaxed
+// device-scope atomic stores and loads, which the compiler emits as ordinary
+// vector memory instructions with device coherence scope (sc1 on gfx950:
+// stores written through to the device's coherence point, loads served from
+// it), so no write-back or invalidation of a whole L2 is needed to hand
+// partials from one work-group to another; ordering comes from each wave's
+// wait for its own stores and a work-group barrier before the relaxed
+// ticket, and on the reading side from the ticket load the merge's loads
+// depend on.  The two-dispatch path (kernel boundary in between) uses plain
+// accesses.
 template <bool COHERENT>
 __device__ inline void st_u32(void* p, uint32_t v) {
   if constexpr (COHERENT) __hip_atomic_store(static_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
