@@ -38,6 +38,21 @@ def test_library_exports_every_declared_symbol():
         assert getattr(L, name) is not None
 
 
+def test_bench_library_exports_its_declared_symbols():
+    """libdeft_bench.so (the benchmark's streaming-read calibration) exports
+    what include/deft_bench.h declares; the sink size needs no GPU."""
+    import ctypes
+    header = open(os.path.join(ROOT, "include", "deft_bench.h")).read()
+    declared = set(re.findall(r"^\S.*?\b(deft_bench_\w+)\(", header, flags=re.M))
+    assert declared == {"deft_bench_stream_read", "deft_bench_stream_read_sink_floats"}
+    D.lib()                        # the HIP runtime torch bundles, first
+    B = ctypes.CDLL(os.path.join(ROOT, "tree_structured_decode_amd", "libdeft_bench.so"))
+    for name in declared:
+        assert getattr(B, name) is not None
+    B.deft_bench_stream_read_sink_floats.restype = ctypes.c_size_t
+    assert B.deft_bench_stream_read_sink_floats() > 0
+
+
 def test_single_hip_runtime_in_process():
     D.lib()
     maps = open("/proc/self/maps").read()
