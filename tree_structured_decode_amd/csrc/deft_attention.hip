@@ -408,136 +408,106 @@ __device__ inline void row_bcast_all(X x, X (&out)[16], std::integer_sequence<in
   ((out[J] = row_bcast<J>(x)), ...);
 }
 
-// Merge of (query, query head) rows: NC rows per 16-lane row of lanes, so
-// 4 * NC per wave; codes[c] = qi * Hq + h of this lane's c-th row, or -1 for
-// none.  Lane sub of a row reads the metadata (slot id, m, l) of the row's
-// slots sub, sub + 16, ... and D/16 consecutive elements of every slot's
-// partial O row.  A round of up to 16 slots costs two rounds of dependent
-// loads (the slot ids, then m, l and the O rows together), and the loads of
-// all NC rows are issued before any of them is reduced, so NC rows cost the
-// latency of one.  With M = max_s m_s and w_s = exp(m_s - M):
+// Merge of (query, query head) rows, one per 16-lane row of lanes (four per
+// wave); `code` = qi * Hq + h of this lane's row, or -1 for none.  Lane sub
+// of a row reads the metadata (slot id, m, l) of the row's slots sub,
+// sub + 16, ... and D/16 consecutive elements of every slot's partial O row.
+// A round of up to 16 slots costs two rounds of dependent loads (the slot
+// ids, then m, l and the O rows together).  With M = max_s m_s and
+// w_s = exp(m_s - M):
 //   fp32 unnormalised partials   out = sum_s w_s O_s / sum_s w_s l_s
 //   bf16 partials holding O_s/l_s out = sum_s w_s l_s (O_s/l_s) / sum_s w_s l_s
 // Rows with more than 16 slots take several rounds, rescaled online.
-// PRE: the caller has already read each row's slot count (cnt0[c], 0 for no
-// row) and this lane's first slot id (raw0[c]: slot sub of the row's list,
-// or -1), so the first round starts with the partials' own loads.
-template <typename T, int D, bool COHERENT, int NC, int FMT, bool PRE = false>
-__device__ __attribute__((always_inline)) void merge_rows(const MergeArgs& a, const int (&codes)[NC],
-                                                          const int* raw0 = nullptr, const int* cnt0 = nullptr) {
+// PRE: the caller has already read the row's slot count (cnt0; 0 for no
+// row) and this lane's first slot id (raw0: slot sub of the row's list, or
+// -1), so the first round starts with the partials' own loads.
+template <typename T, int D, bool COHERENT, int FMT, bool PRE = false>
+__device__ __attribute__((always_inline)) void merge_rows(const MergeArgs& a, int code, int raw0 = -1,
+                                                          int cnt0 = 0) {
   constexpr int EPL = D / 16;      // elements per lane
   const int lane = threadIdx.x & 63, sub = lane & 15;
-  bool live[NC];
-  int qi[NC], h[NC], cnt[NC];
-  const int32_t* list[NC];
-  int cmx = 0;
+  const bool live = code >= 0;
+  const int qi = live ? code / a.hq : 0, h = live ? code % a.hq : 0;
   // the row's slot list: fixed stride (padded with -1, read without a
   // dependent offset lookup) or CSR
-  auto slot_list = [&](int q, int& n) {
+  auto slot_list = [&](int& n) {
     if (a.merge_stride > 0) {
       n = a.merge_stride;
-      return a.merge_slots + static_cast<size_t>(q) * a.merge_stride;
+      return a.merge_slots + static_cast<size_t>(qi) * a.merge_stride;
     }
-    const int s0 = a.query_slot_offsets[q];
-    n = a.query_slot_offsets[q + 1] - s0;
+    const int s0 = a.query_slot_offsets[qi];
+    n = a.query_slot_offsets[qi + 1] - s0;
     return a.query_slots + s0;
   };
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    live[c] = codes[c] >= 0;
-    qi[c] = live[c] ? codes[c] / a.hq : 0;
-    h[c] = live[c] ? codes[c] % a.hq : 0;
-    if constexpr (PRE) {
-      list[c] = nullptr;               // looked up only for rows of more than 16 slots
-      cnt[c] = live[c] ? cnt0[c] : 0;
-    } else {
-      int n;
-      list[c] = slot_list(qi[c], n);
-      cnt[c] = live[c] ? n : 0;
-    }
-    cmx = cnt[c] > cmx ? cnt[c] : cmx;
+  const int32_t* list = nullptr;   // with PRE, looked up only for rows of more than 16 slots
+  int cnt;
+  if constexpr (PRE) {
+    cnt = live ? cnt0 : 0;
+  } else {
+    int n;
+    list = slot_list(n);
+    cnt = live ? n : 0;
   }
-  const int cmax = static_cast<int>(wave_max(static_cast<float>(cmx)));
-  float acc[NC][EPL], mrun[NC], wsum[NC];
+  const int cmax = static_cast<int>(wave_max(static_cast<float>(cnt)));
+  float acc[EPL];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    mrun[c] = kNegInf;
-    wsum[c] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[c][e] = 0.f;
-  }
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float mrun = kNegInf, wsum = 0.f;
   for (int i0 = 0; i0 < cmax; i0 += 16) {
-    int raw[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if constexpr (PRE) {
-        if (i0 == 0) {
-          raw[c] = live[c] ? raw0[c] : -1;
-          continue;
-        }
-        if (i0 == 16 && live[c]) {
-          int n;
-          list[c] = slot_list(qi[c], n);
-        }
-      }
-      raw[c] = i0 + sub < cnt[c] ? list[c][i0 + sub] : -1;
-    }
-    // every slot's m, l and O row of this round, for all NC rows, issued
-    // before any reduction
-    float mv[NC], lv[NC];
-    int sj[NC][16];
-    PartialRow<EPL, FMT> rows[NC][16];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const bool ok = raw[c] >= 0;                   // padding entries are -1
-      const int64_t sh = static_cast<int64_t>(ok ? raw[c] : 0) * a.hq + h[c];
-      mv[c] = ok ? ld_f32<COHERENT>(a.pm + sh) : kNegInf;
-      lv[c] = ok ? ld_f32<COHERENT>(a.pl + sh) : 0.f;
-      row_bcast_all(raw[c], sj[c], std::make_integer_sequence<int, 16>{});
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (sj[c][j] >= 0)
-          load_partial_row<D, EPL, FMT, COHERENT>(a, static_cast<int64_t>(sj[c][j]) * a.hq + h[c], sub, rows[c][j]);
-    }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const float mnew = fmaxf(mrun[c], row_reduce16(mv[c], [](float x, float y) { return fmaxf(x, y); }));
-      const float w = mv[c] == kNegInf ? 0.f : __expf(mv[c] - mnew);
-      const float wl = w * lv[c];
-      const float wt = fmt_bf16<FMT>(a) ? wl : w;      // weight of the stored O row
-      const float rescale = mrun[c] == kNegInf ? 0.f : __expf(mrun[c] - mnew);
-      mrun[c] = mnew;
-      wsum[c] = wsum[c] * rescale + row_reduce16(wl, [](float x, float y) { return x + y; });
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[c][e] *= rescale;
-      float wj[16];
-      row_bcast_all(wt, wj, std::make_integer_sequence<int, 16>{});
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (sj[c][j] >= 0) {
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[c][e] = fmaf(wj[j], partial_elem<EPL, FMT>(a, rows[c][j], e), acc[c][e]);
-        }
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (!live[c]) continue;
-    const float inv = 1.f / wsum[c];
-    const size_t ob = (static_cast<size_t>(qi[c]) * a.hq + h[c]) * D + sub * EPL;
-    if constexpr (sizeof(T) == 2) {
-      uint32_t pk[EPL / 2];
-#pragma unroll
-      for (int e = 0; e < EPL / 2; ++e)
-        pk[e] = pack_bf16x2(acc[c][2 * e] * inv, acc[c][2 * e + 1] * inv);
-      if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ob) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-      else *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = u32x2{pk[0], pk[1]};
+    int raw;
+    if (PRE && i0 == 0) {
+      raw = live ? raw0 : -1;
     } else {
-#pragma unroll
-      for (int e = 0; e < EPL; e += 4)
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob + e) =
-            f32x4{acc[c][e] * inv, acc[c][e + 1] * inv, acc[c][e + 2] * inv, acc[c][e + 3] * inv};
+      if (PRE && i0 == 16 && live) {
+        int n;
+        list = slot_list(n);
+      }
+      raw = i0 + sub < cnt ? list[i0 + sub] : -1;
     }
+    // every slot's m, l and O row of this round, issued before any reduction
+    const bool ok = raw >= 0;                   // padding entries are -1
+    const int64_t sh = static_cast<int64_t>(ok ? raw : 0) * a.hq + h;
+    const float mv = ok ? ld_f32<COHERENT>(a.pm + sh) : kNegInf;
+    const float lv = ok ? ld_f32<COHERENT>(a.pl + sh) : 0.f;
+    int sj[16];
+    row_bcast_all(raw, sj, std::make_integer_sequence<int, 16>{});
+    PartialRow<EPL, FMT> rows[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (sj[j] >= 0) load_partial_row<D, EPL, FMT, COHERENT>(a, static_cast<int64_t>(sj[j]) * a.hq + h, sub, rows[j]);
+    const float mnew = fmaxf(mrun, row_reduce16(mv, [](float x, float y) { return fmaxf(x, y); }));
+    const float w = mv == kNegInf ? 0.f : __expf(mv - mnew);
+    const float wl = w * lv;
+    const float wt = fmt_bf16<FMT>(a) ? wl : w;      // weight of the stored O row
+    const float rescale = mrun == kNegInf ? 0.f : __expf(mrun - mnew);
+    mrun = mnew;
+    wsum = wsum * rescale + row_reduce16(wl, [](float x, float y) { return x + y; });
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= rescale;
+    float wj[16];
+    row_bcast_all(wt, wj, std::make_integer_sequence<int, 16>{});
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (sj[j] >= 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wj[j], partial_elem<EPL, FMT>(a, rows[j], e), acc[e]);
+      }
+  }
+  if (!live) return;
+  const float inv = 1.f / wsum;
+  const size_t ob = (static_cast<size_t>(qi) * a.hq + h) * D + sub * EPL;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t pk[EPL / 2];
+#pragma unroll
+    for (int e = 0; e < EPL / 2; ++e)
+      pk[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    if constexpr (EPL == 8) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + ob) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    else *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + ob) = u32x2{pk[0], pk[1]};
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob + e) =
+          f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
   }
 }
 
@@ -546,8 +516,7 @@ __global__ __launch_bounds__(256) void lse_merge(MergeArgs a) {
   const int wave0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
   if (wave0 >= a.nq * a.hq) return;          // whole waves leave together
   const int code = wave0 + ((threadIdx.x & 63) >> 4);
-  const int codes[1] = {code < a.nq * a.hq ? code : -1};
-  merge_rows<T, D, false, 1, kFmtRuntime>(a, codes);
+  merge_rows<T, D, false, kFmtRuntime>(a, code < a.nq * a.hq ? code : -1);
 }
 
 // ---------------------------------------------------------------------------
@@ -650,10 +619,7 @@ __device__ __attribute__((always_inline)) void merge_worker(const MergeArgs& m, 
   // the partials of this path are bf16 (O / l) for bf16 attention and fp32
   // for fp32, so the format is fixed here
   constexpr int FMT = sizeof(T) == 2 ? kFmtBf16 : kFmtF32;
-  const int codes[1] = {live ? code : -1};
-  const int raws[1] = {raw};
-  const int cnts[1] = {live ? n : 0};
-  merge_rows<T, D, true, 1, FMT, true>(m, codes, raws, cnts);
+  merge_rows<T, D, true, FMT, true>(m, live ? code : -1, raw, live ? n : 0);
 }
 
 // ---------------------------------------------------------------------------
