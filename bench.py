@@ -349,6 +349,33 @@ def main():
     for i in range(copies):
         step(i)
     torch.cuda.synchronize()
+    # The same step with fp32 partials in the workspace (desc.f32_partials):
+    # bf16 inputs only (fp32 inputs use fp32 partials already).
+    f32p = None
+    if bf16:
+        desc32 = D.make_desc(wl.dtype, hq, hkv, d, n_pages, f32_partials=True)
+        _, wb32 = D.deft_plan_device_bytes(plan, desc32)
+        ws32 = torch.empty(wb32, dtype=torch.uint8, device=dev)
+        outs32 = [torch.empty_like(o) for o in outs]
+
+        def step32(i):
+            r = i % copies
+            D.deft_tree_attention_fused(qs[r], kc, vc, bts[r], plan, outs32[r], desc32, ws32)
+
+        for i in range(copies):
+            step32(i)
+        torch.cuda.synchronize()
+        err32 = max(float((outs32[r].float() - eager[r].float()).abs().max()) for r in range(copies))
+        g32 = torch.cuda.CUDAGraph()
+        s32 = torch.cuda.Stream()
+        s32.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g32, stream=s32):
+            for i in range(args.steps):
+                step32(i)
+        torch.cuda.synchronize()
+        f32p = {"step_us": timed_median(g32) * 1e3 / args.steps, "max_abs_diff_vs_default": err32,
+                "partial_bytes": S * hq * (d * 4 + 8)}
+        del g32, ws32, outs32
     def alt_plan_leg(create):
         """Another plan of the same tree on the same kernels, inputs and
         copies, timed the same way; returns (step us, max |diff| vs DeFT)."""
@@ -529,6 +556,7 @@ def main():
         "two_dispatch_step_us": two_ms * 1e3 / args.steps,
         "partial_kernel_us_mean": mean_part,
         "merge_kernel_us_mean": mean_merge,
+        "f32_partials": f32p,
         "query_centric_baseline": None if qc_us is None else {
             "step_us": qc_us,
             "kv_bytes_read_ideal": naive_kv,

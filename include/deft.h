@@ -135,6 +135,10 @@ typedef struct {
   int32_t head_dim;      /* d: 64 or 128 */
   int32_t page_size;     /* tokens per KV page: 16 */
   int32_t num_pages;     /* pages in k_cache and v_cache (each) */
+  int32_t f32_partials;  /* 0: the workspace holds each dtype's internal partial format (bf16 O / l
+                            for bf16 inputs, fp32 unnormalised O for fp32); 1: fp32 unnormalised
+                            O for every dtype (twice the partial bytes for bf16, no rounding of
+                            the per-slot results before the merge) */
 } deft_attn_desc;
 
 /*
@@ -240,13 +244,14 @@ int deft_plan_export(const deft_plan* plan, deft_plan_view* out_view);
  * Sizes the caller must allocate for a given attention shape:
  *   *plan_bytes       device image of the plan (deft_plan_upload)
  *   *workspace_bytes  per-slot partial results of deft_tree_attention: part_o
- *                     in its internal format, then part_m and part_l, each
- *                     padded to 256 bytes
+ *                     in the format desc->f32_partials selects, then part_m
+ *                     and part_l, each padded to 256 bytes
  * Either output pointer may be NULL.  UNSUPPORTED if desc is outside this
  * build (head_dim not 64/128, page_size != 16, Hq % Hkv != 0, chunk_tokens
  * > 4096), if num_queries * num_q_heads reaches 2^28, or if the work items
  * times num_kv_heads exceed 2^23 - 1 (one launch's grid; a larger
- * chunk_tokens makes fewer items); INVALID_ARGUMENT for non-positive shapes.
+ * chunk_tokens makes fewer items); INVALID_ARGUMENT for non-positive shapes
+ * or f32_partials other than 0 and 1.
  */
 int deft_plan_device_bytes(deft_plan* plan, const deft_attn_desc* desc,
                            size_t* plan_bytes, size_t* workspace_bytes);
@@ -270,9 +275,10 @@ int deft_plan_upload(deft_plan* plan, const deft_attn_desc* desc, void* dev_plan
  * chunk's KV streamed once per KV head for all its grouped queries and their
  * query heads, bitmask applied, per-slot partials written to the workspace in
  * format DEFT_PARTIAL_BF16_NORM for bf16 inputs, DEFT_PARTIAL_F32 for fp32
- * inputs) followed by the log-sum-exp merge kernel.
- * q, k_cache, v_cache, block_table, out, workspace: device pointers.
- * desc must equal the desc of the last deft_plan_upload.  workspace_bytes
+ * inputs or when desc->f32_partials is 1) followed by the log-sum-exp merge
+ * kernel.  q, k_cache, v_cache, block_table, out, workspace: device pointers.
+ * desc must equal the desc of the last deft_plan_upload (f32_partials aside:
+ * the image does not depend on it, so each call may choose).  workspace_bytes
  * must be at least the size from deft_plan_device_bytes.  block_table
  * entries are not range-checked on the device; an entry outside
  * [0, num_pages) is undefined behaviour.  With the environment variable

@@ -409,6 +409,36 @@ def test_fused_merge_work_groups_many_rows(dtype, d):
     check_close(ref.double().cpu().numpy(), oracle_out(wl), TOL[dtype], "many rows")
 
 
+@pytest.mark.parametrize("cfg", [2, 3, 6])
+def test_f32_partials_match_oracle(cfg):
+    """bf16 inputs with desc.f32_partials = 1: the workspace holds fp32
+    unnormalised partials.  The single dispatch and the two dispatches give
+    the same bits, the oracle is met, and the output differs from the default
+    bf16 partials' (the format took effect)."""
+    wl = W.standard_workload(cfg)
+    say("f32 partials", cfg)
+    q, kc, vc, bt = gpu_inputs(wl)
+    outs = {}
+    for f32 in (False, True):
+        desc = D.make_desc(wl.dtype, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages,
+                           f32_partials=f32)
+        ta = TreeAttention(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens, desc, device=DEV,
+                           query_lens=wl.query_lens)
+        ta.workspace.view(torch.float32).fill_(float("nan"))
+        one = torch.full_like(q, float("nan"))
+        ta(q, kc, vc, bt, one)
+        two = torch.full_like(q, float("nan"))
+        D.deft_tree_attention(q, kc, vc, bt, ta.plan, two, desc, ta.workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(one, two), f"f32_partials={f32}: single and two dispatches differ"
+        outs[f32] = one
+    assert not torch.equal(outs[False], outs[True])
+    want = oracle_out(wl)
+    got = outs[True].double().cpu().numpy()
+    check_close(got, want, TOL[wl.dtype], f"f32 partials {cfg}")
+    _rms_check(got, want, f"f32 partials {cfg}")
+
+
 @pytest.mark.timeout(900)
 def test_long_context_spec_tree_all_queries():
     """The 32K-prefix / 256-node tree in a pool filling ~60% of HBM, pages at

@@ -394,6 +394,31 @@ def test_auto_chunk_tokens_random_trees(seed):
     assert got == _rule_by_brute_force(p, s, qn, hq, hkv, dtype == torch.bfloat16, cus)
 
 
+def test_f32_partials_workspace_and_validation():
+    """desc.f32_partials = 1 sizes the workspace for fp32 partial O for bf16
+    inputs too (the image is unchanged), and values other than 0 and 1 are
+    rejected."""
+    wl = W.standard_workload(2)
+    plan = D.deft_plan_create(wl.parents, wl.seg_lens, wl.query_nodes, wl.chunk_tokens)
+    s_ = D.deft_plan_export(plan)["num_slots"]
+    dims = (wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages)
+    pb0, wb0 = D.deft_plan_device_bytes(plan, D.make_desc(torch.bfloat16, *dims))
+    pb1, wb1 = D.deft_plan_device_bytes(plan, D.make_desc(torch.bfloat16, *dims, f32_partials=True))
+    pbf, wbf = D.deft_plan_device_bytes(plan, D.make_desc(torch.float32, *dims))
+    assert pb1 == pb0
+    o_words = s_ * wl.num_q_heads * wl.head_dim
+    def pad(w):
+        return -(-w // 64) * 64
+    ml = 2 * pad(s_ * wl.num_q_heads)
+    assert wb0 == 4 * (pad(-(-o_words // 2)) + ml)
+    assert wb1 == 4 * (pad(o_words) + ml) == wbf
+    bad = D.make_desc(torch.bfloat16, *dims)
+    bad.f32_partials = 2
+    with pytest.raises(D.DeftError) as e:
+        D.deft_plan_device_bytes(plan, bad)
+    assert e.value.code == D.DEFT_ERR_INVALID_ARGUMENT
+
+
 def test_auto_chunk_tokens_errors():
     desc = D.make_desc(torch.bfloat16, 8, 2, 128, 10)
     with pytest.raises(D.DeftError) as e:

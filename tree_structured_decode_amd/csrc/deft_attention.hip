@@ -616,10 +616,13 @@ __device__ __attribute__((always_inline)) void merge_worker(const MergeArgs& m, 
   // give-up, increments that arrive later still bring the ticket back to
   // zero by the end of the call
   if (live && sub == 0) __hip_atomic_fetch_add(t, -need, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // the partials of this path are bf16 (O / l) for bf16 attention and fp32
-  // for fp32, so the format is fixed here
-  constexpr int FMT = sizeof(T) == 2 ? kFmtBf16 : kFmtF32;
-  merge_rows<T, D, true, FMT, true>(m, live ? code : -1, raw, live ? n : 0);
+  // the partials of this path: bf16 (O / l) for bf16 attention unless the
+  // descriptor asks for fp32 ones, fp32 for fp32 (one format per launch, so
+  // the branch is uniform)
+  if (sizeof(T) == 2 && m.po_bf16)
+    merge_rows<T, D, true, kFmtBf16, true>(m, live ? code : -1, raw, live ? n : 0);
+  else
+    merge_rows<T, D, true, kFmtF32, true>(m, live ? code : -1, raw, live ? n : 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -2402,7 +2405,7 @@ int deft_tree_attention(const void* q, const void* k_cache, const void* v_cache,
   const size_t need = deft::workspace_bytes_for(plan, desc);
   if (workspace_bytes < need) return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace too small");
   // Internal partial format: bf16 O / l for bf16 inputs, fp32 unnormalised O otherwise.
-  const bool po_bf16 = desc->dtype == DEFT_DTYPE_BF16;
+  const bool po_bf16 = deft::bf16_partials(desc);
   const size_t sh = static_cast<size_t>(plan->num_slots) * desc->num_q_heads;
   auto align = [](size_t n) { return (n + 63) & ~static_cast<size_t>(63); };
   float* po = static_cast<float*>(workspace);
@@ -2428,7 +2431,7 @@ int deft_tree_attention_fused(const void* q, const void* k_cache, const void* v_
     return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   const size_t need = deft::workspace_bytes_for(plan, desc);
   if (workspace_bytes < need) return fail(DEFT_ERR_INVALID_ARGUMENT, "workspace too small");
-  const bool po_bf16 = desc->dtype == DEFT_DTYPE_BF16;
+  const bool po_bf16 = deft::bf16_partials(desc);
   const size_t sh = static_cast<size_t>(plan->num_slots) * desc->num_q_heads;
   auto align = [](size_t n) { return (n + 63) & ~static_cast<size_t>(63); };
   float* po = static_cast<float*>(workspace);
@@ -2480,7 +2483,7 @@ int deft_tree_attention_noalloc(const void* q, const void* k_cache, const void* 
   if (rc) return rc;
   if (!out) return fail(DEFT_ERR_INVALID_ARGUMENT, "out must not be NULL");
   // the same kernels and partial format as deft_tree_attention, on the scratch
-  const bool po_bf16 = desc->dtype == DEFT_DTYPE_BF16;
+  const bool po_bf16 = deft::bf16_partials(desc);
   const size_t sh = static_cast<size_t>(plan->num_slots) * desc->num_q_heads;
   auto align = [](size_t n) { return (n + 63) & ~static_cast<size_t>(63); };
   float* po = static_cast<float*>(ws);

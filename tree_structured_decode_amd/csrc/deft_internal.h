@@ -90,6 +90,9 @@ int device_cu_count();
 void release_upload(deft_plan* p);
 // Workspace: partial O (bf16 O / l for bf16 inputs, fp32 unnormalised O for
 // fp32 inputs), then part_m and part_l, each 256-byte aligned.
+// Whether the attention calls' workspace holds bf16 O / l partials (bf16
+// inputs without desc->f32_partials) rather than fp32 unnormalised ones.
+inline bool bf16_partials(const deft_attn_desc* d) { return d->dtype == DEFT_DTYPE_BF16 && !d->f32_partials; }
 size_t partial_o_words(const deft_plan* p, const deft_attn_desc* desc);
 size_t workspace_bytes_for(const deft_plan* p, const deft_attn_desc* desc);
 }  // namespace deft

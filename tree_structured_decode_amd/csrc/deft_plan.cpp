@@ -342,6 +342,8 @@ int check_desc(const deft_plan* p, const deft_attn_desc* d) {
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(DEFT_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (d->page_size != kPageSize) return fail(DEFT_ERR_UNSUPPORTED, "page_size must be 16");
+  if (d->f32_partials != 0 && d->f32_partials != 1)
+    return fail(DEFT_ERR_INVALID_ARGUMENT, "f32_partials must be 0 or 1");
   if (d->num_q_heads % d->num_kv_heads != 0)
     return fail(DEFT_ERR_UNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
   if (p && p->chunk_tokens > kMaxChunkTokens)
@@ -357,7 +359,7 @@ static size_t align_words(size_t w) { return (w + 63) & ~static_cast<size_t>(63)
 
 size_t partial_o_words(const deft_plan* p, const deft_attn_desc* d) {
   const size_t n = static_cast<size_t>(p->num_slots) * d->num_q_heads * d->head_dim;
-  return d->dtype == DEFT_DTYPE_BF16 ? (n + 1) / 2 : n;
+  return bf16_partials(d) ? (n + 1) / 2 : n;
 }
 
 size_t workspace_bytes_for(const deft_plan* p, const deft_attn_desc* d) {

@@ -69,7 +69,7 @@ class deft_plan_view(ctypes.Structure):
 
 class deft_attn_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "dtype", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "num_pages")]
+        "dtype", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "num_pages", "f32_partials")]
 
 
 _lib = None
@@ -255,9 +255,11 @@ def deft_plan_export(plan: Plan) -> dict:
 
 
 def make_desc(dtype: torch.dtype, num_q_heads: int, num_kv_heads: int, head_dim: int,
-              num_pages: int, page_size: int = 16) -> deft_attn_desc:
+              num_pages: int, page_size: int = 16, f32_partials: bool = False) -> deft_attn_desc:
+    """f32_partials: fp32 unnormalised per-slot partials in the workspace for
+    bf16 inputs too (the default keeps bf16 O / l for bf16 inputs)."""
     code = {torch.float32: DEFT_DTYPE_F32, torch.bfloat16: DEFT_DTYPE_BF16}.get(dtype, 99)
-    return deft_attn_desc(code, num_q_heads, num_kv_heads, head_dim, page_size, num_pages)
+    return deft_attn_desc(code, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, int(f32_partials))
 
 
 def deft_plan_device_bytes(plan: Plan, desc: deft_attn_desc):
