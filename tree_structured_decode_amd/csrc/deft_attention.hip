@@ -23,12 +23,14 @@
 // r = j * G + hh is slot j's query on query head g * G + hh (G = Hq / Hkv).
 //
 // One partial kernel (partial_attention) runs two bodies on one work description:
-//   mfma_body  bf16 groups with >= 16 rows: 16x16x32 bf16 MFMA for S = K Q^T
-//              and O^T = V^T P^T, 64 rows per work-group, the chunk's
-//              tokens split across 4 wave pairs and the splits merged in LDS
-//              (or 128 rows, 2 splits of 4 waves, for wide items);
-//   valu_body  fp32 inputs and bf16 groups below one MFMA tile: per-token
-//              dot products with wavefront reductions.
+//   mfma_body  bf16 chunks (rows padded up to the 16-row MFMA tile):
+//              16x16x32 bf16 MFMA for S = K Q^T and O^T = V^T P^T, 64 rows
+//              per work-group, the chunk's tokens split across 4 wave pairs
+//              and the splits merged in LDS (or 128 rows, 2 splits of 4
+//              waves, for wide items);
+//   valu_body  fp32 inputs, and bf16 chunks below the DEFT_MFMA_MIN_ROWS
+//              threshold when one is set (default 1: none): per-token dot
+//              products with wavefront reductions.
 // Scores are kept in log2 units (scale * log2(e) folded in) so exp2 is used;
 // the stored m is converted back to natural-log units.
 
@@ -710,10 +712,10 @@ __device__ inline void group_sync(int32_t* flags, int me, int32_t i, int lane, i
 }
 
 // ---------------------------------------------------------------------------
-// VALU partial kernel: groups below one MFMA tile, and fp32 inputs; up to R
-// rows per work-group (R = 4 or 8, the smaller that holds the plan's largest
-// VALU work item; larger groups are split into items of 8 rows that share
-// the chunk's KV through L2).  Scores and the PV update are wavefront arithmetic:
+// VALU partial kernel: fp32 inputs (and bf16 chunks the DEFT_MFMA_MIN_ROWS
+// threshold sends here); up to R rows per work-group (R = 4 or 8, the
+// smaller that holds the plan's largest VALU work item; larger groups are
+// split into items of 8 rows that share the chunk's KV through L2).  Scores and the PV update are wavefront arithmetic:
 // lanes are grouped LPT per token (each lane holds 16 or 32 bytes of the
 // token's K and V row), dot products are summed across the group with DPP
 // moves; with bf16 inputs a lane's two tokens of a step share one dot2 per
