@@ -697,13 +697,17 @@ __device__ inline void group_sync(int32_t* flags, int me, int32_t i, int lane, i
   if constexpr (N == 2) {
     pair_sync(&flags[me], &flags[me ^ 1], i, lane, spins, status);
   } else {
+    // four flags (16-byte aligned) are read with one LDS load per check, so a
+    // check costs one LDS round trip rather than three in a row
+    static_assert(N == 4, "pairs or quads of waves");
     if (lane == 0) __hip_atomic_store(&flags[me], i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     for (int spin = 0;; ++spin) {
-      bool done = true;
-#pragma unroll
-      for (int k = 0; k < N; ++k)
-        if (k != me) done &= __hip_atomic_load(&flags[k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= i;
-      if (done) return;
+      typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+      const i32x4 f = *reinterpret_cast<const volatile i32x4*>(flags);
+      if (min(min(f[0], f[1]), min(f[2], f[3])) >= i) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        return;
+      }
       if (spin >= spins) break;
       __builtin_amdgcn_s_sleep(1);
     }
@@ -1155,6 +1159,7 @@ struct MfmaShape {
   static constexpr int STATS_OFF = TOK_OFF + 4 * kMaxChunkTokens;
   static constexpr int FLAGS_OFF = STATS_OFF + 8 * 32 * 3 * 4;
   static constexpr int LDS_B = FLAGS_OFF + 4 * 8;
+  static_assert(FLAGS_OFF % 16 == 0, "a split's flags are read as one 16-byte word");
 };
 
 template <int D, bool FUSED, int NSPLIT>
