@@ -679,12 +679,17 @@ __device__ inline float rowsum4(float x) {
 // argument spin_limit) so that a broken pairing can never leave a wave that
 // does not finish.  A wait that runs out of checks sets *status (device
 // memory of the plan image) to 1: the work-group's results are then invalid,
-// and deft_plan_status reports it to the host.
+// and deft_plan_status reports it to the host.  The flags are addressed as
+// LDS (address space 3), so the accesses are ds_write / ds_read; through a
+// generic pointer they would be flat accesses with device-coherence bits,
+// which take the vector-memory path and cost several times the latency.
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+__device__ inline lds_i32* as_lds(int32_t* p) { return (lds_i32*)p; }
 __device__ inline void pair_sync(int32_t* mine, int32_t* theirs, int32_t i, int lane, int32_t spins,
                                  int32_t* status) {
-  if (lane == 0) __hip_atomic_store(mine, i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (lane == 0) __hip_atomic_store(as_lds(mine), i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   for (int spin = 0;; ++spin) {
-    if (__hip_atomic_load(theirs, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= i) return;
+    if (__hip_atomic_load(as_lds(theirs), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= i) return;
     if (spin >= spins) break;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -700,10 +705,11 @@ __device__ inline void group_sync(int32_t* flags, int me, int32_t i, int lane, i
     // four flags (16-byte aligned) are read with one LDS load per check, so a
     // check costs one LDS round trip rather than three in a row
     static_assert(N == 4, "pairs or quads of waves");
-    if (lane == 0) __hip_atomic_store(&flags[me], i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const volatile i32x4 lds_i32x4;
+    if (lane == 0) __hip_atomic_store(as_lds(&flags[me]), i, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     for (int spin = 0;; ++spin) {
-      typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-      const i32x4 f = *reinterpret_cast<const volatile i32x4*>(flags);
+      const i32x4 f = *(lds_i32x4*)as_lds(flags);
       if (min(min(f[0], f[1]), min(f[2], f[3])) >= i) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         return;
