@@ -1401,25 +1401,25 @@ __device__ __forceinline__ void mfma_body(const PartialArgs& a, char* lds, int b
     const char* kb = ring + STG * STAGE_B;
     const uint32_t* mb = reinterpret_cast<const uint32_t*>(kb + 2 * TILE_B);
     const uint32_t nd = ring_lds + (STG ^ 1) * STAGE_B + kvsel * TILE_B;   // this wave's tile in the other stage
-    const char* ptr[NL];
-    if (next) load_ptrs(step + NSPLIT, ptr);
-
     // The step runs row tile by row tile so that each tile's softmax
     // arithmetic is issued between the MFMAs of the next product (S of tile
     // 1, then PV of tile 0) and executes while the matrix unit works:
     //   S(0) | softmax(0) max  | S(1) + softmax(0) exp | softmax(1) max |
     //   PV(0) + softmax(1) exp | PV(1)
-    // Waves keep a raised issue priority for the whole step.
-    // The next step's loads go out first (the MFMA runs stay free of
-    // branches, so the arithmetic can be interleaved with them).
+    // Waves keep a raised issue priority for the whole step.  The K
+    // fragment reads go out first, then the next step's loads (their
+    // address arithmetic runs while the fragments arrive; the MFMA runs
+    // stay free of branches, so the arithmetic can be interleaved with them).
+    bf16x8 kfr[2 * KS];
+#pragma unroll
+    for (int n = 0; n < 2 * KS; ++n) kfr[n] = *reinterpret_cast<const bf16x8*>(smem + STG * STAGE_B + koff[n]);
     if (next) {
+      const char* ptr[NL];
+      load_ptrs(step + NSPLIT, ptr);
 #pragma unroll
       for (int j = 0; j < NL; ++j) lds_dma16(ptr[j], nd + (n0 + j) * 1024);
       if (loads_mask) lds_dma4(mask_src + step + NSPLIT, ring_lds + (STG ^ 1) * STAGE_B + 2 * TILE_B + gr * 256);
     }
-    bf16x8 kfr[2 * KS];
-#pragma unroll
-    for (int n = 0; n < 2 * KS; ++n) kfr[n] = *reinterpret_cast<const bf16x8*>(smem + STG * STAGE_B + koff[n]);
     __builtin_amdgcn_s_setprio(1);
     // S^T = K Q^T for row tile rt: sacc[tt][rt] over the 4 k-steps; n = (ks, tt).
     f32x4 sacc[2][NRT];
